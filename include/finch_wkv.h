@@ -1,0 +1,147 @@
+/*
+ * finch_wkv.h -- C ABI of the Finch WKV pre-fill library (libfinch_wkv.so).
+ *
+ * The operation (GoldFinch architecture summary page, section 3.4 "Finch-C2
+ * Time Mixing", paragraph "Recurrent state update and output", with base
+ * Finch's static bonus u from modification (4) of the same section):
+ *
+ *   per (sequence n, head h), tokens t = 0 .. L_n - 1 in order,
+ *     o_t[j]   = sum_i r_t[i] * ( S[i][j] + u[h][i] * k_t[i] * v_t[j] )
+ *     S[i][j] <- w_t[i] * S[i][j] + k_t[i] * v_t[j]
+ *   starting from S = state_in[n][h] (zeros when state_in is NULL) and ending
+ *   with state_out[n][h] = S.  Rows i of S are key channels (the decay acts on
+ *   them), columns j are value channels.  This is the recurrent pre-fill of
+ *   the Finch layers: a whole submitted context is consumed at O(1) cost per
+ *   token and leaves a fixed-size state that later tokens continue from
+ *   (abstract; section 3.4 "Training and Inference Procedures", inference
+ *   pre-fill).  Carrying state_out into the next call as state_in continues
+ *   the same sequence exactly.
+ *
+ * Layouts (all row-major, D fastest, no padding):
+ *   r, k, v, w : [B, T, H, D] (fixed length) or [total_tokens, H, D] (packed)
+ *                element type `in_dtype` (WKV_BF16 or WKV_F32)
+ *   u          : [H, D] fp32
+ *   o          : same layout as r, fp32
+ *   state_in   : [B or N, H, D, D] fp32, [i][j] = [key channel][value channel]
+ *   state_out  : same as state_in
+ * Supported head size: D = 64.
+ *
+ * Ownership and concurrency: the caller owns every buffer.  All tensor
+ * pointers are DEVICE pointers, except cu_seqlens_host.  The library never
+ * allocates device memory; scratch lives in the caller's `workspace`.  Calls
+ * are asynchronous on `stream` (a hipStream_t; NULL = the null stream): when a
+ * call returns WKV_OK the work is enqueued, and inputs must stay valid and
+ * unmodified until it completes.  Kernel faults surface at the caller's next
+ * synchronisation.  Two calls that share a workspace must be ordered (same
+ * stream, or synchronised).
+ *
+ * Aliasing: state_out == state_in (exact same pointer) is allowed -- the
+ * carried-state idiom.  Any other overlap between an output (o, state_out)
+ * and any other buffer is rejected with WKV_EINVAL (checked on the address
+ * ranges).
+ *
+ * Domain: 0 < w <= 1 (w == 1 exactly is legal).  Values outside it, NaN or Inf
+ * are not checked and propagate.  Finite |r|, |k| below 2^31 are required
+ * (the chunked evaluation rescales them by powers of two up to 2^96).
+ *
+ * Errors: every entry point validates its arguments before touching the GPU
+ * and returns a wkv_status_t; wkv_last_error() gives a human-readable detail
+ * for the calling thread.  No exception crosses the ABI.  Nothing is written
+ * when a call fails validation.
+ */
+#ifndef FINCH_WKV_H
+#define FINCH_WKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define FINCH_WKV_ABI_VERSION 1
+
+typedef enum {
+    WKV_OK = 0,
+    WKV_EINVAL = 1,       /* null/misaligned pointer, bad size, bad offsets, overlap */
+    WKV_EUNSUPPORTED = 2, /* head size other than 64, unknown dtype */
+    WKV_EWORKSPACE = 3,   /* workspace NULL or smaller than the query says */
+    WKV_EHIP = 4          /* a HIP runtime call or kernel launch failed */
+} wkv_status_t;
+
+typedef enum {
+    WKV_F32 = 0,
+    WKV_BF16 = 1
+} wkv_dtype_t;
+
+/* FINCH_WKV_ABI_VERSION of the loaded library. */
+int wkv_abi_version(void);
+
+/* Static description of a status code (never NULL). */
+const char *wkv_status_string(wkv_status_t status);
+
+/* Detail of the last failed call on this thread ("" if none).  The pointer
+ * stays valid until the next call into the library from the same thread. */
+const char *wkv_last_error(void);
+
+/*
+ * Workspace size in bytes needed by wkv_prefill for these sizes (0 is a valid
+ * answer: then workspace may be NULL).  Returns 0 as well for invalid sizes;
+ * wkv_prefill reports those.  Deterministic: same arguments, same answer on the
+ * same device.
+ */
+size_t wkv_prefill_workspace_bytes(int B, int T, int H, int D, wkv_dtype_t in_dtype);
+
+/*
+ * Fixed-length batch pre-fill: B sequences of T tokens each.
+ *   r, k, v, w  device, [B, T, H, D] of in_dtype, 16-byte aligned
+ *   u           device, [H, D] fp32
+ *   state_in    device, [B, H, D, D] fp32, or NULL (start from zeros)
+ *   o           device, [B, T, H, D] fp32 (output; may be NULL only if T == 0)
+ *   state_out   device, [B, H, D, D] fp32 (output), or NULL (not written)
+ *   B, H >= 1, T >= 0, D == 64
+ *   workspace   device scratch of at least wkv_prefill_workspace_bytes(...)
+ *               bytes (NULL allowed when that is 0), 256-byte aligned
+ *   stream      hipStream_t to enqueue on
+ * T == 0 leaves o untouched and copies state_in (or zeros) to state_out.
+ */
+wkv_status_t wkv_prefill(const void *r, const void *k, const void *v,
+                         const void *w, const float *u, const float *state_in,
+                         float *o, float *state_out,
+                         int B, int T, int H, int D, wkv_dtype_t in_dtype,
+                         void *workspace, size_t workspace_bytes,
+                         void *stream);
+
+/*
+ * Workspace size for wkv_prefill_varlen with these offsets (host copy).
+ * Returns 0 for invalid offsets; wkv_prefill_varlen reports those.
+ */
+size_t wkv_prefill_varlen_workspace_bytes(const int32_t *cu_seqlens_host, int N,
+                                          int H, int D, wkv_dtype_t in_dtype);
+
+/*
+ * Ragged (packed) pre-fill: N sequences concatenated along the token axis.
+ *   cu_seqlens_dev   device, [N + 1] int32 token offsets
+ *   cu_seqlens_host  host,   [N + 1] int32, the same values (used to plan the
+ *                    launch; it must equal the device copy -- a mismatch gives
+ *                    unspecified results but never an out-of-range access)
+ *   Offsets: cu[0] == 0, non-decreasing, cu[N] = total tokens <= 2^31 - 1;
+ *   empty sequences are allowed (their state is passed through).
+ *   r, k, v, w, o    device, [cu[N], H, D]
+ *   state_in/out     device, [N, H, D, D] fp32 (NULL as in wkv_prefill)
+ * Each sequence starts from its own state_in[n] and ends in state_out[n].
+ */
+wkv_status_t wkv_prefill_varlen(const void *r, const void *k, const void *v,
+                                const void *w, const float *u,
+                                const int32_t *cu_seqlens_dev,
+                                const int32_t *cu_seqlens_host, int N,
+                                const float *state_in, float *o, float *state_out,
+                                int H, int D, wkv_dtype_t in_dtype,
+                                void *workspace, size_t workspace_bytes,
+                                void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FINCH_WKV_H */

@@ -1,0 +1,10 @@
+"""Finch WKV pre-fill on MI355X (gfx950).
+
+The hot path of GoldFinch's linear-time pre-fill -- the Finch (RWKV-6) WKV
+recurrence with per-channel data-dependent decay -- as hand-written HIP kernels
+behind a C ABI (include/finch_wkv.h, libfinch_wkv.so).  This package is the
+thin Python binding over that library.
+"""
+from ._binding import (  # noqa: F401
+    HEAD_DIM, LIBRARY_PATH, WkvError, abi_version, prefill, prefill_varlen,
+    varlen_workspace_bytes, workspace_bytes)

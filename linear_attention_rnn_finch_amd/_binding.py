@@ -1,0 +1,203 @@
+"""ctypes binding of libfinch_wkv.so (argument marshalling only).
+
+Every step of the computation runs in the library's HIP kernels; this module
+only checks tensor metadata, allocates outputs/workspace through torch's
+caching allocator and passes raw device pointers plus torch's current HIP
+stream.  There is no CPU fallback: if the library is missing, importing the
+package raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIBRARY_PATH = os.path.join(_PKG, "libfinch_wkv.so")
+
+WKV_OK, WKV_EINVAL, WKV_EUNSUPPORTED, WKV_EWORKSPACE, WKV_EHIP = range(5)
+WKV_F32, WKV_BF16 = 0, 1
+HEAD_DIM = 64
+
+if not os.path.exists(LIBRARY_PATH):
+    raise ImportError(
+        "libfinch_wkv.so is not built (%s); run `python -m "
+        "linear_attention_rnn_finch_amd.build_lib` or __graft_entry__.build()" % LIBRARY_PATH)
+
+_lib = ctypes.CDLL(LIBRARY_PATH)
+_vp, _sz, _i, _i32p = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int, ctypes.POINTER(ctypes.c_int32)
+
+_lib.wkv_abi_version.restype = _i
+_lib.wkv_abi_version.argtypes = []
+_lib.wkv_status_string.restype = ctypes.c_char_p
+_lib.wkv_status_string.argtypes = [_i]
+_lib.wkv_last_error.restype = ctypes.c_char_p
+_lib.wkv_last_error.argtypes = []
+_lib.wkv_prefill_workspace_bytes.restype = _sz
+_lib.wkv_prefill_workspace_bytes.argtypes = [_i, _i, _i, _i, _i]
+_lib.wkv_prefill_varlen_workspace_bytes.restype = _sz
+_lib.wkv_prefill_varlen_workspace_bytes.argtypes = [_vp, _i, _i, _i, _i]
+_lib.wkv_prefill.restype = _i
+_lib.wkv_prefill.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                             _i, _i, _i, _i, _i, _vp, _sz, _vp]
+_lib.wkv_prefill_varlen.restype = _i
+_lib.wkv_prefill_varlen.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i,
+                                    _vp, _vp, _vp, _i, _i, _i, _vp, _sz, _vp]
+
+
+class WkvError(RuntimeError):
+    def __init__(self, status: int, detail: str):
+        self.status = status
+        msg = _lib.wkv_status_string(status).decode()
+        super().__init__("%s (%d): %s" % (msg, status, detail))
+
+
+def abi_version() -> int:
+    return int(_lib.wkv_abi_version())
+
+
+def _check(status: int):
+    if status != WKV_OK:
+        raise WkvError(status, _lib.wkv_last_error().decode())
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return WKV_BF16
+    if t.dtype == torch.float32:
+        return WKV_F32
+    raise TypeError("r, k, v, w must be bfloat16 or float32, got %s" % t.dtype)
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _stream_handle(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream
+
+
+def _device_tensor(name, t, dtype=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s must be a torch.Tensor" % name)
+    if t.device.type != "cuda":
+        raise ValueError("%s must be on a GPU device" % name)
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError("%s must be %s, got %s" % (name, dtype, t.dtype))
+
+
+def workspace_bytes(B: int, T: int, H: int, D: int = HEAD_DIM, dtype=torch.bfloat16) -> int:
+    code = WKV_BF16 if dtype == torch.bfloat16 else WKV_F32
+    return int(_lib.wkv_prefill_workspace_bytes(B, T, H, D, code))
+
+
+def varlen_workspace_bytes(cu_seqlens_host, H: int, D: int = HEAD_DIM, dtype=torch.bfloat16) -> int:
+    cu = torch.as_tensor(cu_seqlens_host, dtype=torch.int32).contiguous()
+    code = WKV_BF16 if dtype == torch.bfloat16 else WKV_F32
+    return int(_lib.wkv_prefill_varlen_workspace_bytes(cu.data_ptr(), cu.numel() - 1, H, D, code))
+
+
+def _workspace(nbytes, device, given):
+    if nbytes == 0:
+        return None, 0
+    if given is not None:
+        return given, given.numel() * given.element_size()
+    return torch.empty(nbytes, dtype=torch.uint8, device=device), nbytes
+
+
+def prefill(r, k, v, w, u, state_in=None, *, o=None, state_out=None, want_state=True,
+            workspace=None, stream=None):
+    """Finch WKV pre-fill of a fixed-length batch on the GPU.
+
+    r, k, v, w: [B, T, H, 64] bfloat16 (or float32), contiguous, same device.
+    u: [H, 64] float32.  state_in: [B, H, 64, 64] float32 or None (zeros).
+    Returns (o [B, T, H, 64] float32, state_out [B, H, 64, 64] float32 or None).
+    ``state_out`` may be ``state_in`` (carried state, updated in place).
+    """
+    for name, t in (("r", r), ("k", k), ("v", v), ("w", w)):
+        _device_tensor(name, t, r.dtype)
+    if r.dim() != 4:
+        raise ValueError("r must be [B, T, H, D]")
+    B, T, H, D = r.shape
+    for name, t in (("k", k), ("v", v), ("w", w)):
+        if t.shape != r.shape:
+            raise ValueError("%s shape %s != r shape %s" % (name, tuple(t.shape), tuple(r.shape)))
+    _device_tensor("u", u, torch.float32)
+    if tuple(u.shape) != (H, D):
+        raise ValueError("u must be [H, D] = %s" % ((H, D),))
+    if state_in is not None:
+        _device_tensor("state_in", state_in, torch.float32)
+        if tuple(state_in.shape) != (B, H, D, D):
+            raise ValueError("state_in must be [B, H, D, D]")
+    code = _dtype_code(r)
+    if o is None:
+        o = torch.empty((B, T, H, D), dtype=torch.float32, device=r.device)
+    else:
+        _device_tensor("o", o, torch.float32)
+        if tuple(o.shape) != (B, T, H, D):
+            raise ValueError("o must be [B, T, H, D]")
+    if state_out is None and want_state:
+        state_out = torch.empty((B, H, D, D), dtype=torch.float32, device=r.device)
+    elif state_out is not None:
+        _device_tensor("state_out", state_out, torch.float32)
+        if tuple(state_out.shape) != (B, H, D, D):
+            raise ValueError("state_out must be [B, H, D, D]")
+    need = int(_lib.wkv_prefill_workspace_bytes(B, T, H, D, code))
+    ws, ws_bytes = _workspace(need, r.device, workspace)
+    with torch.cuda.device(r.device):
+        status = _lib.wkv_prefill(_ptr(r), _ptr(k), _ptr(v), _ptr(w), _ptr(u), _ptr(state_in),
+                                  _ptr(o), _ptr(state_out), B, T, H, D, code, _ptr(ws),
+                                  ws_bytes, _stream_handle(stream))
+    _check(status)
+    return o, state_out
+
+
+def prefill_varlen(r, k, v, w, u, cu_seqlens, state_in=None, *, cu_seqlens_host=None, o=None,
+                   state_out=None, want_state=True, workspace=None, stream=None):
+    """Finch WKV pre-fill of N packed sequences.
+
+    r, k, v, w: [total_tokens, H, 64]; cu_seqlens: [N + 1] int32 offsets on the
+    GPU; cu_seqlens_host: the same offsets on the host (copied from the device,
+    with a synchronisation, when omitted).  state_in/state_out: [N, H, 64, 64].
+    """
+    for name, t in (("r", r), ("k", k), ("v", v), ("w", w)):
+        _device_tensor(name, t, r.dtype)
+    if r.dim() != 3:
+        raise ValueError("packed r must be [tokens, H, D]")
+    total, H, D = r.shape
+    for name, t in (("k", k), ("v", v), ("w", w)):
+        if t.shape != r.shape:
+            raise ValueError("%s shape differs from r" % name)
+    _device_tensor("u", u, torch.float32)
+    _device_tensor("cu_seqlens", cu_seqlens, torch.int32)
+    N = cu_seqlens.numel() - 1
+    if cu_seqlens_host is None:
+        cu_seqlens_host = cu_seqlens.cpu()
+    cu_host = torch.as_tensor(cu_seqlens_host, dtype=torch.int32).contiguous()
+    if cu_host.numel() != N + 1:
+        raise ValueError("cu_seqlens_host must have N + 1 entries")
+    if int(cu_host[-1]) != total:
+        raise ValueError("cu_seqlens[-1]=%d != token count %d" % (int(cu_host[-1]), total))
+    if state_in is not None:
+        _device_tensor("state_in", state_in, torch.float32)
+        if tuple(state_in.shape) != (N, H, D, D):
+            raise ValueError("state_in must be [N, H, D, D]")
+    code = _dtype_code(r)
+    if o is None:
+        o = torch.empty((total, H, D), dtype=torch.float32, device=r.device)
+    if state_out is None and want_state:
+        state_out = torch.empty((N, H, D, D), dtype=torch.float32, device=r.device)
+    need = int(_lib.wkv_prefill_varlen_workspace_bytes(cu_host.data_ptr(), N, H, D, code))
+    ws, ws_bytes = _workspace(need, r.device, workspace)
+    with torch.cuda.device(r.device):
+        status = _lib.wkv_prefill_varlen(_ptr(r), _ptr(k), _ptr(v), _ptr(w), _ptr(u),
+                                         _ptr(cu_seqlens), cu_host.data_ptr(), N, _ptr(state_in),
+                                         _ptr(o), _ptr(state_out), H, D, code, _ptr(ws),
+                                         ws_bytes, _stream_handle(stream))
+    _check(status)
+    return o, state_out

@@ -1,0 +1,302 @@
+// C ABI of libfinch_wkv: argument validation, launch planning and kernel
+// sequencing for the Finch WKV pre-fill.  See include/finch_wkv.h for the
+// contract.
+#include "finch_wkv.h"
+#include "wkv_internal.h"
+
+#include <algorithm>
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <string>
+#include <vector>
+
+namespace finch {
+namespace {
+
+thread_local std::string g_last_error;
+
+wkv_status_t fail(wkv_status_t st, const char *fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return st;
+}
+
+wkv_status_t fail_hip(hipError_t e, const char *what) {
+    return fail(WKV_EHIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+// ---- planning -------------------------------------------------------------
+
+// Work items the planner aims for: two resident 4-wave workgroups on each of
+// the 256 compute units of an MI355X.
+constexpr int64_t kTargetItems = 512;
+constexpr int64_t kMinSegment = 4 * kChunk;
+
+int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
+
+// Segment length for a launch of `work` token-heads whose longest sequence
+// has `max_len` tokens.  fp32 inputs are never split (their kernel is serial).
+int64_t choose_segment(int64_t work, int64_t max_len, bool bf16) {
+    if (!bf16) return std::max<int64_t>(round_up(std::max<int64_t>(max_len, 1), kChunk), kChunk);
+    if (const char *env = std::getenv("FINCH_WKV_SEGMENT_TOKENS")) {
+        int64_t v = std::atoll(env);
+        if (v >= kChunk && v % kChunk == 0) return v;
+    }
+    int64_t seg = round_up(std::max<int64_t>((work + kTargetItems - 1) / kTargetItems, 1), kChunk);
+    seg = std::max(seg, kMinSegment);
+    const int64_t whole = round_up(std::max<int64_t>(max_len, 1), kChunk);
+    return std::min(seg, whole);
+}
+
+struct Plan {
+    Geometry g{};
+    bool bf16 = false;
+    bool split = false;              // some sequence has more than one segment
+    size_t off_seg_state = 0, off_seg_start = 0, off_seg_off = 0, off_seg_seq = 0;
+    size_t bytes = 0;
+};
+
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+void layout_workspace(Plan &p, bool varlen) {
+    size_t off = 0;
+    const size_t items = (size_t)p.g.n_seg * p.g.H;
+    if (p.split) {
+        p.off_seg_state = off;
+        off = align256(off + items * kSegStateFloats * sizeof(float));
+        p.off_seg_start = off;
+        off = align256(off + items * kSegStartFloats * sizeof(float));
+    }
+    if (varlen) {
+        p.off_seg_off = off;
+        off = align256(off + (size_t)(p.g.n_seq + 1) * sizeof(int32_t));
+        p.off_seg_seq = off;
+        off = align256(off + (size_t)p.g.n_seg * sizeof(int32_t));
+    }
+    p.bytes = off;
+}
+
+wkv_status_t check_common(int H, int D, wkv_dtype_t dt) {
+    if (dt != WKV_F32 && dt != WKV_BF16) return fail(WKV_EUNSUPPORTED, "unknown in_dtype %d", (int)dt);
+    if (D != kHeadDim) return fail(WKV_EUNSUPPORTED, "head size D=%d unsupported (only %d)", D, kHeadDim);
+    if (H < 1) return fail(WKV_EINVAL, "H=%d must be >= 1", H);
+    return WKV_OK;
+}
+
+wkv_status_t plan_fixed(int B, int T, int H, int D, wkv_dtype_t dt, Plan &p) {
+    if (wkv_status_t s = check_common(H, D, dt)) return s;
+    if (B < 1) return fail(WKV_EINVAL, "B=%d must be >= 1", B);
+    if (T < 0) return fail(WKV_EINVAL, "T=%d must be >= 0", T);
+    const int64_t tokens = (int64_t)B * T;
+    if (tokens > INT32_MAX) return fail(WKV_EINVAL, "B*T=%lld exceeds 2^31-1 tokens", (long long)tokens);
+    p.bf16 = dt == WKV_BF16;
+    const int64_t seg = choose_segment(tokens * H, T, p.bf16);
+    const int64_t per = T == 0 ? 1 : (T + seg - 1) / seg;
+    if ((int64_t)B * per * H > INT32_MAX) return fail(WKV_EINVAL, "too many work items");
+    p.g.H = H;
+    p.g.n_seq = B;
+    p.g.seg_len = (int)seg;
+    p.g.n_seg = (int)(B * per);
+    p.g.total_tokens = tokens;
+    p.g.uniform_T = T;
+    p.g.segs_per_seq = (int)per;
+    p.split = per > 1;
+    layout_workspace(p, false);
+    return WKV_OK;
+}
+
+wkv_status_t plan_varlen(const int32_t *cu_host, int N, int H, int D, wkv_dtype_t dt, Plan &p) {
+    if (wkv_status_t s = check_common(H, D, dt)) return s;
+    if (N < 0) return fail(WKV_EINVAL, "N=%d must be >= 0", N);
+    if (!cu_host) return fail(WKV_EINVAL, "cu_seqlens_host is NULL");
+    if (cu_host[0] != 0) return fail(WKV_EINVAL, "cu_seqlens[0]=%d must be 0", cu_host[0]);
+    int64_t max_len = 0;
+    for (int n = 0; n < N; ++n) {
+        if (cu_host[n + 1] < cu_host[n])
+            return fail(WKV_EINVAL, "cu_seqlens decreases at %d (%d -> %d)", n, cu_host[n], cu_host[n + 1]);
+        max_len = std::max<int64_t>(max_len, (int64_t)cu_host[n + 1] - cu_host[n]);
+    }
+    const int64_t tokens = cu_host[N];
+    p.bf16 = dt == WKV_BF16;
+    const int64_t seg = choose_segment(tokens * H, max_len, p.bf16);
+    int64_t n_seg = 0;
+    bool split = false;
+    for (int n = 0; n < N; ++n) {
+        const int64_t L = (int64_t)cu_host[n + 1] - cu_host[n];
+        const int64_t P = L == 0 ? 1 : (L + seg - 1) / seg;
+        split |= P > 1;
+        n_seg += P;
+    }
+    if (n_seg * H > INT32_MAX) return fail(WKV_EINVAL, "too many work items");
+    p.g.H = H;
+    p.g.n_seq = N;
+    p.g.seg_len = (int)seg;
+    p.g.n_seg = (int)n_seg;
+    p.g.total_tokens = tokens;
+    p.g.uniform_T = -1;
+    p.g.segs_per_seq = 0;
+    p.split = split;
+    layout_workspace(p, true);
+    return WKV_OK;
+}
+
+// ---- pointer checks ---------------------------------------------------------
+
+struct Range {
+    const char *name;
+    uintptr_t lo, hi;   // [lo, hi)
+};
+
+bool misaligned(const void *p, size_t a) { return p && ((uintptr_t)p % a) != 0; }
+
+Range range_of(const char *name, const void *p, size_t bytes) {
+    uintptr_t lo = (uintptr_t)p;
+    return Range{name, lo, p ? lo + bytes : lo};
+}
+
+bool overlaps(const Range &a, const Range &b) {
+    return a.lo < a.hi && b.lo < b.hi && a.lo < b.hi && b.lo < a.hi;
+}
+
+wkv_status_t check_pointers(const Plan &p, const void *r, const void *k, const void *v,
+                            const void *w, const float *u, const float *state_in, const float *o,
+                            const float *state_out, const void *ws, size_t ws_bytes,
+                            const int32_t *cu_dev) {
+    const int64_t tokens = p.g.total_tokens;
+    const size_t elt = p.bf16 ? 2 : 4;
+    const size_t in_bytes = (size_t)tokens * p.g.H * kHeadDim * elt;
+    const size_t o_bytes = (size_t)tokens * p.g.H * kHeadDim * sizeof(float);
+    const size_t st_bytes = (size_t)p.g.n_seq * p.g.H * kHeadDim * kHeadDim * sizeof(float);
+    if (tokens > 0) {
+        const void *need[] = {r, k, v, w, u, o};
+        const char *names[] = {"r", "k", "v", "w", "u", "o"};
+        for (int i = 0; i < 6; ++i)
+            if (!need[i]) return fail(WKV_EINVAL, "%s is NULL", names[i]);
+    }
+    const void *al[] = {r, k, v, w, u, state_in, o, state_out};
+    const char *aln[] = {"r", "k", "v", "w", "u", "state_in", "o", "state_out"};
+    for (int i = 0; i < 8; ++i)
+        if (misaligned(al[i], 16)) return fail(WKV_EINVAL, "%s is not 16-byte aligned", aln[i]);
+    if (misaligned(cu_dev, 4)) return fail(WKV_EINVAL, "cu_seqlens_dev is not 4-byte aligned");
+    if (misaligned(ws, 256)) return fail(WKV_EINVAL, "workspace is not 256-byte aligned");
+    if (p.bytes > 0 && (!ws || ws_bytes < p.bytes))
+        return fail(WKV_EWORKSPACE, "workspace of %zu bytes given, %zu needed", ws ? ws_bytes : 0,
+                    p.bytes);
+
+    const size_t n_cu = cu_dev ? (size_t)(p.g.n_seq + 1) * sizeof(int32_t) : 0;
+    Range ins[] = {range_of("r", r, in_bytes), range_of("k", k, in_bytes),
+                   range_of("v", v, in_bytes), range_of("w", w, in_bytes),
+                   range_of("u", u, (size_t)p.g.H * kHeadDim * sizeof(float)),
+                   range_of("state_in", state_in, state_in ? st_bytes : 0),
+                   range_of("cu_seqlens_dev", cu_dev, n_cu),
+                   range_of("workspace", ws, p.bytes)};
+    Range outs[] = {range_of("o", o, o ? o_bytes : 0),
+                    range_of("state_out", state_out, state_out ? st_bytes : 0)};
+    for (const Range &out : outs) {
+        for (const Range &in : ins) {
+            if (out.name == std::string("state_out") && in.name == std::string("state_in") &&
+                out.lo == in.lo)
+                continue;                               // exact aliasing: carried state
+            if (overlaps(out, in))
+                return fail(WKV_EINVAL, "output %s overlaps %s", out.name, in.name);
+        }
+    }
+    if (overlaps(outs[0], outs[1])) return fail(WKV_EINVAL, "o overlaps state_out");
+    if (!cu_dev && p.g.uniform_T < 0) return fail(WKV_EINVAL, "cu_seqlens_dev is NULL");
+    return WKV_OK;
+}
+
+// ---- execution --------------------------------------------------------------
+
+wkv_status_t run(const Plan &p, const Tensors &t, void *ws, hipStream_t st) {
+    Geometry g = p.g;
+    char *base = static_cast<char *>(ws);
+    hipError_t e;
+    if (g.uniform_T < 0) {
+        int32_t *seg_off = reinterpret_cast<int32_t *>(base + p.off_seg_off);
+        int32_t *seg_seq = reinterpret_cast<int32_t *>(base + p.off_seg_seq);
+        if (g.n_seq == 0) return WKV_OK;
+        if ((e = launch_plan_varlen(g, seg_off, seg_seq, st)) != hipSuccess)
+            return fail_hip(e, "planner launch");
+        g.seg_off = seg_off;
+        g.seg_seq = seg_seq;
+    }
+    if ((e = launch_serial(g, t, p.bf16, st)) != hipSuccess) return fail_hip(e, "scan launch");
+    return WKV_OK;
+}
+
+}  // namespace
+}  // namespace finch
+
+using namespace finch;
+
+extern "C" {
+
+int wkv_abi_version(void) { return FINCH_WKV_ABI_VERSION; }
+
+const char *wkv_status_string(wkv_status_t s) {
+    switch (s) {
+    case WKV_OK: return "success";
+    case WKV_EINVAL: return "invalid argument";
+    case WKV_EUNSUPPORTED: return "unsupported size or dtype";
+    case WKV_EWORKSPACE: return "workspace missing or too small";
+    case WKV_EHIP: return "HIP runtime error";
+    }
+    return "unknown status";
+}
+
+const char *wkv_last_error(void) { return g_last_error.c_str(); }
+
+size_t wkv_prefill_workspace_bytes(int B, int T, int H, int D, wkv_dtype_t dt) {
+    Plan p;
+    std::string keep = g_last_error;
+    size_t bytes = plan_fixed(B, T, H, D, dt, p) == WKV_OK ? p.bytes : 0;
+    g_last_error = keep;
+    return bytes;
+}
+
+size_t wkv_prefill_varlen_workspace_bytes(const int32_t *cu_host, int N, int H, int D,
+                                          wkv_dtype_t dt) {
+    Plan p;
+    std::string keep = g_last_error;
+    size_t bytes = plan_varlen(cu_host, N, H, D, dt, p) == WKV_OK ? p.bytes : 0;
+    g_last_error = keep;
+    return bytes;
+}
+
+wkv_status_t wkv_prefill(const void *r, const void *k, const void *v, const void *w,
+                         const float *u, const float *state_in, float *o, float *state_out,
+                         int B, int T, int H, int D, wkv_dtype_t dt, void *ws, size_t ws_bytes,
+                         void *stream) {
+    g_last_error.clear();
+    Plan p;
+    if (wkv_status_t s = plan_fixed(B, T, H, D, dt, p)) return s;
+    if (wkv_status_t s = check_pointers(p, r, k, v, w, u, state_in, o, state_out, ws, ws_bytes,
+                                        nullptr))
+        return s;
+    Tensors t{r, k, v, w, u, state_in, o, state_out};
+    return run(p, t, ws, static_cast<hipStream_t>(stream));
+}
+
+wkv_status_t wkv_prefill_varlen(const void *r, const void *k, const void *v, const void *w,
+                                const float *u, const int32_t *cu_dev, const int32_t *cu_host,
+                                int N, const float *state_in, float *o, float *state_out, int H,
+                                int D, wkv_dtype_t dt, void *ws, size_t ws_bytes, void *stream) {
+    g_last_error.clear();
+    Plan p;
+    if (wkv_status_t s = plan_varlen(cu_host, N, H, D, dt, p)) return s;
+    if (N > 0 && !cu_dev) return fail(WKV_EINVAL, "cu_seqlens_dev is NULL");
+    if (wkv_status_t s = check_pointers(p, r, k, v, w, u, state_in, o, state_out, ws, ws_bytes,
+                                        cu_dev))
+        return s;
+    Tensors t{r, k, v, w, u, state_in, o, state_out};
+    return run(p, t, ws, static_cast<hipStream_t>(stream));
+}
+
+}  // extern "C"

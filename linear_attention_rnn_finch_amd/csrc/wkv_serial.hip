@@ -1,0 +1,105 @@
+// Token-serial WKV recurrence in fp32 for fp32 inputs (gfx950).
+//
+// Evaluates the recurrence of the GoldFinch architecture summary (section 3.4,
+// "Recurrent state update and output") exactly as written, one token after the
+// other, in fp32 arithmetic: o_t = r_t S + (r_t . u . k_t) v_t, then
+// S <- diag(w_t) S + k_t^T v_t.  Used for fp32 inputs, whose tolerance (1e-5
+// normwise) leaves no room for the bf16 matrix-core splits of the chunked
+// kernel.  One workgroup per (sequence, head); the 64x64 state lives in
+// registers: thread (q, j) owns rows 16q .. 16q+15 of value column j.
+#include "wkv_internal.h"
+
+namespace finch {
+namespace {
+
+constexpr int kBlockTokens = 32;   // tokens staged in LDS per step
+
+__device__ inline float load_in(const float *p, size_t i) { return p[i]; }
+__device__ inline float load_in(const uint16_t *p, size_t i) {
+    return __uint_as_float((uint32_t)p[i] << 16);
+}
+
+template <typename In>
+__global__ __launch_bounds__(256) void wkv_serial_kernel(Geometry g, Tensors t) {
+    const int item = blockIdx.x;
+    const int h = item % g.H;
+    const ItemRange it = decode_segment(g, item / g.H);
+    if (!it.valid) return;                      // uniform across the workgroup
+
+    const int tid = threadIdx.x;
+    const int j = tid & 63;                     // value column owned by this thread
+    const int q = tid >> 6;                     // row quarter
+
+    __shared__ float tr[kBlockTokens][kHeadDim];
+    __shared__ float tk[kBlockTokens][kHeadDim];
+    __shared__ float tv[kBlockTokens][kHeadDim];
+    __shared__ float tw[kBlockTokens][kHeadDim];
+    __shared__ float part[4][kBlockTokens][kHeadDim];
+    __shared__ float bonus[kBlockTokens];
+    __shared__ float us[kHeadDim];
+
+    const In *rp = static_cast<const In *>(t.r);
+    const In *kp = static_cast<const In *>(t.k);
+    const In *vp = static_cast<const In *>(t.v);
+    const In *wp = static_cast<const In *>(t.w);
+
+    float S[16];
+    const size_t state_off = ((size_t)it.n * g.H + h) * (kHeadDim * kHeadDim);
+    #pragma unroll
+    for (int e = 0; e < 16; ++e)
+        S[e] = t.state_in ? t.state_in[state_off + (16 * q + e) * kHeadDim + j] : 0.f;
+    if (tid < kHeadDim) us[tid] = t.u[(size_t)h * kHeadDim + tid];
+
+    for (int64_t tb = it.t0; tb < it.t1; tb += kBlockTokens) {
+        const int nt = (int)min<int64_t>(kBlockTokens, it.t1 - tb);
+        __syncthreads();                        // previous block fully consumed
+        for (int row = q; row < nt; row += 4) {
+            const size_t idx = ((size_t)(tb + row) * g.H + h) * kHeadDim + j;
+            tr[row][j] = load_in(rp, idx);
+            tk[row][j] = load_in(kp, idx);
+            tv[row][j] = load_in(vp, idx);
+            tw[row][j] = load_in(wp, idx);
+        }
+        __syncthreads();
+        if (tid < nt) {                         // bonus r_t . u . k_t per token
+            float b = 0.f;
+            for (int i = 0; i < kHeadDim; ++i) b += tr[tid][i] * us[i] * tk[tid][i];
+            bonus[tid] = b;
+        }
+        for (int tt = 0; tt < nt; ++tt) {
+            float acc = 0.f;
+            #pragma unroll
+            for (int e = 0; e < 16; ++e) acc += tr[tt][16 * q + e] * S[e];
+            part[q][tt][j] = acc;
+            const float vj = tv[tt][j];
+            #pragma unroll
+            for (int e = 0; e < 16; ++e)
+                S[e] = tw[tt][16 * q + e] * S[e] + tk[tt][16 * q + e] * vj;
+        }
+        __syncthreads();
+        for (int row = q; row < nt; row += 4) {
+            const float o = part[0][row][j] + part[1][row][j] + part[2][row][j] +
+                            part[3][row][j] + bonus[row] * tv[row][j];
+            t.o[((size_t)(tb + row) * g.H + h) * kHeadDim + j] = o;
+        }
+    }
+    if (t.state_out && it.p == it.P - 1) {
+        #pragma unroll
+        for (int e = 0; e < 16; ++e)
+            t.state_out[state_off + (16 * q + e) * kHeadDim + j] = S[e];
+    }
+}
+
+}  // namespace
+
+hipError_t launch_serial(const Geometry &g, const Tensors &t, bool bf16, hipStream_t st) {
+    const int64_t items = (int64_t)g.n_seg * g.H;
+    if (items <= 0) return hipSuccess;
+    if (bf16)
+        hipLaunchKernelGGL(wkv_serial_kernel<uint16_t>, dim3((unsigned)items), dim3(256), 0, st, g, t);
+    else
+        hipLaunchKernelGGL(wkv_serial_kernel<float>, dim3((unsigned)items), dim3(256), 0, st, g, t);
+    return hipGetLastError();
+}
+
+}  // namespace finch

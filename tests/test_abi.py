@@ -1,0 +1,161 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function the
+public header declares, and rejects bad arguments before any HIP call.
+
+Fake device addresses are plain integers here; every call below fails
+validation, so nothing is ever dereferenced or launched.
+"""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "finch_wkv.h")
+LIB = os.path.join(ROOT, "linear_attention_rnn_finch_amd", "libfinch_wkv.so")
+
+OK, EINVAL, EUNSUP, EWS, EHIP = range(5)
+F32, BF16 = 0, 1
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(wkv_[a-z_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(LIB):
+        pytest.skip("library not built")
+    L = ctypes.CDLL(LIB)
+    vp, sz, i = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int
+    L.wkv_prefill.restype = i
+    L.wkv_prefill.argtypes = [vp] * 8 + [i] * 5 + [vp, sz, vp]
+    L.wkv_prefill_varlen.restype = i
+    L.wkv_prefill_varlen.argtypes = [vp] * 7 + [i, vp, vp, vp, i, i, i, vp, sz, vp]
+    L.wkv_prefill_workspace_bytes.restype = sz
+    L.wkv_prefill_workspace_bytes.argtypes = [i] * 5
+    L.wkv_prefill_varlen_workspace_bytes.restype = sz
+    L.wkv_prefill_varlen_workspace_bytes.argtypes = [vp, i, i, i, i]
+    L.wkv_last_error.restype = ctypes.c_char_p
+    L.wkv_status_string.restype = ctypes.c_char_p
+    L.wkv_status_string.argtypes = [i]
+    return L
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = declared_functions()
+    assert "wkv_prefill" in names and "wkv_prefill_varlen" in names
+    for n in names:
+        assert hasattr(lib, n), "missing export %s" % n
+
+
+def test_abi_version_and_status_strings(lib):
+    assert lib.wkv_abi_version() == 1
+    for s in range(5):
+        assert lib.wkv_status_string(s)
+    assert lib.wkv_status_string(99) == b"unknown status"
+
+
+# distinct, aligned fake device addresses, far apart
+A = 1 << 40
+R, K, V, W, U, S_IN, O, S_OUT, WS = (A * (n + 1) for n in range(9))
+
+
+def call(lib, B=1, T=128, H=4, D=64, dt=BF16, r=R, k=K, v=V, w=W, u=U, s_in=S_IN, o=O,
+         s_out=S_OUT, ws=WS, ws_bytes=None):
+    if ws_bytes is None:
+        ws_bytes = lib.wkv_prefill_workspace_bytes(B, T, H, D, dt)
+    st = lib.wkv_prefill(r, k, v, w, u, s_in, o, s_out, B, T, H, D, dt, ws, ws_bytes, None)
+    return st, lib.wkv_last_error().decode()
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(D=32), EUNSUP),
+    (dict(D=128), EUNSUP),
+    (dict(dt=7), EUNSUP),
+    (dict(H=0), EINVAL),
+    (dict(B=0), EINVAL),
+    (dict(T=-1), EINVAL),
+    (dict(B=70000, T=70000), EINVAL),
+    (dict(r=None), EINVAL),
+    (dict(w=None), EINVAL),
+    (dict(u=None), EINVAL),
+    (dict(o=None), EINVAL),
+    (dict(k=K + 2), EINVAL),                  # misaligned
+    (dict(o=O + 4), EINVAL),
+    (dict(s_in=S_IN + 8), EINVAL),
+    (dict(o=R + 64), EINVAL),                 # output overlaps an input
+    (dict(s_out=O + 1024), EINVAL),           # state_out inside o
+    (dict(s_out=S_IN + 256), EINVAL),         # partial overlap with state_in
+])
+def test_fixed_length_validation(lib, kw, expect):
+    st, msg = call(lib, **kw)
+    assert st == expect, (st, msg)
+    assert msg
+
+
+def test_workspace_checks(lib):
+    need = lib.wkv_prefill_workspace_bytes(1, 4096, 32, 64, BF16)
+    assert need > 0                                   # a split plan needs scratch
+    st, msg = call(lib, T=4096, H=32, ws=None)
+    assert st == EWS, msg
+    st, msg = call(lib, T=4096, H=32, ws_bytes=need - 1)
+    assert st == EWS, msg
+    st, msg = call(lib, T=4096, H=32, ws=WS + 128)
+    assert st == EINVAL and "aligned" in msg
+    st, msg = call(lib, T=4096, H=32, ws=O + 256)     # workspace overlaps o
+    assert st == EINVAL, msg
+    assert lib.wkv_prefill_workspace_bytes(1, 64, 1, 64, F32) == 0
+    assert lib.wkv_prefill_workspace_bytes(1, 64, 1, 32, BF16) == 0    # invalid -> 0
+    # the query does not disturb the last error
+    call(lib, D=32)
+    before = lib.wkv_last_error()
+    lib.wkv_prefill_workspace_bytes(1, 64, 1, 32, BF16)
+    assert lib.wkv_last_error() == before
+
+
+def varlen(lib, cu, H=4, dt=BF16, ws_bytes=None, cu_dev=A * 20, **ptrs):
+    cu = np.asarray(cu, dtype=np.int32)
+    N = len(cu) - 1
+    p = dict(r=R, k=K, v=V, w=W, u=U, s_in=S_IN, o=O, s_out=S_OUT, ws=WS)
+    p.update(ptrs)
+    if ws_bytes is None:
+        ws_bytes = lib.wkv_prefill_varlen_workspace_bytes(cu.ctypes.data, N, H, 64, dt)
+    st = lib.wkv_prefill_varlen(p["r"], p["k"], p["v"], p["w"], p["u"], cu_dev, cu.ctypes.data,
+                                N, p["s_in"], p["o"], p["s_out"], H, 64, dt, p["ws"], ws_bytes,
+                                None)
+    return st, lib.wkv_last_error().decode()
+
+
+@pytest.mark.parametrize("cu,expect", [
+    ([1, 5, 9], EINVAL),          # must start at 0
+    ([0, 5, 3], EINVAL),          # decreasing
+])
+def test_varlen_offset_validation(lib, cu, expect):
+    st, msg = varlen(lib, cu)
+    assert st == expect, msg
+    c = np.asarray(cu, dtype=np.int32)
+    assert lib.wkv_prefill_varlen_workspace_bytes(c.ctypes.data, len(c) - 1, 4, 64, BF16) == 0
+
+
+def test_varlen_pointer_validation(lib):
+    st, msg = varlen(lib, [0, 100, 300], cu_dev=None)
+    assert st == EINVAL and "cu_seqlens_dev" in msg
+    st, msg = varlen(lib, [0, 100, 300], cu_dev=A * 20 + 2)
+    assert st == EINVAL
+    st, msg = varlen(lib, [0, 100, 300], ws=None)
+    assert st == EWS
+    st, msg = varlen(lib, [0, 100, 300], o=A * 20)            # o overlaps the offsets
+    assert st == EINVAL
+
+
+def test_varlen_workspace_grows_with_segments(lib):
+    small = np.array([0, 100, 300], dtype=np.int32)
+    big = np.array([0, 30000, 60000, 200000], dtype=np.int32)
+    a = lib.wkv_prefill_varlen_workspace_bytes(small.ctypes.data, 2, 32, 64, BF16)
+    b = lib.wkv_prefill_varlen_workspace_bytes(big.ctypes.data, 3, 32, 64, BF16)
+    assert 0 < a < b
+    assert a % 256 == 0 and b % 256 == 0

@@ -1,0 +1,150 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle.
+
+Tolerances are the normwise per-(sequence, head) block errors of the
+specification: 2e-3 for bf16 inputs (fp32 state and accumulation), 1e-5 for
+fp32 inputs.  Reduced sizes keep the oracle at a few seconds while spanning
+several chunks and a ragged tail; full-size workloads compare every slice the
+oracle can afford and sample the rest.
+"""
+import numpy as np
+import pytest
+
+from synth import make_workload, get_config
+from gpu_util import log, to_gpu, run_gpu, run_oracle, errors
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+def _check(wl, heads=None, tol=None, **kw):
+    tol = tol if tol is not None else wl.config.tolerance
+    log("case %s B=%d H=%d tokens=%d heads=%s" % (wl.config.name, wl.n_seq, wl.u.shape[0],
+                                                 wl.tokens, heads))
+    o, s = run_gpu(wl, **kw)
+    torch.cuda.synchronize()
+    o_ref, s_ref = run_oracle(wl, heads)
+    eo, es = errors(wl, o, s, o_ref, s_ref, heads)
+    log("  err o=%.3e state=%.3e (tol %.0e)" % (eo, es, tol))
+    assert np.isfinite(eo) and np.isfinite(es)
+    assert eo <= tol and es <= tol, (eo, es)
+    return o, s
+
+
+def test_tiny_f32_config():
+    _check(make_workload(0))
+
+
+@pytest.mark.parametrize("T", [1, 2, 63, 64, 65, 200, 1000])
+def test_bf16_short_sequences(T):
+    _check(make_workload(1, T=T, H=4))
+
+
+def test_bf16_with_initial_state_and_batch():
+    wl = make_workload(3, B=3, T=777, H=5)          # long-context distributions, random S_0
+    _check(wl)
+
+
+def test_f32_ragged_and_state():
+    wl = make_workload(0, lengths=[70, 1, 0, 130], H=2)
+    wl.state0 = np.random.default_rng(3).normal(0, 0.1, size=(4, 2, 64, 64)).astype(np.float32)
+    _check(wl)
+
+
+def test_layer_shape_full_size():
+    """T=4096, H=32 (d_model 2048): every slice against the oracle."""
+    _check(make_workload(1))
+
+
+def test_ragged_reduced():
+    wl = make_workload(4, lengths=[1024, 3, 0, 2500, 64, 4097], H=4)
+    _check(wl)
+
+
+def test_zero_length_passes_state_through():
+    wl = make_workload(3, B=2, T=0, H=3)
+    g = to_gpu(wl)
+    o, s = run_gpu(wl, g)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(s.cpu().numpy(), wl.state0)
+    wl2 = make_workload(1, B=2, T=0, H=3)
+    o2, s2 = run_gpu(wl2)
+    torch.cuda.synchronize()
+    assert float(s2.abs().max()) == 0.0
+
+
+def test_state_in_aliases_state_out():
+    wl = make_workload(3, B=2, T=300, H=3)
+    g = to_gpu(wl)
+    o_ref, s_ref = run_gpu(wl, g)
+    carried = g["state0"].clone()
+    o2, s2 = run_gpu(wl, g, state_in=carried, state_out=carried)
+    torch.cuda.synchronize()
+    assert s2.data_ptr() == carried.data_ptr()
+    assert torch.equal(o2, o_ref) and torch.equal(carried, s_ref)
+
+
+def test_carried_state_chain_equals_single_pass():
+    wl = make_workload(1, T=1000, H=4)
+    g = to_gpu(wl)
+    o_full, s_full = run_gpu(wl, g)
+    cuts = [0, 1, 130, 512, 1000]
+    state = None
+    outs = []
+    import linear_attention_rnn_finch_amd as fw
+    for a, z in zip(cuts[:-1], cuts[1:]):
+        o, state = fw.prefill(g["r"][:, a:z].contiguous(), g["k"][:, a:z].contiguous(),
+                              g["v"][:, a:z].contiguous(), g["w"][:, a:z].contiguous(),
+                              g["u"], state)
+        outs.append(o)
+    torch.cuda.synchronize()
+    o_chain = torch.cat(outs, dim=1)
+    o_ref, s_ref = run_oracle(wl)
+    eo, es = errors(wl, o_chain, state, o_ref, s_ref)
+    assert eo <= 2e-3 and es <= 2e-3
+    eo2, es2 = errors(wl, o_chain, state, o_full.cpu().numpy().astype(np.float64),
+                      s_full.cpu().numpy().astype(np.float64))
+    assert eo2 <= 2e-3 and es2 <= 2e-3
+
+
+def test_deterministic():
+    wl = make_workload(1, T=700, H=8)
+    g = to_gpu(wl)
+    o1, s1 = run_gpu(wl, g)
+    o2, s2 = run_gpu(wl, g)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(s1, s2)
+
+
+def test_guard_bands_untouched():
+    wl = make_workload(1, T=130, H=2)
+    g = to_gpu(wl)
+    B, T, H, D = 1, 130, 2, 64
+    pad = 4096
+    o_buf = torch.full((pad + B * T * H * D + pad,), 12345.0, device="cuda")
+    s_buf = torch.full((pad + B * H * D * D + pad,), -777.0, device="cuda")
+    o = o_buf[pad:pad + B * T * H * D].view(B, T, H, D)
+    s = s_buf[pad:pad + B * H * D * D].view(B, H, D, D)
+    run_gpu(wl, g, o=o, state_out=s)
+    torch.cuda.synchronize()
+    assert torch.all(o_buf[:pad] == 12345.0) and torch.all(o_buf[-pad:] == 12345.0)
+    assert torch.all(s_buf[:pad] == -777.0) and torch.all(s_buf[-pad:] == -777.0)
+    o_ref, s_ref = run_oracle(wl)
+    eo, es = errors(wl, o, s, o_ref, s_ref)
+    assert eo <= 2e-3 and es <= 2e-3
+
+
+def test_validation_errors_raise():
+    """An output overlapping another buffer is rejected before any launch."""
+    import linear_attention_rnn_finch_amd as fw
+    wl = make_workload(1, T=64, H=2)
+    g = to_gpu(wl)
+    B, T, H, D = g["r"].shape
+    big = torch.zeros(B * T * H * D, dtype=torch.float32, device="cuda")
+    o = big.view(B, T, H, D)
+    st = big[: B * H * D * D].view(B, H, D, D)       # state_out inside o
+    with pytest.raises(fw.WkvError) as ei:
+        fw.prefill(g["r"], g["k"], g["v"], g["w"], g["u"], None, o=o, state_out=st)
+    assert ei.value.status == 1
+    torch.cuda.synchronize()
+    assert float(big.abs().max()) == 0.0              # nothing was written
