@@ -219,6 +219,7 @@ wkv_status_t run(const Plan &p, const Tensors &t, void *ws, hipStream_t st) {
     char *base = static_cast<char *>(ws);
     hipError_t e;
     if (g.uniform_T < 0) {
+        if (!g.cu) return fail(WKV_EINVAL, "packed launch without device offsets");
         int32_t *seg_off = reinterpret_cast<int32_t *>(base + p.off_seg_off);
         int32_t *seg_seq = reinterpret_cast<int32_t *>(base + p.off_seg_seq);
         if (g.n_seq == 0) return WKV_OK;
@@ -227,7 +228,16 @@ wkv_status_t run(const Plan &p, const Tensors &t, void *ws, hipStream_t st) {
         g.seg_off = seg_off;
         g.seg_seq = seg_seq;
     }
-    if ((e = launch_serial(g, t, p.bf16, st)) != hipSuccess) return fail_hip(e, "scan launch");
+    if (!p.bf16) {
+        if ((e = launch_serial(g, t, false, st)) != hipSuccess) return fail_hip(e, "scan launch");
+        return WKV_OK;
+    }
+    Workspace w{};
+    if (p.split) {
+        w.seg_state = reinterpret_cast<float *>(base + p.off_seg_state);
+        w.seg_start = reinterpret_cast<float *>(base + p.off_seg_start);
+    }
+    if ((e = launch_chunked(g, t, w, p.split, st)) != hipSuccess) return fail_hip(e, "scan launch");
     return WKV_OK;
 }
 
@@ -295,6 +305,7 @@ wkv_status_t wkv_prefill_varlen(const void *r, const void *k, const void *v, con
     if (wkv_status_t s = check_pointers(p, r, k, v, w, u, state_in, o, state_out, ws, ws_bytes,
                                         cu_dev))
         return s;
+    p.g.cu = cu_dev;
     Tensors t{r, k, v, w, u, state_in, o, state_out};
     return run(p, t, ws, static_cast<hipStream_t>(stream));
 }

@@ -98,6 +98,8 @@ constexpr int kSegStartFloats = kHeadDim * kHeadDim;
 
 // Launchers (defined in the .hip files).
 hipError_t launch_serial(const Geometry &g, const Tensors &t, bool bf16, hipStream_t st);
+hipError_t launch_chunked(const Geometry &g, const Tensors &t, const Workspace &ws, bool split,
+                          hipStream_t st);
 hipError_t launch_plan_varlen(const Geometry &g, int32_t *seg_off, int32_t *seg_seq,
                               hipStream_t st);
 
