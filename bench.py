@@ -1,0 +1,256 @@
+#!/usr/bin/env python3
+"""Finch WKV pre-fill benchmark on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 1]
+
+One step = one complete pre-fill call (segment state pass, segment scan and
+the chunked scan: every step of the path) over the synthetic workload, inputs
+already resident in HBM.  The K timed steps are captured once into a HIP graph
+and replayed, bracketed by device synchronisations, so host launch overhead is
+not part of the figure.  The main chunked-scan kernel is also timed per launch
+with HIP events recorded on its own stream (through the library's timing
+hook), which gives the roofline figure.  The fp64 CPU oracle is timed on the
+host cores over a bounded sample of the same workload (cpu_baseline).
+
+Prints ONE JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "WKV pre-fill tokens/s at d_model 2048, T=4096; % of HBM/MFMA roofline"
+HBM_PEAK_GBS = 8000.0            # MI355X HBM3E, GB/s
+
+
+def algorithmic_bytes(cfg, tokens, n_seq, has_state_in):
+    """r, k, v, w in (bf16 or fp32) + o out (fp32) per token and head, plus the
+    fp32 state out (and in, when given) per (sequence, head)."""
+    elt = 2 if cfg.dtype == "bf16" else 4
+    per_token = cfg.H * cfg.D * (4 * elt + 4)
+    per_state = cfg.D * cfg.D * 4 * (2 if has_state_in else 1)
+    return tokens * per_token + n_seq * cfg.H * per_state
+
+
+def hip_runtime():
+    hip = ctypes.CDLL("libamdhip64.so")
+    hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+    hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                        ctypes.c_void_p]
+    hip.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+    hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+    return hip
+
+
+def time_main_kernel(call, n, hip, lib, torch):
+    """Average duration (ms) of the main scan kernel over n calls, from HIP
+    events the library records around that launch.  A device-side sleep keeps
+    the GPU busy while the host enqueues, so no launch gap falls inside an
+    event pair."""
+    evs = []
+    for _ in range(2 * n):
+        e = ctypes.c_void_p()
+        if hip.hipEventCreate(ctypes.byref(e)) != 0:
+            raise RuntimeError("hipEventCreate failed")
+        evs.append(e)
+    torch.cuda.synchronize()
+    torch.cuda._sleep(50_000_000)
+    for i in range(n):
+        lib.wkv_set_kernel_timing_events(evs[2 * i], evs[2 * i + 1])
+        call()
+    lib.wkv_set_kernel_timing_events(None, None)
+    torch.cuda.synchronize()
+    total = 0.0
+    ms = ctypes.c_float()
+    durations = []
+    for i in range(n):
+        hip.hipEventElapsedTime(ctypes.byref(ms), evs[2 * i], evs[2 * i + 1])
+        durations.append(ms.value)
+        total += ms.value
+    for e in evs:
+        hip.hipEventDestroy(e)
+    durations.sort()
+    return total / n, durations[len(durations) // 2]
+
+
+def cpu_baseline(wl, target_seconds):
+    """Time the fp64 oracle on the host over whole passes of the workload (all
+    slices), repeating until about target_seconds of work; returns the record
+    and the oracle outputs of the last pass."""
+    import oracle
+    threads = len(os.sched_getaffinity(0))
+    if os.environ.get("OMP_NUM_THREADS", "").isdigit():
+        threads = min(threads, int(os.environ["OMP_NUM_THREADS"]))
+    passes, t0, out = 0, time.perf_counter(), None
+    while True:
+        out = oracle.wkv_scan(wl.r, wl.k, wl.v, wl.w, wl.u, wl.state0, wl.cu_seqlens,
+                              threads=threads)
+        passes += 1
+        el = time.perf_counter() - t0
+        if el >= target_seconds or passes >= 64:
+            break
+    tokens = wl.tokens * passes
+    rec = {"value": tokens / el, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+           "sample": "%d full pass(es) of the %s workload (%d tokens x %d heads), fp64 "
+                     "sequential recurrence, OpenMP over (sequence, head) slices, %.1f s"
+                     % (passes, wl.config.name, wl.tokens, wl.u.shape[0], el)}
+    return rec, out
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--config", default="1", help="workload index or name (default: 1)")
+    ap.add_argument("--kernel-samples", type=int, default=100)
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="time eager calls instead of a graph replay (for profiler runs)")
+    ap.add_argument("--copy-mb", type=int, default=0,
+                    help="first run a plain device copy of this many MiB (counter calibration)")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(--gpus %d requested)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    import linear_attention_rnn_finch_amd as fw
+    from linear_attention_rnn_finch_amd import _binding
+    from synth import make_workload, get_config, max_block_error
+
+    cfg = get_config(int(args.config) if args.config.isdigit() else args.config)
+    wl = make_workload(cfg)
+    dev = torch.device("cuda", 0)
+
+    def cvt(a):
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(a).to(dev)
+
+    r, k, v, w = (cvt(getattr(wl, n)) for n in ("r", "k", "v", "w"))
+    u = torch.from_numpy(wl.u).to(dev)
+    s0 = None if wl.state0 is None else torch.from_numpy(wl.state0).to(dev)
+    n_seq = wl.n_seq
+    if wl.packed:
+        cu = torch.from_numpy(wl.cu_seqlens.astype(np.int32)).to(dev)
+        cu_host = torch.from_numpy(wl.cu_seqlens.astype(np.int32))
+        o = torch.empty((wl.tokens, cfg.H, cfg.D), dtype=torch.float32, device=dev)
+        ws_bytes = fw.varlen_workspace_bytes(cu_host, cfg.H, cfg.D, r.dtype)
+    else:
+        o = torch.empty((cfg.B, cfg.T, cfg.H, cfg.D), dtype=torch.float32, device=dev)
+        ws_bytes = fw.workspace_bytes(cfg.B, cfg.T, cfg.H, cfg.D, r.dtype)
+    st = torch.empty((n_seq, cfg.H, cfg.D, cfg.D), dtype=torch.float32, device=dev)
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+
+    def call():
+        if wl.packed:
+            fw.prefill_varlen(r, k, v, w, u, cu, s0, cu_seqlens_host=cu_host, o=o,
+                              state_out=st, workspace=ws)
+        else:
+            fw.prefill(r, k, v, w, u, s0, o=o, state_out=st, workspace=ws)
+
+    if args.copy_mb > 0:                          # known-size copy for counter scaling
+        src = torch.empty(args.copy_mb << 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    # warm-up (eager)
+    for _ in range(args.warmup):
+        call()
+    torch.cuda.synchronize()
+
+    if args.no_graph:
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            call()
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+    else:
+        # capture K steps into one HIP graph on a side stream
+        graph = torch.cuda.CUDAGraph()
+        cap = torch.cuda.Stream()
+        cap.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(cap):
+            call()                               # first use on this stream
+            torch.cuda.synchronize()
+            with torch.cuda.graph(graph, stream=cap):
+                for _ in range(args.steps):
+                    call()
+        torch.cuda.synchronize()
+        graph.replay()                           # warm replay
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        graph.replay()
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    tokens_per_step = wl.tokens
+    value = tokens_per_step / (ms_per_step * 1e-3)
+
+    # main kernel duration, live HIP events
+    hip = hip_runtime()
+    lib = _binding._lib
+    lib.wkv_set_kernel_timing_events.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+    k_avg_ms, k_med_ms = time_main_kernel(call, args.kernel_samples, hip, lib, torch)
+    alg = algorithmic_bytes(cfg, wl.tokens, n_seq, s0 is not None)
+    achieved = alg / (k_avg_ms * 1e-3) / 1e9
+    step_gbs = alg / (ms_per_step * 1e-3) / 1e9
+
+    rec = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg.dtype,
+        "data": "synthetic",
+        "config": {"workload": cfg.name, "B": cfg.B, "T": cfg.T, "H": cfg.H, "D": cfg.D,
+                   "d_model": cfg.H * cfg.D, "tokens": wl.tokens,
+                   "timing": ("eager calls" if args.no_graph else
+                              "HIP graph of %d captured calls, one replay" % args.steps)},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": None,
+                     "kernel": "wkv_chunk_kernel<Main>",
+                     "kernel_avg_us": round(k_avg_ms * 1e3, 2),
+                     "kernel_median_us": round(k_med_ms * 1e3, 2),
+                     "algorithmic_bytes_per_launch": alg,
+                     "whole_step_GBps": round(step_gbs, 1),
+                     "whole_step_frac": round(step_gbs / HBM_PEAK_GBS, 4)},
+    }
+
+    if not args.no_cpu_baseline:
+        cpu_rec, (o_ref, s_ref) = cpu_baseline(wl, args.cpu_seconds)
+        rec["cpu_baseline"] = cpu_rec
+        call()
+        torch.cuda.synchronize()
+        rec["parity"] = {
+            "max_block_err_o": float(max_block_error(o.cpu().numpy(), o_ref, wl.cu_seqlens)),
+            "max_block_err_state": float(max_block_error(st.cpu().numpy(), s_ref, kind="state")),
+            "tol": cfg.tolerance}
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

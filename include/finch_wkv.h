@@ -140,6 +140,18 @@ wkv_status_t wkv_prefill_varlen(const void *r, const void *k, const void *v,
                                 void *workspace, size_t workspace_bytes,
                                 void *stream);
 
+/*
+ * Kernel timing hook for profiling tools (the benchmark uses it).  When
+ * event_before/event_after (hipEvent_t, cast to void *) are non-NULL, every
+ * later pre-fill call made from the calling thread records event_before on
+ * its stream immediately before the launch of its main chunked-scan kernel and
+ * event_after immediately after it, so hipEventElapsedTime gives that
+ * kernel's duration alone.  Pass NULL, NULL to stop.  The events are owned by
+ * the caller and must outlive the calls that record them.  Per thread; always
+ * returns WKV_OK.
+ */
+wkv_status_t wkv_set_kernel_timing_events(void *event_before, void *event_after);
+
 #ifdef __cplusplus
 }
 #endif

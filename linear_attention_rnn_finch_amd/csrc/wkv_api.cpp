@@ -16,6 +16,8 @@ namespace finch {
 namespace {
 
 thread_local std::string g_last_error;
+thread_local hipEvent_t g_ev_before = nullptr;   // optional timing of the main kernel
+thread_local hipEvent_t g_ev_after = nullptr;
 
 wkv_status_t fail(wkv_status_t st, const char *fmt, ...) {
     char buf[512];
@@ -229,7 +231,11 @@ wkv_status_t run(const Plan &p, const Tensors &t, void *ws, hipStream_t st) {
         g.seg_seq = seg_seq;
     }
     if (!p.bf16) {
+        if (g_ev_before && (e = hipEventRecord(g_ev_before, st)) != hipSuccess)
+            return fail_hip(e, "timing event");
         if ((e = launch_serial(g, t, false, st)) != hipSuccess) return fail_hip(e, "scan launch");
+        if (g_ev_after && (e = hipEventRecord(g_ev_after, st)) != hipSuccess)
+            return fail_hip(e, "timing event");
         return WKV_OK;
     }
     Workspace w{};
@@ -237,7 +243,13 @@ wkv_status_t run(const Plan &p, const Tensors &t, void *ws, hipStream_t st) {
         w.seg_state = reinterpret_cast<float *>(base + p.off_seg_state);
         w.seg_start = reinterpret_cast<float *>(base + p.off_seg_start);
     }
-    if ((e = launch_chunked(g, t, w, p.split, st)) != hipSuccess) return fail_hip(e, "scan launch");
+    if (p.split && (e = launch_segment_states(g, t, w, st)) != hipSuccess)
+        return fail_hip(e, "segment-state launch");
+    if (g_ev_before && (e = hipEventRecord(g_ev_before, st)) != hipSuccess)
+        return fail_hip(e, "timing event");
+    if ((e = launch_chunked_main(g, t, w, st)) != hipSuccess) return fail_hip(e, "scan launch");
+    if (g_ev_after && (e = hipEventRecord(g_ev_after, st)) != hipSuccess)
+        return fail_hip(e, "timing event");
     return WKV_OK;
 }
 
@@ -262,6 +274,12 @@ const char *wkv_status_string(wkv_status_t s) {
 }
 
 const char *wkv_last_error(void) { return g_last_error.c_str(); }
+
+wkv_status_t wkv_set_kernel_timing_events(void *before, void *after) {
+    g_ev_before = static_cast<hipEvent_t>(before);
+    g_ev_after = static_cast<hipEvent_t>(after);
+    return WKV_OK;
+}
 
 size_t wkv_prefill_workspace_bytes(int B, int T, int H, int D, wkv_dtype_t dt) {
     Plan p;

@@ -26,9 +26,11 @@
 // Workgroup = 4 waves, one (segment, head) work item.  Wave w owns value
 // columns 16w..16w+15 of the state and of o; lane (i16 = lane%16, grp =
 // lane/16) holds S[16*ib + 4*grp + e][16*w + i16] for ib, e in 0..3 (the
-// accumulator layout of the 16x16 MFMA).  LDS holds every operand tile in
-// natural row-major [token][channel] order; transposed operands (contraction
-// over tokens) are read with ds_read_b64_tr_b16.
+// accumulator layout of the 16x16 MFMA).  r, k, w are loaded from memory
+// straight into the pre-processing layout; LDS holds every MFMA operand tile
+// row-major [token][channel] with a row-dependent XOR swizzle of its column
+// units (bank-conflict free); operands contracted over tokens are read with
+// ds_read_b64_tr_b16.
 #include "wkv_internal.h"
 
 namespace finch {
@@ -42,23 +44,41 @@ typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
-constexpr int kPitch = 72;                    // bf16 per LDS tile row (64 + 8 padding)
-constexpr int kTile = kChunk * kPitch;        // bf16 per tile
 constexpr float kStiffLog2 = 96.f;            // largest |half-chunk log2 decay| rescaled
 constexpr float kLog2Floor = -127.f;          // log2 w below this only occurs in stiff chunks
 constexpr unsigned kOnePair = 0x3F803F80u;    // two bf16 1.0 (padding value of w)
+constexpr int kTileElems = kChunk * kHeadDim; // one 64 x 64 bf16 tile
 
 enum class Mode { Main, State };
 
+// ---- LDS tile layouts ---------------------------------------------------------
+// Every tile is 64 rows x 64 bf16 (128 B per row, no padding).  Column units
+// are XOR-swizzled with a function of the low four row bits, which keeps the
+// MFMA operand reads free of bank conflicts (32 banks x 4 B) while every access
+// address stays "per-lane base + compile-time constant":
+//   rt, a : 8-byte unit u -> u ^ (r & 15)
+//   kt    : 8-byte unit u -> u ^ g(r & 15), g swaps the two bit pairs
+//   v     : 16-byte unit u -> u ^ ((r & 3) << 1)
+__device__ __forceinline__ int g_kt(int x) { return (x >> 2) | ((x & 3) << 2); }
+__device__ __forceinline__ int off_v(int r, int c) {
+    return r * 64 + ((((c >> 3) ^ ((r & 3) << 1)) << 3) | (c & 7));
+}
+
+// Target of the o stores of rows past the end of a partial last chunk.  Every
+// global memory operation inside the chunk loop is issued unconditionally, so
+// the compiler can wait for exactly the prefetched loads it needs instead of
+// draining all outstanding stores; lanes with nothing to store write here.
+// Never read.
+__device__ __attribute__((aligned(256))) float g_store_sink[64 * 4];
+
 struct Smem {
-    uint16_t raw_r[kTile];   // raw chunk tiles; after pre-processing raw_r/raw_k
-    uint16_t raw_k[kTile];   // hold the hi/lo planes of the in-chunk matrix A
-    uint16_t raw_w[kTile];
-    uint16_t raw_v[kTile];
-    uint16_t rt_hi[kTile];   // r~ split
-    uint16_t rt_lo[kTile];
-    uint16_t kt_hi[kTile];   // k~ split (k^ = k 2^{Lam_63 - Lam} in the state pass)
-    uint16_t kt_lo[kTile];
+    uint16_t v[kTileElems];          // values of the chunk
+    uint16_t rt_hi[kTileElems];      // r~ = r 2^{Lam_{t-1}-R}, bf16 hi/lo planes
+    uint16_t rt_lo[kTileElems];
+    uint16_t kt_hi[kTileElems];      // k~ = k 2^{R-Lam_s} (state pass: k 2^{Lam_63-Lam_s})
+    uint16_t kt_lo[kTileElems];
+    uint16_t a_hi[kTileElems];       // in-chunk matrix A[t][s], hi/lo planes
+    uint16_t a_lo[kTileElems];
     float bonus_part[4][kChunk];     // per-wave partial sums of r.u.k per token
     float row_exp2ref[kHeadDim];     // 2^{R_i}
     float row_dec[kHeadDim];         // 2^{Lam_63,i}
@@ -69,20 +89,21 @@ struct Smem {
 using lds_i16x4 = __attribute__((address_space(3))) i16x4;
 using lds_u32x2 = __attribute__((address_space(3))) u32x2;
 using lds_u32x4 = __attribute__((address_space(3))) u32x4;
+using lds_u16 = __attribute__((address_space(3))) uint16_t;
 
-__device__ inline f32x4 mfma(bf16x8 a, bf16x8 b, f32x4 c) {
+__device__ __forceinline__ f32x4 mfma(bf16x8 a, bf16x8 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
-__device__ inline float bf16_lo(unsigned pair) { return __uint_as_float(pair << 16); }
-__device__ inline float bf16_hi(unsigned pair) { return __uint_as_float(pair & 0xFFFF0000u); }
+__device__ __forceinline__ float bf16_lo(unsigned pair) { return __uint_as_float(pair << 16); }
+__device__ __forceinline__ float bf16_hi(unsigned pair) { return __uint_as_float(pair & 0xFFFF0000u); }
 
 // x = hi + lo with hi the bf16 truncation of x (exact difference) and lo
 // rounded to bf16; returns packed pairs for two values.
 struct HiLo {
     unsigned hi, lo;
 };
-__device__ inline HiLo split2(float x0, float x1) {
+__device__ __forceinline__ HiLo split2(float x0, float x1) {
     const unsigned b0 = __float_as_uint(x0), b1 = __float_as_uint(x1);
     HiLo r;
     r.hi = __builtin_amdgcn_perm(b1, b0, 0x07060302u);      // {x1.hi16, x0.hi16}
@@ -93,53 +114,88 @@ __device__ inline HiLo split2(float x0, float x1) {
     return r;
 }
 // four values -> packed (hi, lo) planes of 4 bf16 each
-__device__ inline void split4(float x0, float x1, float x2, float x3, u32x2 &hi, u32x2 &lo) {
+__device__ __forceinline__ void split4(float x0, float x1, float x2, float x3, u32x2 &hi, u32x2 &lo) {
     const HiLo a = split2(x0, x1), b = split2(x2, x3);
     hi = u32x2{a.hi, b.hi};
     lo = u32x2{a.lo, b.lo};
 }
 
-__device__ inline bf16x8 as_bf16x8(u32x2 a, u32x2 b) {
+__device__ __forceinline__ bf16x8 as_bf16x8(u32x2 a, u32x2 b) {
     u32x4 v = {a.x, a.y, b.x, b.y};
     return __builtin_bit_cast(bf16x8, v);
 }
-__device__ inline bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 
-__device__ inline u32x2 lds_read_b64(const uint16_t *base, int elem) {
-    return *reinterpret_cast<const lds_u32x2 *>(
-        ((const __attribute__((address_space(3))) uint16_t *)(base)) + elem);
+__device__ __forceinline__ u32x2 lds_read_b64(const uint16_t *tile, int elem) {
+    return *((const lds_u32x2 *)((const lds_u16 *)tile + elem));
 }
-__device__ inline u32x4 lds_read_b128(const uint16_t *base, int elem) {
-    return *reinterpret_cast<const lds_u32x4 *>(
-        ((const __attribute__((address_space(3))) uint16_t *)(base)) + elem);
+__device__ __forceinline__ void lds_write_b64(uint16_t *tile, int elem, u32x2 v) {
+    *((lds_u32x2 *)((lds_u16 *)tile + elem)) = v;
 }
-__device__ inline void lds_write_b64(uint16_t *base, int elem, u32x2 v) {
-    *reinterpret_cast<lds_u32x2 *>(((__attribute__((address_space(3))) uint16_t *)(base)) + elem) = v;
-}
-__device__ inline void lds_write_b128(uint16_t *base, int elem, u32x4 v) {
-    *reinterpret_cast<lds_u32x4 *>(((__attribute__((address_space(3))) uint16_t *)(base)) + elem) = v;
+__device__ __forceinline__ void lds_write_b128(uint16_t *tile, int elem, u32x4 v) {
+    *((lds_u32x4 *)((lds_u16 *)tile + elem)) = v;
 }
 
-// Transposed operand read: 16 lanes of a group cover a 4 x 16 block (rows
-// k0..k0+3, columns n0..n0+15) of a natural tile; lane i16 receives column
-// n0 + i16 as four 16-bit values (rows k0..k0+3).
-__device__ inline u32x2 lds_read_tr(const uint16_t *tile, int k0, int n0, int i16) {
-    const int elem = (k0 + (i16 >> 2)) * kPitch + n0 + 4 * (i16 & 3);
-    const lds_i16x4 *p = reinterpret_cast<const lds_i16x4 *>(
-        ((const __attribute__((address_space(3))) uint16_t *)(tile)) + elem);
-    i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(const_cast<lds_i16x4 *>(p));
+// Transposed read (ds_read_b64_tr_b16): the 16 lanes of a group each name one
+// 8-byte piece of a 4 x 16 block (rows k0..k0+3, columns n0..n0+15); lane i16
+// receives column n0 + i16 as four 16-bit values, rows k0..k0+3.  `elem` is
+// this lane's piece: row k0 + i16/4, columns n0 + 4*(i16%4) .. +3.
+__device__ __forceinline__ u32x2 lds_read_tr(const uint16_t *tile, int elem) {
+    i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)((const lds_u16 *)tile + elem));
     return __builtin_bit_cast(u32x2, v);
 }
 
-// Operand with K = tokens 32*kk + 8*grp .. +7 (natural order) and the 16
-// M/N indices n0..n0+15, from a natural [token][channel] tile.
-__device__ inline bf16x8 tr_operand(const uint16_t *tile, int kk, int n0, int i16, int grp) {
-    const int k0 = 32 * kk + 8 * grp;
-    return as_bf16x8(lds_read_tr(tile, k0, n0, i16), lds_read_tr(tile, k0 + 4, n0, i16));
+// MFMA K order.  For the 16x16x32 instruction lane group grp holds 8 K slots;
+// here slots 0..3 are indices 32*kk + 4*grp + 0..3 and slots 4..7 are
+// 32*kk + 16 + 4*grp + 0..3, for contractions over channels and over tokens
+// alike (the state's accumulator layout provides exactly this order).
+
+// Per-lane LDS element offsets (lane i16 = x, group grp, wave w), computed once.
+struct LdsBases {
+    int ro_x[4];   // channel-contracted rows 16*b + x of rt / a: [2*kk + hh] (+ 1024*b)
+    int ro_k[4];   // same for kt
+    int pw_rt[4];  // pre-processing writes, rows 4*x + a: [a]
+    int pw_kt[4];
+    int aw[4];     // A tile writes, row 16*TB + x, columns 16*SB + 4*grp: [SB] (+ 1024*TB)
+    int tr_kt[4];  // token-contracted kt columns 16*ib + x: [ib] (+ 64*(32*kk + 16*hh))
+    int tr_v;      // token-contracted v columns 16*w + x (+ 64*(32*kk + 16*hh))
+    int vw;        // v writes, rows tid/8 (+ 64*32*m), 16-byte piece tid%8
+};
+
+__device__ __forceinline__ LdsBases make_bases(int tid) {
+    const int lane = tid & 63, x = lane & 15, grp = lane >> 4, w = tid >> 6;
+    LdsBases b;
+    const int gx = x, gk = g_kt(x);
+    #pragma unroll
+    for (int q = 0; q < 4; ++q) {                 // q = 2*kk + hh -> column unit bits 8*kk + 4*hh
+        const int hi = 4 * q;
+        b.ro_x[q] = x * 64 + (((grp ^ (gx & 3)) | (hi ^ (gx & 12))) << 2);
+        b.ro_k[q] = x * 64 + (((grp ^ (gk & 3)) | (hi ^ (gk & 12))) << 2);
+    }
+    #pragma unroll
+    for (int a = 0; a < 4; ++a) {
+        b.pw_rt[a] = (4 * x + a) * 64 + (((4 * w + grp) ^ (4 * (x & 3) + a)) << 2);
+        b.pw_kt[a] = (4 * x + a) * 64 + (((4 * w + grp) ^ ((x & 3) | (a << 2))) << 2);
+        b.aw[a] = x * 64 + ((((4 * a) ^ (x & 12)) | (grp ^ (x & 3))) << 2);
+        b.tr_kt[a] = (4 * grp + (x >> 2)) * 64 + ((((4 * a) ^ (4 * (x >> 2))) | ((x & 3) ^ grp)) << 2);
+    }
+    b.tr_v = (4 * grp + (x >> 2)) * 64 + (((2 * w + ((x & 3) >> 1)) ^ (((x >> 2) & 3) << 1)) << 3) + 4 * (x & 1);
+    const int ld_row = tid >> 3;
+    b.vw = ld_row * 64 + (((tid & 7) ^ ((ld_row & 3) << 1)) << 3);
+    return b;
+}
+
+// channel-contracted operand of rt / a (row 16*b + x) or kt (with ro_k)
+__device__ __forceinline__ bf16x8 row_op(const uint16_t *tile, const int (&ro)[4], int b, int kk) {
+    return as_bf16x8(lds_read_b64(tile, ro[2 * kk] + 1024 * b), lds_read_b64(tile, ro[2 * kk + 1] + 1024 * b));
+}
+// token-contracted operand: lane i16 gets column n0 + i16 (base chosen by the caller)
+__device__ __forceinline__ bf16x8 col_op(const uint16_t *tile, int base, int kk) {
+    return as_bf16x8(lds_read_tr(tile, base + 64 * (32 * kk)), lds_read_tr(tile, base + 64 * (32 * kk + 16)));
 }
 
 // Inclusive prefix sum over the 16 lanes of each DPP row.
-__device__ inline float row_scan16(float x) {
+__device__ __forceinline__ float row_scan16(float x) {
     int v = __float_as_int(x);
     v = __float_as_int(__int_as_float(v) + __int_as_float(__builtin_amdgcn_update_dpp(0, v, 0x111, 0xF, 0xF, true)));
     v = __float_as_int(__int_as_float(v) + __int_as_float(__builtin_amdgcn_update_dpp(0, v, 0x112, 0xF, 0xF, true)));
@@ -148,8 +204,55 @@ __device__ inline float row_scan16(float x) {
     return __int_as_float(v);
 }
 
-__device__ inline float shfl(float x, int src_lane) {
+__device__ __forceinline__ float shfl(float x, int src_lane) {
     return __int_as_float(__builtin_amdgcn_ds_bpermute(src_lane << 2, __float_as_int(x)));
+}
+
+// Tiles of the in-chunk matrix, A[t][s] for t in block TB, s in block SB
+// (SB <= TB), computed as A^T = k~ r~^T and masked on diagonal blocks (bonus
+// on the diagonal, zeros above), split and stored.  NT tiles are processed
+// together so that their MFMA chains interleave.
+template <int NT>
+__device__ __forceinline__ void a_tiles(Smem &sm, const LdsBases &lb, const int (&TB)[NT],
+                                        const int (&SB)[NT], int i16, int grp) {
+    f32x4 a[NT];
+    #pragma unroll
+    for (int n = 0; n < NT; ++n) a[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+    #pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+        bf16x8 k_hi[NT], k_lo[NT], r_hi[NT], r_lo[NT];
+        #pragma unroll
+        for (int n = 0; n < NT; ++n) {
+            k_hi[n] = row_op(sm.kt_hi, lb.ro_k, SB[n], kk);
+            k_lo[n] = row_op(sm.kt_lo, lb.ro_k, SB[n], kk);
+            r_hi[n] = row_op(sm.rt_hi, lb.ro_x, TB[n], kk);
+            r_lo[n] = row_op(sm.rt_lo, lb.ro_x, TB[n], kk);
+        }
+        #pragma unroll
+        for (int n = 0; n < NT; ++n) a[n] = mfma(k_hi[n], r_hi[n], a[n]);
+        #pragma unroll
+        for (int n = 0; n < NT; ++n) a[n] = mfma(k_hi[n], r_lo[n], a[n]);
+        #pragma unroll
+        for (int n = 0; n < NT; ++n) a[n] = mfma(k_lo[n], r_hi[n], a[n]);
+    }
+    #pragma unroll
+    for (int n = 0; n < NT; ++n) {
+        // a[n][e] = A[t][s], t = 16*TB + i16, s = 16*SB + 4*grp + e
+        const int t = 16 * TB[n] + i16;
+        if (SB[n] == TB[n]) {
+            const float b = sm.bonus_part[0][t] + sm.bonus_part[1][t] + sm.bonus_part[2][t] + sm.bonus_part[3][t];
+            #pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int s_loc = 4 * grp + e;
+                a[n][e] = s_loc < i16 ? a[n][e] : (s_loc == i16 ? b : 0.f);
+            }
+        }
+        u32x2 hi, lo;
+        split4(a[n][0], a[n][1], a[n][2], a[n][3], hi, lo);
+        const int elem = lb.aw[SB[n]] + 1024 * TB[n];
+        lds_write_b64(sm.a_hi, elem, hi);
+        lds_write_b64(sm.a_lo, elem, lo);
+    }
 }
 
 template <Mode M>
@@ -166,13 +269,15 @@ __global__ __launch_bounds__(256, 2) void wkv_chunk_kernel(Geometry g, Tensors t
     if (it.P > 1 && (ws.seg_start == nullptr || ws.seg_state == nullptr)) return;
 
     const int tid = threadIdx.x;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lane = tid & 63;
     const int i16 = lane & 15;
     const int grp = lane >> 4;
     const int H = g.H;
+    const LdsBases lb = make_bases(tid);
 
     // ---- carried state ------------------------------------------------------
+    // lane (i16, grp) of wave w holds S[16*ib + 4*grp + e][16*w + i16]
     float S[4][4];
     const float *s_src = nullptr;
     if (M == Mode::Main) {
@@ -193,28 +298,43 @@ __global__ __launch_bounds__(256, 2) void wkv_chunk_kernel(Geometry g, Tensors t
     if (M == Mode::Main) u4 = *reinterpret_cast<const f32x4 *>(t.u + (size_t)h * kHeadDim + c0);
     float lam_seg[4] = {0.f, 0.f, 0.f, 0.f};                // State: segment log2-decay per channel
 
+    if (M == Mode::Main) {
+        // A is zero above the diagonal tiles that the A.v product reads
+        const u32x2 z = {0u, 0u};
+        if (wave == 2 || wave == 3) {
+            const int TB = wave == 2 ? 0 : 2, SB = TB + 1;
+            lds_write_b64(sm.a_hi, lb.aw[SB] + 1024 * TB, z);
+            lds_write_b64(sm.a_lo, lb.aw[SB] + 1024 * TB, z);
+        }
+    }
+
     const uint16_t *gr = static_cast<const uint16_t *>(t.r);
     const uint16_t *gk = static_cast<const uint16_t *>(t.k);
     const uint16_t *gv = static_cast<const uint16_t *>(t.v);
     const uint16_t *gw = static_cast<const uint16_t *>(t.w);
 
     // ---- global -> register prefetch of one chunk ------------------------------
-    // thread tid loads rows tid/8 and tid/8 + 32, 16-byte column piece tid%8
+    // r, k, w straight into the pre-processing layout (8-byte pieces); v in row
+    // order (16-byte pieces: rows tid/8 and tid/8 + 32) for the LDS tile.  Rows
+    // past the segment end re-read its last row (always in bounds); the padding
+    // values (0 for r, k, v and 1 for w) are substituted after arrival.
     const int ld_row = tid >> 3;
     const int ld_col = (tid & 7) * 8;
-    u32x4 pf_r[2], pf_k[2], pf_v[2], pf_w[2];
+    u32x2 pr[4], pk[4], pw[4];
+    u32x4 pv[2];
     auto issue_loads = [&](int64_t tc) {
         #pragma unroll
+        for (int a = 0; a < 4; ++a) {
+            const int64_t row = min<int64_t>(tc + 4 * i16 + a, it.t1 - 1);
+            const size_t off = ((size_t)row * H + h) * kHeadDim + c0;
+            if (M == Mode::Main) pr[a] = *reinterpret_cast<const u32x2 *>(gr + off);
+            pk[a] = *reinterpret_cast<const u32x2 *>(gk + off);
+            pw[a] = *reinterpret_cast<const u32x2 *>(gw + off);
+        }
+        #pragma unroll
         for (int m = 0; m < 2; ++m) {
-            const int64_t row = tc + ld_row + 32 * m;
-            const bool in = row < it.t1;
-            const size_t off = ((size_t)row * H + h) * kHeadDim + ld_col;
-            const u32x4 zero = {0u, 0u, 0u, 0u};
-            const u32x4 one = {kOnePair, kOnePair, kOnePair, kOnePair};
-            if (M == Mode::Main) pf_r[m] = in ? *reinterpret_cast<const u32x4 *>(gr + off) : zero;
-            pf_k[m] = in ? *reinterpret_cast<const u32x4 *>(gk + off) : zero;
-            pf_v[m] = in ? *reinterpret_cast<const u32x4 *>(gv + off) : zero;
-            pf_w[m] = in ? *reinterpret_cast<const u32x4 *>(gw + off) : one;
+            const int64_t row = min<int64_t>(tc + ld_row + 32 * m, it.t1 - 1);
+            pv[m] = *reinterpret_cast<const u32x4 *>(gv + ((size_t)row * H + h) * kHeadDim + ld_col);
         }
     };
 
@@ -226,38 +346,42 @@ __global__ __launch_bounds__(256, 2) void wkv_chunk_kernel(Geometry g, Tensors t
         const int64_t tc = it.t0 + (int64_t)c * kChunk;
         const int nt = (int)min<int64_t>(kChunk, it.t1 - tc);
 
-        // ---- stage raw tiles --------------------------------------------------
-        #pragma unroll
-        for (int m = 0; m < 2; ++m) {
-            const int elem = (ld_row + 32 * m) * kPitch + ld_col;
-            if (M == Mode::Main) lds_write_b128(sm.raw_r, elem, pf_r[m]);
-            lds_write_b128(sm.raw_k, elem, pf_k[m]);
-            lds_write_b128(sm.raw_v, elem, pf_v[m]);
-            lds_write_b128(sm.raw_w, elem, pf_w[m]);
+        // ---- stage v; unpack this chunk's r, k, w; prefetch the next chunk ---------
+        if (nt < kChunk) {                      // partial last chunk: padding rows
+            #pragma unroll
+            for (int a = 0; a < 4; ++a) {
+                if (4 * i16 + a >= nt) {
+                    pr[a] = u32x2{0u, 0u};
+                    pk[a] = u32x2{0u, 0u};
+                    pw[a] = u32x2{kOnePair, kOnePair};
+                }
+            }
+            #pragma unroll
+            for (int m = 0; m < 2; ++m)
+                if (ld_row + 32 * m >= nt) pv[m] = u32x4{0u, 0u, 0u, 0u};
         }
-        __syncthreads();
+        #pragma unroll
+        for (int m = 0; m < 2; ++m) lds_write_b128(sm.v, lb.vw + 64 * 32 * m, pv[m]);
+        float lam[4][4], kk_[4][4], rr[4][4];
+        #pragma unroll
+        for (int a = 0; a < 4; ++a) {
+            lam[a][0] = bf16_lo(pw[a].x); lam[a][1] = bf16_hi(pw[a].x);
+            lam[a][2] = bf16_lo(pw[a].y); lam[a][3] = bf16_hi(pw[a].y);
+            kk_[a][0] = bf16_lo(pk[a].x); kk_[a][1] = bf16_hi(pk[a].x);
+            kk_[a][2] = bf16_lo(pk[a].y); kk_[a][3] = bf16_hi(pk[a].y);
+            if (M == Mode::Main) {
+                rr[a][0] = bf16_lo(pr[a].x); rr[a][1] = bf16_hi(pr[a].x);
+                rr[a][2] = bf16_lo(pr[a].y); rr[a][3] = bf16_hi(pr[a].y);
+            }
+        }
         if (c + 1 < n_chunks) issue_loads(tc + kChunk);
 
         // ---- pre-processing: log-decay prefix, rescaled operands, bonus -------
         {
-            float lam[4][4], kk[4][4], rr[4][4];
             #pragma unroll
-            for (int a = 0; a < 4; ++a) {
-                const int elem = (4 * i16 + a) * kPitch + c0;
-                const u32x2 wv = lds_read_b64(sm.raw_w, elem);
-                const u32x2 kv = lds_read_b64(sm.raw_k, elem);
-                lam[a][0] = bf16_lo(wv.x); lam[a][1] = bf16_hi(wv.x);
-                lam[a][2] = bf16_lo(wv.y); lam[a][3] = bf16_hi(wv.y);
-                kk[a][0] = bf16_lo(kv.x); kk[a][1] = bf16_hi(kv.x);
-                kk[a][2] = bf16_lo(kv.y); kk[a][3] = bf16_hi(kv.y);
-                if (M == Mode::Main) {
-                    const u32x2 rv = lds_read_b64(sm.raw_r, elem);
-                    rr[a][0] = bf16_lo(rv.x); rr[a][1] = bf16_hi(rv.x);
-                    rr[a][2] = bf16_lo(rv.y); rr[a][3] = bf16_hi(rv.y);
-                }
+            for (int a = 0; a < 4; ++a)
                 #pragma unroll
                 for (int q = 0; q < 4; ++q) lam[a][q] = fmaxf(__builtin_amdgcn_logf(lam[a][q]), kLog2Floor);
-            }
             // inclusive prefix over the chunk: in-lane over 4 tokens, then across the 16 lanes
             float excl[4], total[4], ref[4];
             #pragma unroll
@@ -298,17 +422,16 @@ __global__ __launch_bounds__(256, 2) void wkv_chunk_kernel(Geometry g, Tensors t
                     for (int q = 0; q < 4; ++q) {
                         const float prev = a == 0 ? excl[q] : lam[a - 1][q];
                         rs[q] = rr[a][q] * __builtin_amdgcn_exp2f(prev - ref[q]);
-                        ks[q] = kk[a][q] * __builtin_amdgcn_exp2f(ref[q] - lam[a][q]);
-                        bp[a] += rr[a][q] * u4[q] * kk[a][q];
+                        ks[q] = kk_[a][q] * __builtin_amdgcn_exp2f(ref[q] - lam[a][q]);
+                        bp[a] += rr[a][q] * u4[q] * kk_[a][q];
                     }
                     u32x2 rh, rl, kh, kl;
                     split4(rs[0], rs[1], rs[2], rs[3], rh, rl);
                     split4(ks[0], ks[1], ks[2], ks[3], kh, kl);
-                    const int elem = (4 * i16 + a) * kPitch + c0;
-                    lds_write_b64(sm.rt_hi, elem, rh);
-                    lds_write_b64(sm.rt_lo, elem, rl);
-                    lds_write_b64(sm.kt_hi, elem, kh);
-                    lds_write_b64(sm.kt_lo, elem, kl);
+                    lds_write_b64(sm.rt_hi, lb.pw_rt[a], rh);
+                    lds_write_b64(sm.rt_lo, lb.pw_rt[a], rl);
+                    lds_write_b64(sm.kt_hi, lb.pw_kt[a], kh);
+                    lds_write_b64(sm.kt_lo, lb.pw_kt[a], kl);
                     bp[a] += shfl(bp[a], lane ^ 16);
                     bp[a] += shfl(bp[a], lane ^ 32);
                 }
@@ -329,198 +452,194 @@ __global__ __launch_bounds__(256, 2) void wkv_chunk_kernel(Geometry g, Tensors t
                     float ks[4];
                     #pragma unroll
                     for (int q = 0; q < 4; ++q)
-                        ks[q] = kk[a][q] * __builtin_amdgcn_exp2f(total[q] - lam[a][q]);
+                        ks[q] = kk_[a][q] * __builtin_amdgcn_exp2f(total[q] - lam[a][q]);
                     u32x2 kh, kl;
                     split4(ks[0], ks[1], ks[2], ks[3], kh, kl);
-                    const int elem = (4 * i16 + a) * kPitch + c0;
-                    lds_write_b64(sm.kt_hi, elem, kh);
-                    lds_write_b64(sm.kt_lo, elem, kl);
+                    lds_write_b64(sm.kt_hi, lb.pw_kt[a], kh);
+                    lds_write_b64(sm.kt_lo, lb.pw_kt[a], kl);
                 }
             }
         }
         __syncthreads();
 
         // value operand, shared by the in-chunk product and the state update:
-        // lane (i16, grp) holds v[32*kk + 8*grp + 0..7][16*wave + i16]
+        // lane (i16, grp) holds v[K slots of step kk][16*wave + i16]
         bf16x8 vop[2];
-        vop[0] = tr_operand(sm.raw_v, 0, 16 * wave, i16, grp);
-        vop[1] = tr_operand(sm.raw_v, 1, 16 * wave, i16, grp);
+        vop[0] = col_op(sm.v, lb.tr_v, 0);
+        vop[1] = col_op(sm.v, lb.tr_v, 1);
 
         if (M == Mode::State) {
+            f32x4 p[4];
+            #pragma unroll
+            for (int ib = 0; ib < 4; ++ib) p[ib] = f32x4{0.f, 0.f, 0.f, 0.f};
+            #pragma unroll
+            for (int kk = 0; kk < 2; ++kk) {
+                bf16x8 k_hi[4], k_lo[4];
+                #pragma unroll
+                for (int ib = 0; ib < 4; ++ib) {
+                    k_hi[ib] = col_op(sm.kt_hi, lb.tr_kt[ib], kk);
+                    k_lo[ib] = col_op(sm.kt_lo, lb.tr_kt[ib], kk);
+                }
+                #pragma unroll
+                for (int ib = 0; ib < 4; ++ib) p[ib] = mfma(k_hi[ib], vop[kk], p[ib]);
+                #pragma unroll
+                for (int ib = 0; ib < 4; ++ib) p[ib] = mfma(k_lo[ib], vop[kk], p[ib]);
+            }
             #pragma unroll
             for (int ib = 0; ib < 4; ++ib) {
-                f32x4 p = {0.f, 0.f, 0.f, 0.f};
-                #pragma unroll
-                for (int kk2 = 0; kk2 < 2; ++kk2) {
-                    p = mfma(tr_operand(sm.kt_hi, kk2, 16 * ib, i16, grp), vop[kk2], p);
-                    p = mfma(tr_operand(sm.kt_lo, kk2, 16 * ib, i16, grp), vop[kk2], p);
-                }
                 const f32x4 dec = *reinterpret_cast<const f32x4 *>(&sm.row_dec[16 * ib + 4 * grp]);
                 #pragma unroll
-                for (int e = 0; e < 4; ++e) S[ib][e] = dec[e] * S[ib][e] + p[e];
+                for (int e = 0; e < 4; ++e) S[ib][e] = dec[e] * S[ib][e] + p[ib][e];
             }
             __syncthreads();
             continue;
         }
 
         const bool stiff = (sm.stiff[0] | sm.stiff[1] | sm.stiff[2] | sm.stiff[3]) != 0;
+        f32x4 acc[4];
         if (stiff) {
-            // exact token-by-token evaluation of this chunk (rare path)
+            // exact token-by-token evaluation of this chunk (rare path); raw
+            // r, k, w of this lane's 16 state rows come straight from memory;
+            // outputs are staged as fp32 [t][j] in the (unused) A planes
+            float *o_stage = reinterpret_cast<float *>(sm.a_hi);
             for (int tt = 0; tt < nt; ++tt) {
+                const size_t base = ((size_t)(tc + tt) * H + h) * kHeadDim;
                 float part = 0.f;
-                float rv[4][4], kv[4][4], wv[4][4];
+                float kv[4][4], wv[4][4];
                 #pragma unroll
                 for (int ib = 0; ib < 4; ++ib) {
-                    const int elem = tt * kPitch + 16 * ib + 4 * grp;
-                    const u32x2 a = lds_read_b64(sm.raw_r, elem);
-                    const u32x2 b = lds_read_b64(sm.raw_k, elem);
-                    const u32x2 d = lds_read_b64(sm.raw_w, elem);
-                    rv[ib][0] = bf16_lo(a.x); rv[ib][1] = bf16_hi(a.x); rv[ib][2] = bf16_lo(a.y); rv[ib][3] = bf16_hi(a.y);
+                    const size_t off = base + 16 * ib + 4 * grp;
+                    const u32x2 a = *reinterpret_cast<const u32x2 *>(gr + off);
+                    const u32x2 b = *reinterpret_cast<const u32x2 *>(gk + off);
+                    const u32x2 d = *reinterpret_cast<const u32x2 *>(gw + off);
+                    const float rv[4] = {bf16_lo(a.x), bf16_hi(a.x), bf16_lo(a.y), bf16_hi(a.y)};
                     kv[ib][0] = bf16_lo(b.x); kv[ib][1] = bf16_hi(b.x); kv[ib][2] = bf16_lo(b.y); kv[ib][3] = bf16_hi(b.y);
                     wv[ib][0] = bf16_lo(d.x); wv[ib][1] = bf16_hi(d.x); wv[ib][2] = bf16_lo(d.y); wv[ib][3] = bf16_hi(d.y);
                     #pragma unroll
-                    for (int e = 0; e < 4; ++e) part += rv[ib][e] * S[ib][e];
+                    for (int e = 0; e < 4; ++e) part += rv[e] * S[ib][e];
                 }
                 part += shfl(part, lane ^ 16);
                 part += shfl(part, lane ^ 32);
-                const unsigned vbits = sm.raw_v[tt * kPitch + 16 * wave + i16];
+                const unsigned vbits = sm.v[off_v(tt, 16 * wave + i16)];
                 const float vj = __uint_as_float(vbits << 16);
                 const float b = sm.bonus_part[0][tt] + sm.bonus_part[1][tt] +
                                 sm.bonus_part[2][tt] + sm.bonus_part[3][tt];
-                if (grp == (tt & 3))
-                    t.o[((size_t)(tc + tt) * H + h) * kHeadDim + 16 * wave + i16] = part + b * vj;
+                if (grp == (tt & 3)) o_stage[tt * kHeadDim + 16 * wave + i16] = part + b * vj;
                 #pragma unroll
                 for (int ib = 0; ib < 4; ++ib)
                     #pragma unroll
                     for (int e = 0; e < 4; ++e) S[ib][e] = wv[ib][e] * S[ib][e] + kv[ib][e] * vj;
             }
             __syncthreads();
-            continue;
+            #pragma unroll
+            for (int tb = 0; tb < 4; ++tb)
+                acc[tb] = *reinterpret_cast<const f32x4 *>(&o_stage[(16 * tb + i16) * kHeadDim + 16 * wave + 4 * grp]);
+        } else {
+        // ---- in-chunk matrix A: 10 lower 16x16 tiles spread over the waves -------
+        if (wave == 0) {
+            const int TB[3] = {0, 1, 2}, SB[3] = {0, 0, 0};
+            a_tiles<3>(sm, lb, TB, SB, i16, grp);
+        } else if (wave == 1) {
+            const int TB[3] = {1, 2, 3}, SB[3] = {1, 1, 0};
+            a_tiles<3>(sm, lb, TB, SB, i16, grp);
+        } else if (wave == 2) {
+            const int TB[2] = {2, 3}, SB[2] = {2, 1};
+            a_tiles<2>(sm, lb, TB, SB, i16, grp);
+        } else {
+            const int TB[2] = {3, 3}, SB[2] = {3, 2};
+            a_tiles<2>(sm, lb, TB, SB, i16, grp);
         }
 
-        // ---- read-out of the carried state: o^T += (2^R S)^T r~^T ----------------
-        f32x4 acc[4];
+        // ---- read-out of the carried state: o^T = (2^R S)^T r~^T ------------------
         {
             bf16x8 s_hi[2], s_lo[2];
             #pragma unroll
-            for (int kk2 = 0; kk2 < 2; ++kk2) {
+            for (int kk = 0; kk < 2; ++kk) {
                 unsigned hi[4], lo[4];
                 #pragma unroll
                 for (int half = 0; half < 2; ++half) {
-                    const int ib = 2 * kk2 + half;
+                    const int ib = 2 * kk + half;
                     const f32x4 er = *reinterpret_cast<const f32x4 *>(&sm.row_exp2ref[16 * ib + 4 * grp]);
-                    const HiLo a = split2(S[ib][0] * er[0], S[ib][1] * er[1]);
-                    const HiLo b = split2(S[ib][2] * er[2], S[ib][3] * er[3]);
-                    hi[2 * half] = a.hi; lo[2 * half] = a.lo;
-                    hi[2 * half + 1] = b.hi; lo[2 * half + 1] = b.lo;
+                    const HiLo x = split2(S[ib][0] * er[0], S[ib][1] * er[1]);
+                    const HiLo y = split2(S[ib][2] * er[2], S[ib][3] * er[3]);
+                    hi[2 * half] = x.hi; lo[2 * half] = x.lo;
+                    hi[2 * half + 1] = y.hi; lo[2 * half + 1] = y.lo;
                 }
                 const u32x4 h4 = {hi[0], hi[1], hi[2], hi[3]}, l4 = {lo[0], lo[1], lo[2], lo[3]};
-                s_hi[kk2] = as_bf16x8(h4);
-                s_lo[kk2] = as_bf16x8(l4);
+                s_hi[kk] = as_bf16x8(h4);
+                s_lo[kk] = as_bf16x8(l4);
             }
             #pragma unroll
-            for (int tb = 0; tb < 4; ++tb) {
-                acc[tb] = f32x4{0.f, 0.f, 0.f, 0.f};
-                const int row = (16 * tb + i16) * kPitch;
-                #pragma unroll
-                for (int kk2 = 0; kk2 < 2; ++kk2) {
-                    const int e0 = row + 32 * kk2 + 4 * grp;
-                    const bf16x8 r_hi = as_bf16x8(lds_read_b64(sm.rt_hi, e0), lds_read_b64(sm.rt_hi, e0 + 16));
-                    const bf16x8 r_lo = as_bf16x8(lds_read_b64(sm.rt_lo, e0), lds_read_b64(sm.rt_lo, e0 + 16));
-                    acc[tb] = mfma(s_hi[kk2], r_hi, acc[tb]);
-                    acc[tb] = mfma(s_hi[kk2], r_lo, acc[tb]);
-                    acc[tb] = mfma(s_lo[kk2], r_hi, acc[tb]);
-                }
-            }
-        }
-
-        // ---- in-chunk matrix A (lower triangle of 16x16 tiles), shared via LDS --
-        // tile list per wave (10 lower tiles + the 2 zero tiles that the
-        // A.v product reads above the diagonal)
-        {
-            uint16_t *a_hi = sm.raw_r;
-            uint16_t *a_lo = sm.raw_k;
-            // tiles: (TB, SB) packed as TB*4+SB; -1 ends
-            const int tiles[4][3] = {{0 * 4 + 0, 1 * 4 + 0, 2 * 4 + 0},
-                                     {1 * 4 + 1, 2 * 4 + 1, 3 * 4 + 0},
-                                     {2 * 4 + 2, 3 * 4 + 1, 0 * 4 + 1},
-                                     {3 * 4 + 3, 3 * 4 + 2, 2 * 4 + 3}};
+            for (int tb = 0; tb < 4; ++tb) acc[tb] = f32x4{0.f, 0.f, 0.f, 0.f};
             #pragma unroll
-            for (int ti = 0; ti < 3; ++ti) {
-                const int code = tiles[wave][ti];
-                const int TB = code >> 2, SB = code & 3;
-                const int t_row = 16 * TB + i16;
-                const int elem_out = t_row * kPitch + 16 * SB + 4 * grp;
-                if (SB > TB) {                          // zero tile above the diagonal
-                    const u32x2 z = {0u, 0u};
-                    lds_write_b64(a_hi, elem_out, z);
-                    lds_write_b64(a_lo, elem_out, z);
-                    continue;
-                }
-                f32x4 a = {0.f, 0.f, 0.f, 0.f};
+            for (int kk = 0; kk < 2; ++kk) {
+                bf16x8 r_hi[4], r_lo[4];
                 #pragma unroll
-                for (int kk2 = 0; kk2 < 2; ++kk2) {
-                    const int ek = (16 * SB + i16) * kPitch + 32 * kk2 + 8 * grp;
-                    const int er = t_row * kPitch + 32 * kk2 + 8 * grp;
-                    const bf16x8 k_hi = as_bf16x8(lds_read_b128(sm.kt_hi, ek));
-                    const bf16x8 k_lo = as_bf16x8(lds_read_b128(sm.kt_lo, ek));
-                    const bf16x8 r_hi = as_bf16x8(lds_read_b128(sm.rt_hi, er));
-                    const bf16x8 r_lo = as_bf16x8(lds_read_b128(sm.rt_lo, er));
-                    a = mfma(k_hi, r_hi, a);
-                    a = mfma(k_hi, r_lo, a);
-                    a = mfma(k_lo, r_hi, a);
+                for (int tb = 0; tb < 4; ++tb) {
+                    r_hi[tb] = row_op(sm.rt_hi, lb.ro_x, tb, kk);
+                    r_lo[tb] = row_op(sm.rt_lo, lb.ro_x, tb, kk);
                 }
-                // a[e] = A[t][s], t = 16*TB + i16, s = 16*SB + 4*grp + e
-                if (SB == TB) {
-                    const int t_loc = i16;
-                    const float b = sm.bonus_part[0][t_row] + sm.bonus_part[1][t_row] +
-                                    sm.bonus_part[2][t_row] + sm.bonus_part[3][t_row];
-                    #pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const int s_loc = 4 * grp + e;
-                        a[e] = s_loc < t_loc ? a[e] : (s_loc == t_loc ? b : 0.f);
-                    }
-                }
-                u32x2 hi, lo;
-                split4(a[0], a[1], a[2], a[3], hi, lo);
-                lds_write_b64(a_hi, elem_out, hi);
-                lds_write_b64(a_lo, elem_out, lo);
+                #pragma unroll
+                for (int tb = 0; tb < 4; ++tb) acc[tb] = mfma(s_hi[kk], r_hi[tb], acc[tb]);
+                #pragma unroll
+                for (int tb = 0; tb < 4; ++tb) acc[tb] = mfma(s_hi[kk], r_lo[tb], acc[tb]);
+                #pragma unroll
+                for (int tb = 0; tb < 4; ++tb) acc[tb] = mfma(s_lo[kk], r_hi[tb], acc[tb]);
             }
         }
         __syncthreads();
 
-        // ---- in-chunk pairs: o^T += v^T A^T, then store o ------------------------
+        // ---- in-chunk pairs: o^T += v^T A^T ----------------------------------------
+        // A is zero for s >= 32 when t < 32: K step 1 only for row blocks 2, 3
         #pragma unroll
-        for (int tb = 0; tb < 4; ++tb) {
-            const int row = (16 * tb + i16) * kPitch;
+        for (int kk = 0; kk < 2; ++kk) {
+            bf16x8 a_hi[4], a_lo[4];
             #pragma unroll
-            for (int kk2 = 0; kk2 < 2; ++kk2) {
-                if (kk2 == 1 && tb < 2) continue;       // A is zero for s >= 32 when t < 32
-                const int e0 = row + 32 * kk2 + 8 * grp;
-                acc[tb] = mfma(vop[kk2], as_bf16x8(lds_read_b128(sm.raw_r, e0)), acc[tb]);
-                acc[tb] = mfma(vop[kk2], as_bf16x8(lds_read_b128(sm.raw_k, e0)), acc[tb]);
+            for (int tb = 2 * kk; tb < 4; ++tb) {
+                a_hi[tb] = row_op(sm.a_hi, lb.ro_x, tb, kk);
+                a_lo[tb] = row_op(sm.a_lo, lb.ro_x, tb, kk);
             }
-            const int t_loc = 16 * tb + i16;
-            if (t_loc < nt) {
-                // acc[tb][e] = o[t][16*wave + 4*grp + e]
-                *reinterpret_cast<f32x4 *>(t.o + ((size_t)(tc + t_loc) * H + h) * kHeadDim +
-                                           16 * wave + 4 * grp) = acc[tb];
-            }
+            #pragma unroll
+            for (int tb = 2 * kk; tb < 4; ++tb) acc[tb] = mfma(vop[kk], a_hi[tb], acc[tb]);
+            #pragma unroll
+            for (int tb = 2 * kk; tb < 4; ++tb) acc[tb] = mfma(vop[kk], a_lo[tb], acc[tb]);
         }
 
         // ---- state update: S = diag(2^Lam63) S + diag(2^{Lam63-R}) k~^T v --------
-        #pragma unroll
-        for (int ib = 0; ib < 4; ++ib) {
-            f32x4 p = {0.f, 0.f, 0.f, 0.f};
+        {
+            f32x4 p[4];
             #pragma unroll
-            for (int kk2 = 0; kk2 < 2; ++kk2) {
-                p = mfma(tr_operand(sm.kt_hi, kk2, 16 * ib, i16, grp), vop[kk2], p);
-                p = mfma(tr_operand(sm.kt_lo, kk2, 16 * ib, i16, grp), vop[kk2], p);
+            for (int ib = 0; ib < 4; ++ib) p[ib] = f32x4{0.f, 0.f, 0.f, 0.f};
+            #pragma unroll
+            for (int kk = 0; kk < 2; ++kk) {
+                bf16x8 k_hi[4], k_lo[4];
+                #pragma unroll
+                for (int ib = 0; ib < 4; ++ib) {
+                    k_hi[ib] = col_op(sm.kt_hi, lb.tr_kt[ib], kk);
+                    k_lo[ib] = col_op(sm.kt_lo, lb.tr_kt[ib], kk);
+                }
+                #pragma unroll
+                for (int ib = 0; ib < 4; ++ib) p[ib] = mfma(k_hi[ib], vop[kk], p[ib]);
+                #pragma unroll
+                for (int ib = 0; ib < 4; ++ib) p[ib] = mfma(k_lo[ib], vop[kk], p[ib]);
             }
-            const f32x4 dec = *reinterpret_cast<const f32x4 *>(&sm.row_dec[16 * ib + 4 * grp]);
-            const f32x4 kf = *reinterpret_cast<const f32x4 *>(&sm.row_kfac[16 * ib + 4 * grp]);
             #pragma unroll
-            for (int e = 0; e < 4; ++e) S[ib][e] = dec[e] * S[ib][e] + kf[e] * p[e];
+            for (int ib = 0; ib < 4; ++ib) {
+                const f32x4 dec = *reinterpret_cast<const f32x4 *>(&sm.row_dec[16 * ib + 4 * grp]);
+                const f32x4 kf = *reinterpret_cast<const f32x4 *>(&sm.row_kfac[16 * ib + 4 * grp]);
+                #pragma unroll
+                for (int e = 0; e < 4; ++e) S[ib][e] = dec[e] * S[ib][e] + kf[e] * p[ib][e];
+            }
+        }
+        }
+
+        // ---- store o: acc[tb][e] = o[16*tb + i16][16*wave + 4*grp + e] -------------
+        #pragma unroll
+        for (int tb = 0; tb < 4; ++tb) {
+            const int t_loc = 16 * tb + i16;
+            float *dst = t_loc < nt ? t.o + ((size_t)(tc + t_loc) * H + h) * kHeadDim + 16 * wave + 4 * grp
+                                    : g_store_sink + 4 * lane;
+            *reinterpret_cast<f32x4 *>(dst) = acc[tb];
         }
         __syncthreads();
     }
@@ -547,12 +666,19 @@ __global__ __launch_bounds__(256, 2) void wkv_chunk_kernel(Geometry g, Tensors t
     }
 }
 
-// Serial combine of segment aggregates: the state entering segment p of a
-// sequence is  S_{p+1} = diag(2^{Lam_p}) S_p + B_p  starting from state_in.
-// One workgroup per (sequence, head); thread tid owns entries tid + 256*m.
+// Combine of segment aggregates: the state entering segment p of a sequence is
+//   S_{p+1} = diag(2^{Lam_p}) S_p + B_p,   S_0 = state_in (or zeros),
+// a first-order recurrence per state entry.  Entries are independent, so the
+// 4096 entries of each (sequence, head) are spread over 16 workgroups of 256
+// threads (one entry per thread) and each thread issues the loads of a batch
+// of segments before chaining them.
+constexpr int kScanSlices = 16;
+constexpr int kScanBatch = 8;
+
 __global__ __launch_bounds__(256) void wkv_segment_scan_kernel(Geometry g, Tensors t, Workspace ws) {
-    const int n = blockIdx.x / g.H;
-    const int h = blockIdx.x % g.H;
+    const int nh = blockIdx.x / kScanSlices;
+    const int n = nh / g.H;
+    const int h = nh % g.H;
     int first, P;
     if (g.uniform_T >= 0) {
         first = n * g.segs_per_seq;
@@ -563,23 +689,26 @@ __global__ __launch_bounds__(256) void wkv_segment_scan_kernel(Geometry g, Tenso
         if (first < 0 || first + P > g.n_seg) return;
     }
     if (P <= 1) return;
-    const int tid = threadIdx.x;
-    float S[16];
-    const float *s0 = t.state_in ? t.state_in + ((size_t)n * g.H + h) * (kHeadDim * kHeadDim) : nullptr;
-    #pragma unroll
-    for (int m = 0; m < 16; ++m) S[m] = s0 ? s0[tid + 256 * m] : 0.f;
-    for (int p = 0; p < P; ++p) {
-        const size_t item = (size_t)(first + p) * g.H + h;
-        float *dst = ws.seg_start + item * kSegStartFloats;
+    const int idx = (blockIdx.x % kScanSlices) * 256 + threadIdx.x;    // state entry [i][j]
+    const int row = idx >> 6;
+    float S = t.state_in ? t.state_in[((size_t)n * g.H + h) * (kHeadDim * kHeadDim) + idx] : 0.f;
+    for (int p0 = 0; p0 < P; p0 += kScanBatch) {
+        float b[kScanBatch], lam[kScanBatch];
         #pragma unroll
-        for (int m = 0; m < 16; ++m) dst[tid + 256 * m] = S[m];
-        if (p + 1 < P) {
-            const float *agg = ws.seg_state + item * kSegStateFloats;
-            #pragma unroll
-            for (int m = 0; m < 16; ++m) {
-                const int idx = tid + 256 * m;
-                const float dec = __builtin_amdgcn_exp2f(agg[kHeadDim * kHeadDim + (idx >> 6)]);
-                S[m] = dec * S[m] + agg[idx];
+        for (int q = 0; q < kScanBatch; ++q) {
+            b[q] = 0.f;
+            lam[q] = 0.f;
+            if (p0 + q < P - 1) {
+                const float *agg = ws.seg_state + ((size_t)(first + p0 + q) * g.H + h) * kSegStateFloats;
+                b[q] = agg[idx];
+                lam[q] = agg[kHeadDim * kHeadDim + row];
+            }
+        }
+        #pragma unroll
+        for (int q = 0; q < kScanBatch; ++q) {
+            if (p0 + q < P) {
+                ws.seg_start[((size_t)(first + p0 + q) * g.H + h) * kSegStartFloats + idx] = S;
+                if (p0 + q < P - 1) S = __builtin_amdgcn_exp2f(lam[q]) * S + b[q];
             }
         }
     }
@@ -587,18 +716,22 @@ __global__ __launch_bounds__(256) void wkv_segment_scan_kernel(Geometry g, Tenso
 
 }  // namespace
 
-hipError_t launch_chunked(const Geometry &g, const Tensors &t, const Workspace &ws, bool split,
-                          hipStream_t st) {
+hipError_t launch_segment_states(const Geometry &g, const Tensors &t, const Workspace &ws,
+                                 hipStream_t st) {
     const int64_t items = (int64_t)g.n_seg * g.H;
     if (items <= 0) return hipSuccess;
-    if (split) {
-        hipLaunchKernelGGL(wkv_chunk_kernel<Mode::State>, dim3((unsigned)items), dim3(256), 0, st, g, t, ws);
-        hipError_t e = hipGetLastError();
-        if (e != hipSuccess) return e;
-        hipLaunchKernelGGL(wkv_segment_scan_kernel, dim3((unsigned)(g.n_seq * g.H)), dim3(256), 0, st, g, t, ws);
-        e = hipGetLastError();
-        if (e != hipSuccess) return e;
-    }
+    hipLaunchKernelGGL(wkv_chunk_kernel<Mode::State>, dim3((unsigned)items), dim3(256), 0, st, g, t, ws);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(wkv_segment_scan_kernel, dim3((unsigned)(g.n_seq * g.H * kScanSlices)), dim3(256), 0, st,
+                       g, t, ws);
+    return hipGetLastError();
+}
+
+hipError_t launch_chunked_main(const Geometry &g, const Tensors &t, const Workspace &ws,
+                               hipStream_t st) {
+    const int64_t items = (int64_t)g.n_seg * g.H;
+    if (items <= 0) return hipSuccess;
     hipLaunchKernelGGL(wkv_chunk_kernel<Mode::Main>, dim3((unsigned)items), dim3(256), 0, st, g, t, ws);
     return hipGetLastError();
 }

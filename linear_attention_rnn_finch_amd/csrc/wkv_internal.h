@@ -98,8 +98,12 @@ constexpr int kSegStartFloats = kHeadDim * kHeadDim;
 
 // Launchers (defined in the .hip files).
 hipError_t launch_serial(const Geometry &g, const Tensors &t, bool bf16, hipStream_t st);
-hipError_t launch_chunked(const Geometry &g, const Tensors &t, const Workspace &ws, bool split,
-                          hipStream_t st);
+// bf16 path: state pass + segment scan (only when some sequence is split), then
+// the main chunked scan.
+hipError_t launch_segment_states(const Geometry &g, const Tensors &t, const Workspace &ws,
+                                 hipStream_t st);
+hipError_t launch_chunked_main(const Geometry &g, const Tensors &t, const Workspace &ws,
+                               hipStream_t st);
 hipError_t launch_plan_varlen(const Geometry &g, int32_t *seg_off, int32_t *seg_seq,
                               hipStream_t st);
 

@@ -148,3 +148,36 @@ def test_validation_errors_raise():
     assert ei.value.status == 1
     torch.cuda.synchronize()
     assert float(big.abs().max()) == 0.0              # nothing was written
+
+
+def test_graph_replays_match_eager():
+    """The benchmark replays captured calls: every replay must equal the eager
+    result, with eager work and synchronisations between replays."""
+    import linear_attention_rnn_finch_amd as fw
+    wl = make_workload(3, B=1, T=1500, H=4)          # split into segments, with S_0
+    g = to_gpu(wl)
+    B, T, H, D = g["r"].shape
+    o = torch.empty((B, T, H, D), dtype=torch.float32, device="cuda")
+    st = torch.empty((B, H, D, D), dtype=torch.float32, device="cuda")
+    ws = torch.empty(max(fw.workspace_bytes(B, T, H, D), 1), dtype=torch.uint8, device="cuda")
+    o_ref, s_ref = run_gpu(wl, g)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    cap = torch.cuda.Stream()
+    cap.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(cap):
+        fw.prefill(g["r"], g["k"], g["v"], g["w"], g["u"], g["state0"], o=o, state_out=st, workspace=ws)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(graph, stream=cap):
+            fw.prefill(g["r"], g["k"], g["v"], g["w"], g["u"], g["state0"], o=o, state_out=st,
+                       workspace=ws)
+    torch.cuda.synchronize()
+    for rep in range(4):
+        o.fill_(float("nan"))
+        st.fill_(float("nan"))
+        ws.fill_(0xAB)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(o, o_ref), rep
+        assert torch.equal(st, s_ref), rep
