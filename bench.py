@@ -8,8 +8,8 @@ the chunked scan: every step of the path) over the synthetic workload, inputs
 already resident in HBM.  The K timed steps are captured once into a HIP graph
 and replayed, bracketed by device synchronisations, so host launch overhead is
 not part of the figure.  The main chunked-scan kernel is also timed per launch
-with HIP events recorded on its own stream (through the library's timing
-hook), which gives the roofline figure.  The fp64 CPU oracle is timed on the
+with HIP events attached to its dispatch (through the library's timing hook),
+which gives the roofline figure.  The fp64 CPU oracle is timed on the
 host cores over a bounded sample of the same workload (cpu_baseline).
 
 Prints ONE JSON line.
@@ -18,6 +18,7 @@ from __future__ import annotations
 
 import argparse
 import ctypes
+import hashlib
 import json
 import os
 import sys
@@ -39,6 +40,62 @@ def algorithmic_bytes(cfg, tokens, n_seq, has_state_in):
     return tokens * per_token + n_seq * cfg.H * per_state
 
 
+# HBM traffic of the main kernel, from rocprofv3 FETCH_SIZE / WRITE_SIZE passes
+# (scaled by a plain copy of known size); valid only for the kernel source the
+# counters were taken on
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "wkv_chunk_main_layer_1p5b_t4096_traffic.md")
+KERNEL_SOURCES = ("linear_attention_rnn_finch_amd/csrc/wkv_chunk.hip",
+                  "linear_attention_rnn_finch_amd/csrc/wkv_internal.h")
+
+
+def kernel_source_digest():
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic(workload_name):
+    """HBM bytes per launch of the main kernel recorded for this workload and
+    this exact kernel source, else None."""
+    try:
+        text = open(TRAFFIC_FILE).read()
+    except OSError:
+        return None
+    fields = {}
+    for line in text.splitlines():
+        if line.startswith("- ") and ": " in line:
+            key, val = line[2:].split(": ", 1)
+            fields[key.strip()] = val.strip().strip("`")
+    if fields.get("workload") != workload_name:
+        return None
+    if fields.get("kernel_source_sha256") != kernel_source_digest():
+        return None
+    try:
+        return int(fields["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def copy_bandwidth(torch, mib=1024, reps=20):
+    """Device-to-device copy rate (read + write bytes per second, GB/s)."""
+    src = torch.empty(mib << 20, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    a.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / reps
+    del src, dst
+    return 2 * (mib << 20) / (ms * 1e-3) / 1e9
+
+
 def hip_runtime():
     hip = ctypes.CDLL("libamdhip64.so")
     hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
@@ -50,10 +107,10 @@ def hip_runtime():
 
 
 def time_main_kernel(call, n, hip, lib, torch):
-    """Average duration (ms) of the main scan kernel over n calls, from HIP
-    events the library records around that launch.  A device-side sleep keeps
-    the GPU busy while the host enqueues, so no launch gap falls inside an
-    event pair."""
+    """Average and median duration (ms) of the main scan kernel over n calls,
+    from the HIP events the library attaches to that kernel's launch (its own
+    start and end timestamps).  A device-side sleep keeps the GPU busy while
+    the host enqueues the calls, so they run back to back as in a step."""
     evs = []
     for _ in range(2 * n):
         e = ctypes.c_void_p()
@@ -94,7 +151,7 @@ def cpu_baseline(wl, target_seconds):
                               threads=threads)
         passes += 1
         el = time.perf_counter() - t0
-        if el >= target_seconds or passes >= 64:
+        if el >= target_seconds or passes >= 100000:
             break
     tokens = wl.tokens * passes
     rec = {"value": tokens / el, "unit": "tokens/s", "cores": threads, "kind": "oracle",
@@ -211,6 +268,7 @@ def main():
     alg = algorithmic_bytes(cfg, wl.tokens, n_seq, s0 is not None)
     achieved = alg / (k_avg_ms * 1e-3) / 1e9
     step_gbs = alg / (ms_per_step * 1e-3) / 1e9
+    copy_gbs = copy_bandwidth(torch)
 
     rec = {
         "metric": METRIC,
@@ -231,13 +289,15 @@ def main():
                               "HIP graph of %d captured calls, one replay" % args.steps)},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": None,
+                     "traffic": measured_traffic(cfg.name),
                      "kernel": "wkv_chunk_kernel<Main>",
                      "kernel_avg_us": round(k_avg_ms * 1e3, 2),
                      "kernel_median_us": round(k_med_ms * 1e3, 2),
                      "algorithmic_bytes_per_launch": alg,
                      "whole_step_GBps": round(step_gbs, 1),
-                     "whole_step_frac": round(step_gbs / HBM_PEAK_GBS, 4)},
+                     "whole_step_frac": round(step_gbs / HBM_PEAK_GBS, 4),
+                     "measured_copy_GBps": round(copy_gbs, 1),
+                     "kernel_frac_of_copy": round(achieved / copy_gbs, 4)},
     }
 
     if not args.no_cpu_baseline:

@@ -143,12 +143,13 @@ wkv_status_t wkv_prefill_varlen(const void *r, const void *k, const void *v,
 /*
  * Kernel timing hook for profiling tools (the benchmark uses it).  When
  * event_before/event_after (hipEvent_t, cast to void *) are non-NULL, every
- * later pre-fill call made from the calling thread records event_before on
- * its stream immediately before the launch of its main chunked-scan kernel and
- * event_after immediately after it, so hipEventElapsedTime gives that
- * kernel's duration alone.  Pass NULL, NULL to stop.  The events are owned by
- * the caller and must outlive the calls that record them.  Per thread; always
- * returns WKV_OK.
+ * later pre-fill call made from the calling thread attaches them to the launch
+ * of its main scan kernel (the chunked kernel for bf16, the token-serial one
+ * for fp32): event_before takes that kernel's start timestamp and event_after
+ * its end timestamp, so hipEventElapsedTime gives the kernel's own duration,
+ * free of queue and launch gaps.  Pass NULL, NULL to stop.  The events are
+ * owned by the caller, must be created with timing enabled and must outlive the
+ * calls that record them.  Per thread; always returns WKV_OK.
  */
 wkv_status_t wkv_set_kernel_timing_events(void *event_before, void *event_after);
 

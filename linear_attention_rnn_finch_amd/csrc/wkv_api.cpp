@@ -230,12 +230,9 @@ wkv_status_t run(const Plan &p, const Tensors &t, void *ws, hipStream_t st) {
         g.seg_off = seg_off;
         g.seg_seq = seg_seq;
     }
+    const KernelTiming tm{g_ev_before, g_ev_after};
     if (!p.bf16) {
-        if (g_ev_before && (e = hipEventRecord(g_ev_before, st)) != hipSuccess)
-            return fail_hip(e, "timing event");
-        if ((e = launch_serial(g, t, false, st)) != hipSuccess) return fail_hip(e, "scan launch");
-        if (g_ev_after && (e = hipEventRecord(g_ev_after, st)) != hipSuccess)
-            return fail_hip(e, "timing event");
+        if ((e = launch_serial(g, t, false, st, tm)) != hipSuccess) return fail_hip(e, "scan launch");
         return WKV_OK;
     }
     Workspace w{};
@@ -245,11 +242,7 @@ wkv_status_t run(const Plan &p, const Tensors &t, void *ws, hipStream_t st) {
     }
     if (p.split && (e = launch_segment_states(g, t, w, st)) != hipSuccess)
         return fail_hip(e, "segment-state launch");
-    if (g_ev_before && (e = hipEventRecord(g_ev_before, st)) != hipSuccess)
-        return fail_hip(e, "timing event");
-    if ((e = launch_chunked_main(g, t, w, st)) != hipSuccess) return fail_hip(e, "scan launch");
-    if (g_ev_after && (e = hipEventRecord(g_ev_after, st)) != hipSuccess)
-        return fail_hip(e, "timing event");
+    if ((e = launch_chunked_main(g, t, w, st, tm)) != hipSuccess) return fail_hip(e, "scan launch");
     return WKV_OK;
 }
 

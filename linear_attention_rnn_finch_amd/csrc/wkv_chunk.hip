@@ -31,6 +31,10 @@
 // row-major [token][channel] with a row-dependent XOR swizzle of its column
 // units (bank-conflict free); operands contracted over tokens are read with
 // ds_read_b64_tr_b16.
+#include <cstddef>
+
+#include <hip/hip_ext.h>
+
 #include "wkv_internal.h"
 
 namespace finch {
@@ -85,6 +89,9 @@ struct Smem {
     float row_kfac[kHeadDim];        // 2^{Lam_63,i - R_i}
     int stiff[4];
 };
+// the token-serial path stages 64 x 64 fp32 outputs across rt_hi and rt_lo
+static_assert(offsetof(Smem, rt_lo) == offsetof(Smem, rt_hi) + sizeof(uint16_t) * kTileElems,
+              "rt planes must be adjacent");
 
 using lds_i16x4 = __attribute__((address_space(3))) i16x4;
 using lds_u32x2 = __attribute__((address_space(3))) u32x2;
@@ -500,8 +507,10 @@ __global__ __launch_bounds__(256, 2) void wkv_chunk_kernel(Geometry g, Tensors t
         if (stiff) {
             // exact token-by-token evaluation of this chunk (rare path); raw
             // r, k, w of this lane's 16 state rows come straight from memory;
-            // outputs are staged as fp32 [t][j] in the (unused) A planes
-            float *o_stage = reinterpret_cast<float *>(sm.a_hi);
+            // outputs are staged as fp32 [t][j] in the r~ planes, which this
+            // path does not read and the next chunk rewrites (the A planes
+            // must keep their zero tiles)
+            float *o_stage = reinterpret_cast<float *>(sm.rt_hi);
             for (int tt = 0; tt < nt; ++tt) {
                 const size_t base = ((size_t)(tc + tt) * H + h) * kHeadDim;
                 float part = 0.f;
@@ -729,10 +738,14 @@ hipError_t launch_segment_states(const Geometry &g, const Tensors &t, const Work
 }
 
 hipError_t launch_chunked_main(const Geometry &g, const Tensors &t, const Workspace &ws,
-                               hipStream_t st) {
+                               hipStream_t st, KernelTiming tm) {
     const int64_t items = (int64_t)g.n_seg * g.H;
     if (items <= 0) return hipSuccess;
-    hipLaunchKernelGGL(wkv_chunk_kernel<Mode::Main>, dim3((unsigned)items), dim3(256), 0, st, g, t, ws);
+    if (tm.start || tm.stop)
+        hipExtLaunchKernelGGL(wkv_chunk_kernel<Mode::Main>, dim3((unsigned)items), dim3(256), 0, st,
+                              tm.start, tm.stop, 0, g, t, ws);
+    else
+        hipLaunchKernelGGL(wkv_chunk_kernel<Mode::Main>, dim3((unsigned)items), dim3(256), 0, st, g, t, ws);
     return hipGetLastError();
 }
 

@@ -97,13 +97,20 @@ constexpr int kSegStateFloats = kHeadDim * kHeadDim + kHeadDim;
 constexpr int kSegStartFloats = kHeadDim * kHeadDim;
 
 // Launchers (defined in the .hip files).
-hipError_t launch_serial(const Geometry &g, const Tensors &t, bool bf16, hipStream_t st);
+// Scan kernels take an optional event pair: when set, the launch records the
+// kernel's own start and end timestamps into them (profiling hook).
+struct KernelTiming {
+    hipEvent_t start = nullptr, stop = nullptr;
+};
+
+hipError_t launch_serial(const Geometry &g, const Tensors &t, bool bf16, hipStream_t st,
+                         KernelTiming tm = {});
 // bf16 path: state pass + segment scan (only when some sequence is split), then
 // the main chunked scan.
 hipError_t launch_segment_states(const Geometry &g, const Tensors &t, const Workspace &ws,
                                  hipStream_t st);
 hipError_t launch_chunked_main(const Geometry &g, const Tensors &t, const Workspace &ws,
-                               hipStream_t st);
+                               hipStream_t st, KernelTiming tm = {});
 hipError_t launch_plan_varlen(const Geometry &g, int32_t *seg_off, int32_t *seg_seq,
                               hipStream_t st);
 

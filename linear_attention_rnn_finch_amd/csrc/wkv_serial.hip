@@ -7,6 +7,8 @@
 // normwise) leaves no room for the bf16 matrix-core splits of the chunked
 // kernel.  One workgroup per (sequence, head); the 64x64 state lives in
 // registers: thread (q, j) owns rows 16q .. 16q+15 of value column j.
+#include <hip/hip_ext.h>
+
 #include "wkv_internal.h"
 
 namespace finch {
@@ -92,13 +94,15 @@ __global__ __launch_bounds__(256) void wkv_serial_kernel(Geometry g, Tensors t) 
 
 }  // namespace
 
-hipError_t launch_serial(const Geometry &g, const Tensors &t, bool bf16, hipStream_t st) {
+hipError_t launch_serial(const Geometry &g, const Tensors &t, bool bf16, hipStream_t st,
+                         KernelTiming tm) {
     const int64_t items = (int64_t)g.n_seg * g.H;
     if (items <= 0) return hipSuccess;
+    const dim3 grid((unsigned)items), block(256);
     if (bf16)
-        hipLaunchKernelGGL(wkv_serial_kernel<uint16_t>, dim3((unsigned)items), dim3(256), 0, st, g, t);
+        hipExtLaunchKernelGGL(wkv_serial_kernel<uint16_t>, grid, block, 0, st, tm.start, tm.stop, 0, g, t);
     else
-        hipLaunchKernelGGL(wkv_serial_kernel<float>, dim3((unsigned)items), dim3(256), 0, st, g, t);
+        hipExtLaunchKernelGGL(wkv_serial_kernel<float>, grid, block, 0, st, tm.start, tm.stop, 0, g, t);
     return hipGetLastError();
 }
 

@@ -7,6 +7,8 @@ exactly these bits.
 """
 from __future__ import annotations
 
+import os
+from concurrent.futures import ThreadPoolExecutor
 from dataclasses import dataclass, field, replace
 from typing import Optional
 
@@ -19,12 +21,19 @@ _R, _K, _V, _X, _U, _S0, _LEN = 1, 2, 3, 4, 5, 6, 7
 
 
 def f32_to_bf16_bits(x) -> np.ndarray:
-    """float32 -> bf16 bit patterns, round to nearest, ties to even."""
+    """float32 -> bf16 bit patterns, round to nearest, ties to even.
+
+    In uint32 arithmetic: add 0x7FFF plus the lowest kept bit, keep the top
+    16 bits.  Only NaN patterns can wrap; they are replaced by a quiet NaN."""
     x = np.ascontiguousarray(x, dtype=np.float32)
-    u = x.view(np.uint32).astype(np.uint64)
+    u = x.view(np.uint32)
+    acc = u >> 16
+    acc &= 1
+    acc += 0x7FFF
+    acc += u
+    acc >>= 16
+    out = acc.astype(np.uint16)
     nan = np.isnan(x)
-    bias = ((u >> 16) & 1) + 0x7FFF
-    out = ((u + bias) >> 16).astype(np.uint16)
     if nan.any():
         out[nan] = 0x7FC0
     return out
@@ -69,15 +78,22 @@ def ragged_lengths(cfg: WorkloadConfig) -> np.ndarray:
     return _rng(cfg.seed, _LEN).integers(lo, hi, size=cfg.B, endpoint=True).astype(np.int64)
 
 
+def _default_workers() -> int:
+    n = len(os.sched_getaffinity(0))
+    return max(1, min(16, n))
+
+
 def make_workload(cfg, *, T: Optional[int] = None, B: Optional[int] = None,
                   H: Optional[int] = None, lengths=None, heads=None,
-                  seed: Optional[int] = None) -> Workload:
+                  seed: Optional[int] = None, workers: Optional[int] = None) -> Workload:
     """Draw the inputs of ``cfg`` (an index, a name or a WorkloadConfig).
 
     ``T``, ``B``, ``H``, ``lengths`` and ``seed`` override the config's sizes
     (same distributions) for reduced parity cases.  ``lengths`` (a list of
     sequence lengths) makes a packed ragged workload.  Every (tensor, head)
-    pair draws from its own substream, so a head's values do not depend on H.
+    pair draws from its own substream, so a head's values do not depend on H,
+    nor on ``workers`` (threads filling the (tensor, head) pairs in parallel;
+    numpy releases the GIL while it draws).
     """
     cfg = get_config(cfg)
     over = {}
@@ -114,23 +130,28 @@ def make_workload(cfg, *, T: Optional[int] = None, B: Optional[int] = None,
         vals = np.asarray(vals, dtype=np.float32)
         return f32_to_bf16_bits(vals) if bf16 else vals
 
-    out = {}
-    for name, tag in (("r", _R), ("k", _K), ("v", _V), ("w", _X)):
-        arr = np.empty(shape, dtype=store)
-        for h in range(Hh):
-            if name == "w":
-                lo, hi = cfg.x_range
+    def fn_w(g, s, lo=cfg.x_range[0], hi=cfg.x_range[1]):
+        x = g.uniform(lo, hi, size=s)
+        return np.exp(-np.exp(x))
 
-                def fn(g, s, lo=lo, hi=hi):
-                    x = g.uniform(lo, hi, size=s)
-                    return np.exp(-np.exp(x))
-            else:
-                sigma = cfg.rkv_sigma
+    def fn_rkv(g, s, sigma=cfg.rkv_sigma):
+        return g.normal(0.0, sigma, size=s)
 
-                def fn(g, s, sigma=sigma):
-                    return g.normal(0.0, sigma, size=s)
-            arr[..., h, :] = draw(tag, h, fn)
-        out[name] = arr
+    tensors = (("r", _R), ("k", _K), ("v", _V), ("w", _X))
+    out = {name: np.empty(shape, dtype=store) for name, _ in tensors}
+
+    def fill(job):
+        name, tag, h = job
+        out[name][..., h, :] = draw(tag, h, fn_w if name == "w" else fn_rkv)
+
+    jobs = [(name, tag, h) for name, tag in tensors for h in range(Hh)]
+    n_workers = workers if workers is not None else _default_workers()
+    if n_workers > 1 and len(jobs) > 1 and shape[0] * (shape[1] if len(shape) == 4 else 1) >= 4096:
+        with ThreadPoolExecutor(max_workers=n_workers) as ex:
+            list(ex.map(fill, jobs))
+    else:
+        for job in jobs:
+            fill(job)
 
     u = np.stack([_rng(cfg.seed, _U, h).normal(0.0, cfg.u_sigma, size=D)
                   for h in range(Hh)]).astype(np.float32)

@@ -8,7 +8,7 @@ import sys
 import numpy as np
 
 import oracle
-from synth import max_block_error
+from synth import max_block_error, select_heads
 
 
 def log(msg):
@@ -46,25 +46,43 @@ def run_gpu(wl, g=None, state_in="default", **kw):
 
 
 def run_oracle(wl, heads=None, want_o=True):
-    """fp64 oracle on the same bits; ``heads`` restricts the computed slices."""
-    mask = None
+    """fp64 oracle on the same bits.  With ``heads``, only those heads are
+    computed and returned (arrays hold just the selected heads, in order)."""
+    sub = wl if heads is None else select_heads(wl, heads)
+    return oracle.wkv_scan(sub.r, sub.k, sub.v, sub.w, sub.u, sub.state0, sub.cu_seqlens,
+                           want_o=want_o)
+
+
+def _host(x, heads, axis):
+    """Selected heads of a GPU (torch) or host array, as a float64 numpy array;
+    the selection happens before the copy to the host."""
     if heads is not None:
-        H = wl.u.shape[0]
-        sel = np.zeros(H, dtype=np.uint8)
-        sel[list(heads)] = 1
-        mask = np.tile(sel, wl.n_seq)
-    return oracle.wkv_scan(wl.r, wl.k, wl.v, wl.w, wl.u, wl.state0, wl.cu_seqlens,
-                           slice_mask=mask, want_o=want_o)
+        idx = list(heads)
+        if hasattr(x, "cpu"):
+            import torch
+            x = x.index_select(axis % x.dim(), torch.tensor(idx, device=x.device))
+        else:
+            x = np.take(x, idx, axis=axis)
+    if hasattr(x, "cpu"):
+        x = x.float().cpu().numpy()
+    return x
 
 
 def errors(wl, o_gpu, s_gpu, o_ref, s_ref, heads=None):
-    """Max normwise block errors (o, state) over the selected heads."""
-    o_np = o_gpu.float().cpu().numpy() if hasattr(o_gpu, "cpu") else o_gpu
-    s_np = s_gpu.float().cpu().numpy() if hasattr(s_gpu, "cpu") else s_gpu
-    if heads is not None:
-        heads = list(heads)
-        o_np, o_ref = o_np[..., heads, :], o_ref[..., heads, :]
-        s_np, s_ref = s_np[:, heads], s_ref[:, heads]
-    eo = max_block_error(o_np, o_ref, wl.cu_seqlens) if o_ref is not None else 0.0
-    es = max_block_error(s_np, s_ref, kind="state")
+    """Max normwise block errors (o, state); with ``heads``, the references
+    hold only those heads and the GPU results are reduced to them."""
+    eo = 0.0
+    if o_ref is not None:
+        eo = max_block_error(_host(o_gpu, heads, -2), o_ref, wl.cu_seqlens)
+    es = max_block_error(_host(s_gpu, heads, 1), s_ref, kind="state")
     return eo, es
+
+
+def gpu_block_error(a, b, dims):
+    """Normwise error max|a - b| / max|b| over each block of two GPU tensors,
+    a block being all elements that differ only along ``dims``; max over the
+    blocks.  o [B, T, H, D]: dims (1, 3); state [N, H, D, D]: dims (2, 3)."""
+    import torch
+    num = (a - b).abs().amax(dim=dims)
+    den = b.abs().amax(dim=dims)
+    return float(torch.max(num / torch.clamp(den, min=1e-30)))

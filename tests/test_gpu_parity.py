@@ -9,19 +9,21 @@ oracle can afford and sample the rest.
 import numpy as np
 import pytest
 
-from synth import make_workload, get_config
-from gpu_util import log, to_gpu, run_gpu, run_oracle, errors
+from dataclasses import replace
+
+from synth import make_workload, get_config, f32_to_bf16_bits
+from gpu_util import log, to_gpu, run_gpu, run_oracle, errors, gpu_block_error
 
 pytestmark = pytest.mark.gpu
 
 torch = pytest.importorskip("torch")
 
 
-def _check(wl, heads=None, tol=None, **kw):
+def _check(wl, heads=None, tol=None, g=None, **kw):
     tol = tol if tol is not None else wl.config.tolerance
     log("case %s B=%d H=%d tokens=%d heads=%s" % (wl.config.name, wl.n_seq, wl.u.shape[0],
                                                  wl.tokens, heads))
-    o, s = run_gpu(wl, **kw)
+    o, s = run_gpu(wl, g, **kw)
     torch.cuda.synchronize()
     o_ref, s_ref = run_oracle(wl, heads)
     eo, es = errors(wl, o, s, o_ref, s_ref, heads)
@@ -181,3 +183,73 @@ def test_graph_replays_match_eager():
         torch.cuda.synchronize()
         assert torch.equal(o, o_ref), rep
         assert torch.equal(st, s_ref), rep
+
+
+def test_train_batch_full_size():
+    """B=8, T=4096, H=32: every one of the 256 slices against the oracle."""
+    _check(make_workload(2))
+
+
+@pytest.mark.timeout(900)
+def test_long_context_full_size_and_8_segment_chain():
+    """T=262144, H=64 with random fp32 initial states: sampled heads against the
+    oracle, and the same sequence run as 8 consecutive carried-state calls
+    against both the oracle and the single call (every head)."""
+    import linear_attention_rnn_finch_amd as fw
+    wl = make_workload(3)
+    heads = [0, 29, 63]
+    g = to_gpu(wl)
+    o_full, s_full = _check(wl, heads=heads, g=g)
+    B, T, H, D = g["r"].shape
+    o_chain = torch.empty_like(o_full)
+    state = g["state0"].clone()
+    seg = T // 8
+    for p in range(8):
+        a, z = p * seg, (p + 1) * seg
+        log("  chain segment %d tokens %d..%d" % (p, a, z))
+        fw.prefill(g["r"][:, a:z], g["k"][:, a:z], g["v"][:, a:z], g["w"][:, a:z], g["u"],
+                   state, o=o_chain[:, a:z], state_out=state)
+    torch.cuda.synchronize()
+    tol = wl.config.tolerance
+    e_o = gpu_block_error(o_chain, o_full, (1, 3))
+    e_s = gpu_block_error(state, s_full, (2, 3))
+    log("  chain vs single call: o=%.3e state=%.3e" % (e_o, e_s))
+    assert e_o <= tol and e_s <= tol
+    o_ref, s_ref = run_oracle(wl, heads)
+    eo, es = errors(wl, o_chain, state, o_ref, s_ref, heads)
+    log("  chain vs oracle: o=%.3e state=%.3e" % (eo, es))
+    assert eo <= tol and es <= tol
+
+
+@pytest.mark.timeout(600)
+def test_ragged_full_size():
+    """16 packed sequences of U{1024..32768} tokens, own initial states: all
+    sequences, sampled heads."""
+    wl = make_workload(4)
+    _check(wl, heads=[0, 13, 31])
+
+
+def _stiff_workload(T, H):
+    """Decays that vary by many orders of magnitude inside one chunk: a channel
+    at w = 1e-3 over 80 tokens, one at 1e-30, one at the smallest subnormal
+    bf16, and one head with no decay at all (w = 1 exactly)."""
+    wl = make_workload(replace(get_config(1), state_sigma=0.1), T=T, H=H)
+    w = wl.w
+    bits = lambda x: f32_to_bf16_bits(np.float32(x)).item()
+    w[:, 100 % T:180 % T + 1, 1 % H, 5] = bits(1e-3)
+    w[:, (T // 3):(T // 3) + 60, 2 % H, 63] = bits(1e-30)
+    w[:, T - 20:T - 10, (H - 1), 0] = 0x0001
+    w[:, :, 0, 17:30] = bits(1.0)
+    return wl
+
+
+@pytest.mark.parametrize("T,H", [(300, 1), (2000, 4)])
+def test_stiff_decays(T, H):
+    """Chunks whose decay exceeds the rescaling range take the exact token-serial
+    path; with H=4, T=2000 the sequence is also split into segments."""
+    _check(_stiff_workload(T, H))
+
+
+def test_f32_long_sequence():
+    wl = make_workload(0, T=3000, H=3, B=2)
+    _check(wl)
