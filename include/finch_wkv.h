@@ -99,7 +99,7 @@ size_t wkv_prefill_workspace_bytes(int B, int T, int H, int D, wkv_dtype_t in_dt
  *   state_in    device, [B, H, D, D] fp32, or NULL (start from zeros)
  *   o           device, [B, T, H, D] fp32 (output; may be NULL only if T == 0)
  *   state_out   device, [B, H, D, D] fp32 (output), or NULL (not written)
- *   B, H >= 1, T >= 0, D == 64
+ *   B >= 1, 1 <= H <= 65536, T >= 0, D == 64
  *   workspace   device scratch of at least wkv_prefill_workspace_bytes(...)
  *               bytes (NULL allowed when that is 0), 256-byte aligned
  *   stream      hipStream_t to enqueue on

@@ -38,6 +38,9 @@ wkv_status_t fail_hip(hipError_t e, const char *what) {
 // Work items the planner aims for: two resident 4-wave workgroups on each of
 // the 256 compute units of an MI355X.
 constexpr int64_t kTargetItems = 512;
+// the kernels address one 64-token chunk with 32-bit byte offsets:
+// 64 rows x H heads x 256 B (fp32 o) must stay below 2^31
+constexpr int kMaxHeads = 65536;
 constexpr int64_t kMinSegment = 4 * kChunk;
 
 int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
@@ -87,7 +90,7 @@ void layout_workspace(Plan &p, bool varlen) {
 wkv_status_t check_common(int H, int D, wkv_dtype_t dt) {
     if (dt != WKV_F32 && dt != WKV_BF16) return fail(WKV_EUNSUPPORTED, "unknown in_dtype %d", (int)dt);
     if (D != kHeadDim) return fail(WKV_EUNSUPPORTED, "head size D=%d unsupported (only %d)", D, kHeadDim);
-    if (H < 1) return fail(WKV_EINVAL, "H=%d must be >= 1", H);
+    if (H < 1 || H > kMaxHeads) return fail(WKV_EINVAL, "H=%d must be in [1, %d]", H, kMaxHeads);
     return WKV_OK;
 }
 

@@ -55,6 +55,13 @@ constexpr int kTileElems = kChunk * kHeadDim; // one 64 x 64 bf16 tile
 
 enum class Mode { Main, State };
 
+// Registers holding one prefetched chunk: r, k, w in the pre-processing layout
+// (8-byte pieces), v as two 16-byte row pieces.
+struct ChunkRegs {
+    u32x2 r[4], k[4], w[4];
+    u32x4 v[2];
+};
+
 // ---- LDS tile layouts ---------------------------------------------------------
 // Every tile is 64 rows x 64 bf16 (128 B per row, no padding).  Column units
 // are XOR-swizzled with a function of the low four row bits, which keeps the
@@ -68,12 +75,20 @@ __device__ __forceinline__ int off_v(int r, int c) {
     return r * 64 + ((((c >> 3) ^ ((r & 3) << 1)) << 3) | (c & 7));
 }
 
-// Target of the o stores of rows past the end of a partial last chunk.  Every
-// global memory operation inside the chunk loop is issued unconditionally, so
-// the compiler can wait for exactly the prefetched loads it needs instead of
-// draining all outstanding stores; lanes with nothing to store write here.
-// Never read.
-__device__ __attribute__((aligned(256))) float g_store_sink[64 * 4];
+// ---- global memory through buffer resources --------------------------------
+// Each chunk gets resources whose base is (first token of the chunk, head h)
+// and whose size ends after the chunk's last valid token row, so the per-lane
+// byte offsets are loop invariant and rows past the end of a partial chunk
+// read as zero and drop their stores (raw-buffer range checking).
+typedef __amdgpu_buffer_rsrc_t Rsrc;
+constexpr int kRsrcWord3 = 0x00020000;         // raw dword access, no swizzle
+
+__device__ __forceinline__ Rsrc chunk_rsrc(const void *base, int64_t row0, int rows, int H, int h,
+                                           int row_bytes) {
+    const char *p = static_cast<const char *>(base) + ((size_t)row0 * H + h) * row_bytes;
+    const int bytes = ((rows - 1) * H + 1) * row_bytes;
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<char *>(p), (short)0, bytes, kRsrcWord3);
+}
 
 struct Smem {
     uint16_t v[kTileElems];          // values of the chunk
@@ -83,10 +98,10 @@ struct Smem {
     uint16_t kt_lo[kTileElems];
     uint16_t a_hi[kTileElems];       // in-chunk matrix A[t][s], hi/lo planes
     uint16_t a_lo[kTileElems];
-    float bonus_part[4][kChunk];     // per-wave partial sums of r.u.k per token
-    float row_exp2ref[kHeadDim];     // 2^{R_i}
-    float row_dec[kHeadDim];         // 2^{Lam_63,i}
-    float row_kfac[kHeadDim];        // 2^{Lam_63,i - R_i}
+    alignas(16) float bonus_part[4][kChunk];   // per-wave partial sums of r.u.k per token
+    alignas(16) float row_exp2ref[kHeadDim];   // 2^{R_i}
+    alignas(16) float row_dec[kHeadDim];       // 2^{Lam_63,i}
+    alignas(16) float row_kfac[kHeadDim];      // 2^{Lam_63,i - R_i}
     int stiff[4];
 };
 // the token-serial path stages 64 x 64 fp32 outputs across rt_hi and rt_lo
@@ -133,8 +148,11 @@ __device__ __forceinline__ bf16x8 as_bf16x8(u32x2 a, u32x2 b) {
 }
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 
+// Operand reads are volatile so that the compiler keeps each one a separate
+// ds_read_b64 landing directly in its MFMA operand registers (merged reads of
+// neighbouring tiles would need register copies to regroup).
 __device__ __forceinline__ u32x2 lds_read_b64(const uint16_t *tile, int elem) {
-    return *((const lds_u32x2 *)((const lds_u16 *)tile + elem));
+    return *((const volatile lds_u32x2 *)((const lds_u16 *)tile + elem));
 }
 __device__ __forceinline__ void lds_write_b64(uint16_t *tile, int elem, u32x2 v) {
     *((lds_u32x2 *)((lds_u16 *)tile + elem)) = v;
@@ -211,8 +229,19 @@ __device__ __forceinline__ float row_scan16(float x) {
     return __int_as_float(v);
 }
 
-__device__ __forceinline__ float shfl(float x, int src_lane) {
-    return __int_as_float(__builtin_amdgcn_ds_bpermute(src_lane << 2, __float_as_int(x)));
+// Value of lane N of this lane's 16-lane row (DPP row_newbcast).
+template <int N>
+__device__ __forceinline__ float row_bcast(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x150 + N, 0xF, 0xF, false));
+}
+
+// Sum over the four 16-lane rows (lane, lane ^ 16, lane ^ 32, lane ^ 48),
+// with the row-swapping permutes (VALU, no LDS round trip).
+__device__ __forceinline__ float sum_rows4(float x) {
+    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    const float y = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+    const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(y), __float_as_uint(y), false, false);
+    return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
 // Tiles of the in-chunk matrix, A[t][s] for t in block TB, s in block SB
@@ -317,71 +346,89 @@ __global__ __launch_bounds__(256, 2) void wkv_chunk_kernel(Geometry g, Tensors t
 
     const uint16_t *gr = static_cast<const uint16_t *>(t.r);
     const uint16_t *gk = static_cast<const uint16_t *>(t.k);
-    const uint16_t *gv = static_cast<const uint16_t *>(t.v);
     const uint16_t *gw = static_cast<const uint16_t *>(t.w);
 
     // ---- global -> register prefetch of one chunk ------------------------------
     // r, k, w straight into the pre-processing layout (8-byte pieces); v in row
     // order (16-byte pieces: rows tid/8 and tid/8 + 32) for the LDS tile.  Rows
-    // past the segment end re-read its last row (always in bounds); the padding
-    // values (0 for r, k, v and 1 for w) are substituted after arrival.
+    // past the segment end read as zero (buffer range check); w's padding
+    // value 1 is substituted after arrival.
     const int ld_row = tid >> 3;
     const int ld_col = (tid & 7) * 8;
-    u32x2 pr[4], pk[4], pw[4];
-    u32x4 pv[2];
-    auto issue_loads = [&](int64_t tc) {
+    constexpr int kRowIn = kHeadDim * 2;                 // bytes of one bf16 token row of a head
+    constexpr int kRowOut = kHeadDim * 4;                // bytes of one fp32 token row of a head
+    int off_in[4], off_vin[2];
+    #pragma unroll
+    for (int a = 0; a < 4; ++a) off_in[a] = (4 * i16 + a) * H * kRowIn + 2 * c0;
+    #pragma unroll
+    for (int m = 0; m < 2; ++m) off_vin[m] = (ld_row + 32 * m) * H * kRowIn + 2 * ld_col;
+    int off_out[4];                                      // o rows 16*tb + i16, columns 16*wave + 4*grp
+    #pragma unroll
+    for (int tb = 0; tb < 4; ++tb) off_out[tb] = (16 * tb + i16) * H * kRowOut + 4 * (16 * wave + 4 * grp);
+    auto issue_loads = [&](ChunkRegs &P, int64_t tc) {
+        const int rows = (int)min<int64_t>(kChunk, it.t1 - tc);
+        const Rsrc rk = chunk_rsrc(t.k, tc, rows, H, h, kRowIn);
+        const Rsrc rw = chunk_rsrc(t.w, tc, rows, H, h, kRowIn);
+        const Rsrc rv = chunk_rsrc(t.v, tc, rows, H, h, kRowIn);
+        if (M == Mode::Main) {
+            const Rsrc rr = chunk_rsrc(t.r, tc, rows, H, h, kRowIn);
+            #pragma unroll
+            for (int a = 0; a < 4; ++a) P.r[a] = __builtin_amdgcn_raw_buffer_load_b64(rr, off_in[a], 0, 0);
+        }
         #pragma unroll
         for (int a = 0; a < 4; ++a) {
-            const int64_t row = min<int64_t>(tc + 4 * i16 + a, it.t1 - 1);
-            const size_t off = ((size_t)row * H + h) * kHeadDim + c0;
-            if (M == Mode::Main) pr[a] = *reinterpret_cast<const u32x2 *>(gr + off);
-            pk[a] = *reinterpret_cast<const u32x2 *>(gk + off);
-            pw[a] = *reinterpret_cast<const u32x2 *>(gw + off);
+            P.k[a] = __builtin_amdgcn_raw_buffer_load_b64(rk, off_in[a], 0, 0);
+            P.w[a] = __builtin_amdgcn_raw_buffer_load_b64(rw, off_in[a], 0, 0);
         }
         #pragma unroll
-        for (int m = 0; m < 2; ++m) {
-            const int64_t row = min<int64_t>(tc + ld_row + 32 * m, it.t1 - 1);
-            pv[m] = *reinterpret_cast<const u32x4 *>(gv + ((size_t)row * H + h) * kHeadDim + ld_col);
-        }
+        for (int m = 0; m < 2; ++m) P.v[m] = __builtin_amdgcn_raw_buffer_load_b128(rv, off_vin[m], 0, 0);
     };
 
     const int64_t n_tok = it.t1 - it.t0;
     const int n_chunks = (int)((n_tok + kChunk - 1) / kChunk);
-    if (n_chunks > 0) issue_loads(it.t0);
+    // o of chunk c (acc[tb][e] = o[16*tb + i16][16*wave + 4*grp + e]) is held
+    // until chunk c + 1 has its inputs, and stored just before the loads of
+    // chunk c + 2 are issued: a store queued behind the prefetch would make
+    // the next wait for inputs wait for the store's completion as well.
+    f32x4 o_pend[4];
+    int64_t tc_pend = 0;
+    int nt_pend = 0;
+    auto store_o = [&]() {
+        const Rsrc ro = chunk_rsrc(t.o, tc_pend, nt_pend, H, h, kRowOut);
+        #pragma unroll
+        for (int tb = 0; tb < 4; ++tb)
+            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, o_pend[tb]), ro, off_out[tb], 0, 0);
+    };
+
+    ChunkRegs P;
+    if (n_chunks > 0) issue_loads(P, it.t0);
 
     for (int c = 0; c < n_chunks; ++c) {
         const int64_t tc = it.t0 + (int64_t)c * kChunk;
         const int nt = (int)min<int64_t>(kChunk, it.t1 - tc);
 
         // ---- stage v; unpack this chunk's r, k, w; prefetch the next chunk ---------
-        if (nt < kChunk) {                      // partial last chunk: padding rows
+        if (nt < kChunk) {                      // partial last chunk: w = 1 on padding rows
             #pragma unroll
-            for (int a = 0; a < 4; ++a) {
-                if (4 * i16 + a >= nt) {
-                    pr[a] = u32x2{0u, 0u};
-                    pk[a] = u32x2{0u, 0u};
-                    pw[a] = u32x2{kOnePair, kOnePair};
-                }
-            }
-            #pragma unroll
-            for (int m = 0; m < 2; ++m)
-                if (ld_row + 32 * m >= nt) pv[m] = u32x4{0u, 0u, 0u, 0u};
+            for (int a = 0; a < 4; ++a)
+                if (4 * i16 + a >= nt) P.w[a] = u32x2{kOnePair, kOnePair};
         }
         #pragma unroll
-        for (int m = 0; m < 2; ++m) lds_write_b128(sm.v, lb.vw + 64 * 32 * m, pv[m]);
+        for (int m = 0; m < 2; ++m) lds_write_b128(sm.v, lb.vw + 64 * 32 * m, P.v[m]);
         float lam[4][4], kk_[4][4], rr[4][4];
         #pragma unroll
         for (int a = 0; a < 4; ++a) {
-            lam[a][0] = bf16_lo(pw[a].x); lam[a][1] = bf16_hi(pw[a].x);
-            lam[a][2] = bf16_lo(pw[a].y); lam[a][3] = bf16_hi(pw[a].y);
-            kk_[a][0] = bf16_lo(pk[a].x); kk_[a][1] = bf16_hi(pk[a].x);
-            kk_[a][2] = bf16_lo(pk[a].y); kk_[a][3] = bf16_hi(pk[a].y);
+            lam[a][0] = bf16_lo(P.w[a].x); lam[a][1] = bf16_hi(P.w[a].x);
+            lam[a][2] = bf16_lo(P.w[a].y); lam[a][3] = bf16_hi(P.w[a].y);
+            kk_[a][0] = bf16_lo(P.k[a].x); kk_[a][1] = bf16_hi(P.k[a].x);
+            kk_[a][2] = bf16_lo(P.k[a].y); kk_[a][3] = bf16_hi(P.k[a].y);
             if (M == Mode::Main) {
-                rr[a][0] = bf16_lo(pr[a].x); rr[a][1] = bf16_hi(pr[a].x);
-                rr[a][2] = bf16_lo(pr[a].y); rr[a][3] = bf16_hi(pr[a].y);
+                rr[a][0] = bf16_lo(P.r[a].x); rr[a][1] = bf16_hi(P.r[a].x);
+                rr[a][2] = bf16_lo(P.r[a].y); rr[a][3] = bf16_hi(P.r[a].y);
             }
         }
-        if (c + 1 < n_chunks) issue_loads(tc + kChunk);
+        if (M == Mode::Main && c > 0) store_o();
+        if (c + 1 < n_chunks) issue_loads(P, tc + kChunk);
 
         // ---- pre-processing: log-decay prefix, rescaled operands, bonus -------
         {
@@ -389,19 +436,21 @@ __global__ __launch_bounds__(256, 2) void wkv_chunk_kernel(Geometry g, Tensors t
             for (int a = 0; a < 4; ++a)
                 #pragma unroll
                 for (int q = 0; q < 4; ++q) lam[a][q] = fmaxf(__builtin_amdgcn_logf(lam[a][q]), kLog2Floor);
-            // inclusive prefix over the chunk: in-lane over 4 tokens, then across the 16 lanes
-            float excl[4], total[4], ref[4];
+            // inclusive prefix over the chunk: in-lane over 4 tokens, then across
+            // the 16 lanes; lam becomes E_t = Lam_t - reference (Main: R = Lam_31,
+            // State: Lam_63), and off = E_{t-1} for the first token of the lane
+            float off[4], total[4], ref[4];
             #pragma unroll
             for (int q = 0; q < 4; ++q) {
                 lam[1][q] += lam[0][q];
                 lam[2][q] += lam[1][q];
                 lam[3][q] += lam[2][q];
                 const float incl = row_scan16(lam[3][q]);
-                excl[q] = incl - lam[3][q];
+                total[q] = row_bcast<15>(incl);                         // Lam_63
+                ref[q] = row_bcast<7>(incl);                            // Lam_31
+                off[q] = (incl - lam[3][q]) - (M == Mode::Main ? ref[q] : total[q]);
                 #pragma unroll
-                for (int a = 0; a < 4; ++a) lam[a][q] += excl[q];      // Lam_t, t = 4*i16 + a
-                total[q] = shfl(incl, (lane & 48) | 15);                // Lam_63
-                ref[q] = shfl(incl, (lane & 48) | 7);                   // Lam_31
+                for (int a = 0; a < 4; ++a) lam[a][q] += off[q];
             }
             if (M == Mode::Main) {
                 bool stiff = false;
@@ -427,9 +476,9 @@ __global__ __launch_bounds__(256, 2) void wkv_chunk_kernel(Geometry g, Tensors t
                     bp[a] = 0.f;
                     #pragma unroll
                     for (int q = 0; q < 4; ++q) {
-                        const float prev = a == 0 ? excl[q] : lam[a - 1][q];
-                        rs[q] = rr[a][q] * __builtin_amdgcn_exp2f(prev - ref[q]);
-                        ks[q] = kk_[a][q] * __builtin_amdgcn_exp2f(ref[q] - lam[a][q]);
+                        const float e_prev = a == 0 ? off[q] : lam[a - 1][q];   // Lam_{t-1} - R
+                        rs[q] = rr[a][q] * __builtin_amdgcn_exp2f(e_prev);
+                        ks[q] = kk_[a][q] * __builtin_amdgcn_exp2f(-lam[a][q]);  // R - Lam_t
                         bp[a] += rr[a][q] * u4[q] * kk_[a][q];
                     }
                     u32x2 rh, rl, kh, kl;
@@ -439,8 +488,7 @@ __global__ __launch_bounds__(256, 2) void wkv_chunk_kernel(Geometry g, Tensors t
                     lds_write_b64(sm.rt_lo, lb.pw_rt[a], rl);
                     lds_write_b64(sm.kt_hi, lb.pw_kt[a], kh);
                     lds_write_b64(sm.kt_lo, lb.pw_kt[a], kl);
-                    bp[a] += shfl(bp[a], lane ^ 16);
-                    bp[a] += shfl(bp[a], lane ^ 32);
+                    bp[a] = sum_rows4(bp[a]);
                 }
                 if (grp == 0) {
                     f32x4 b4 = {bp[0], bp[1], bp[2], bp[3]};
@@ -459,7 +507,7 @@ __global__ __launch_bounds__(256, 2) void wkv_chunk_kernel(Geometry g, Tensors t
                     float ks[4];
                     #pragma unroll
                     for (int q = 0; q < 4; ++q)
-                        ks[q] = kk_[a][q] * __builtin_amdgcn_exp2f(total[q] - lam[a][q]);
+                        ks[q] = kk_[a][q] * __builtin_amdgcn_exp2f(-lam[a][q]);   // Lam_63 - Lam_t
                     u32x2 kh, kl;
                     split4(ks[0], ks[1], ks[2], ks[3], kh, kl);
                     lds_write_b64(sm.kt_hi, lb.pw_kt[a], kh);
@@ -527,8 +575,7 @@ __global__ __launch_bounds__(256, 2) void wkv_chunk_kernel(Geometry g, Tensors t
                     #pragma unroll
                     for (int e = 0; e < 4; ++e) part += rv[e] * S[ib][e];
                 }
-                part += shfl(part, lane ^ 16);
-                part += shfl(part, lane ^ 32);
+                part = sum_rows4(part);
                 const unsigned vbits = sm.v[off_v(tt, 16 * wave + i16)];
                 const float vj = __uint_as_float(vbits << 16);
                 const float b = sm.bonus_part[0][tt] + sm.bonus_part[1][tt] +
@@ -642,16 +689,14 @@ __global__ __launch_bounds__(256, 2) void wkv_chunk_kernel(Geometry g, Tensors t
         }
         }
 
-        // ---- store o: acc[tb][e] = o[16*tb + i16][16*wave + 4*grp + e] -------------
+        // o of this chunk is stored early in the next iteration (see store_o)
         #pragma unroll
-        for (int tb = 0; tb < 4; ++tb) {
-            const int t_loc = 16 * tb + i16;
-            float *dst = t_loc < nt ? t.o + ((size_t)(tc + t_loc) * H + h) * kHeadDim + 16 * wave + 4 * grp
-                                    : g_store_sink + 4 * lane;
-            *reinterpret_cast<f32x4 *>(dst) = acc[tb];
-        }
+        for (int tb = 0; tb < 4; ++tb) o_pend[tb] = acc[tb];
+        tc_pend = tc;
+        nt_pend = nt;
         __syncthreads();
     }
+    if (M == Mode::Main && n_chunks > 0) store_o();
 
     // ---- outputs of the work item ------------------------------------------------
     if (M == Mode::State) {

@@ -77,6 +77,7 @@ def call(lib, B=1, T=128, H=4, D=64, dt=BF16, r=R, k=K, v=V, w=W, u=U, s_in=S_IN
     (dict(D=128), EUNSUP),
     (dict(dt=7), EUNSUP),
     (dict(H=0), EINVAL),
+    (dict(H=65537), EINVAL),
     (dict(B=0), EINVAL),
     (dict(T=-1), EINVAL),
     (dict(B=70000, T=70000), EINVAL),
