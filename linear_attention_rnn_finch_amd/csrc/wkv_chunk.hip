@@ -407,6 +407,16 @@ __global__ __launch_bounds__(256, 2) void wkv_chunk_kernel(Geometry g, Tensors t
         const int64_t tc = it.t0 + (int64_t)c * kChunk;
         const int nt = (int)min<int64_t>(kChunk, it.t1 - tc);
 
+        // Wave priority falls with progress through the segment: the two
+        // workgroups sharing a CU then advance together (instead of the older
+        // one finishing first and leaving the CU half idle at the end).
+        switch ((4 * c) / n_chunks) {
+        case 0: __builtin_amdgcn_s_setprio(3); break;
+        case 1: __builtin_amdgcn_s_setprio(2); break;
+        case 2: __builtin_amdgcn_s_setprio(1); break;
+        default: __builtin_amdgcn_s_setprio(0); break;
+        }
+
         // ---- stage v; unpack this chunk's r, k, w; prefetch the next chunk ---------
         if (nt < kChunk) {                      // partial last chunk: w = 1 on padding rows
             #pragma unroll
@@ -722,12 +732,12 @@ __global__ __launch_bounds__(256, 2) void wkv_chunk_kernel(Geometry g, Tensors t
 
 // Combine of segment aggregates: the state entering segment p of a sequence is
 //   S_{p+1} = diag(2^{Lam_p}) S_p + B_p,   S_0 = state_in (or zeros),
-// a first-order recurrence per state entry.  Entries are independent, so the
-// 4096 entries of each (sequence, head) are spread over 16 workgroups of 256
-// threads (one entry per thread) and each thread issues the loads of a batch
-// of segments before chaining them.
-constexpr int kScanSlices = 16;
-constexpr int kScanBatch = 8;
+// a first-order recurrence per state entry.  Entries are independent: each
+// thread chains four neighbouring entries of one row (16-byte accesses), the
+// 4096 entries of a (sequence, head) spread over 4 workgroups of 256 threads,
+// and the loads of a batch of segments are issued before the chain.
+constexpr int kScanSlices = 4;
+constexpr int kScanBatch = 16;
 
 __global__ __launch_bounds__(256) void wkv_segment_scan_kernel(Geometry g, Tensors t, Workspace ws) {
     const int nh = blockIdx.x / kScanSlices;
@@ -743,26 +753,33 @@ __global__ __launch_bounds__(256) void wkv_segment_scan_kernel(Geometry g, Tenso
         if (first < 0 || first + P > g.n_seg) return;
     }
     if (P <= 1) return;
-    const int idx = (blockIdx.x % kScanSlices) * 256 + threadIdx.x;    // state entry [i][j]
+    const int idx = ((blockIdx.x % kScanSlices) * 256 + threadIdx.x) * 4;   // entries [i][j..j+3]
     const int row = idx >> 6;
-    float S = t.state_in ? t.state_in[((size_t)n * g.H + h) * (kHeadDim * kHeadDim) + idx] : 0.f;
+    f32x4 S = {0.f, 0.f, 0.f, 0.f};
+    if (t.state_in)
+        S = *reinterpret_cast<const f32x4 *>(t.state_in + ((size_t)n * g.H + h) * (kHeadDim * kHeadDim) + idx);
     for (int p0 = 0; p0 < P; p0 += kScanBatch) {
-        float b[kScanBatch], lam[kScanBatch];
+        f32x4 b[kScanBatch];
+        float lam[kScanBatch];
         #pragma unroll
         for (int q = 0; q < kScanBatch; ++q) {
-            b[q] = 0.f;
+            b[q] = f32x4{0.f, 0.f, 0.f, 0.f};
             lam[q] = 0.f;
             if (p0 + q < P - 1) {
                 const float *agg = ws.seg_state + ((size_t)(first + p0 + q) * g.H + h) * kSegStateFloats;
-                b[q] = agg[idx];
+                b[q] = *reinterpret_cast<const f32x4 *>(agg + idx);
                 lam[q] = agg[kHeadDim * kHeadDim + row];
             }
         }
         #pragma unroll
         for (int q = 0; q < kScanBatch; ++q) {
             if (p0 + q < P) {
-                ws.seg_start[((size_t)(first + p0 + q) * g.H + h) * kSegStartFloats + idx] = S;
-                if (p0 + q < P - 1) S = __builtin_amdgcn_exp2f(lam[q]) * S + b[q];
+                *reinterpret_cast<f32x4 *>(ws.seg_start + ((size_t)(first + p0 + q) * g.H + h) * kSegStartFloats + idx) = S;
+                if (p0 + q < P - 1) {
+                    const float d = __builtin_amdgcn_exp2f(lam[q]);
+                    #pragma unroll
+                    for (int e = 0; e < 4; ++e) S[e] = d * S[e] + b[q][e];
+                }
             }
         }
     }
