@@ -52,14 +52,16 @@ constexpr float kStiffLog2 = 96.f;            // largest |half-chunk log2 decay|
 constexpr float kLog2Floor = -127.f;          // log2 w below this only occurs in stiff chunks
 constexpr unsigned kOnePair = 0x3F803F80u;    // two bf16 1.0 (padding value of w)
 constexpr int kTileElems = kChunk * kHeadDim; // one 64 x 64 bf16 tile
+constexpr int kStageRow = 72;                  // staging row pitch in bf16 (144 B)
+constexpr int kStageElems = kChunk * kStageRow;
 
 enum class Mode { Main, State };
 
-// Registers holding one prefetched chunk: r, k, w in the pre-processing layout
-// (8-byte pieces), v as two 16-byte row pieces.
+// Registers holding one prefetched chunk: r, k, w, v as 16-byte pieces of
+// whole token rows (rows tid/8 and tid/8 + 32, piece tid%8), so that every load
+// instruction covers complete 128-byte lines.
 struct ChunkRegs {
-    u32x2 r[4], k[4], w[4];
-    u32x4 v[2];
+    u32x4 r[2], k[2], w[2], v[2];
 };
 
 // ---- LDS tile layouts ---------------------------------------------------------
@@ -74,6 +76,11 @@ __device__ __forceinline__ int g_kt(int x) { return (x >> 2) | ((x & 3) << 2); }
 __device__ __forceinline__ int off_v(int r, int c) {
     return r * 64 + ((((c >> 3) ^ ((r & 3) << 1)) << 3) | (c & 7));
 }
+//   stage : 144-byte rows, 16-byte piece p -> p ^ f(r), f(r) = r bits (2, 4, 5);
+//           conflict-free both for whole-row 16-byte writes and for the
+//           pre-processing reads (8 bytes of rows 4x + a)
+__device__ __forceinline__ int stage_f(int r) { return ((r >> 2) & 1) | (((r >> 4) & 1) << 1) | (((r >> 5) & 1) << 2); }
+__device__ __forceinline__ int off_stage(int r, int piece) { return r * kStageRow + ((piece ^ stage_f(r)) << 3); }
 
 // ---- global memory through buffer resources --------------------------------
 // Each chunk gets resources whose base is (first token of the chunk, head h)
@@ -96,8 +103,13 @@ struct Smem {
     uint16_t rt_lo[kTileElems];
     uint16_t kt_hi[kTileElems];      // k~ = k 2^{R-Lam_s} (state pass: k 2^{Lam_63-Lam_s})
     uint16_t kt_lo[kTileElems];
-    uint16_t a_hi[kTileElems];       // in-chunk matrix A[t][s], hi/lo planes
-    uint16_t a_lo[kTileElems];
+    union {
+        struct {
+            uint16_t a_hi[kTileElems];   // in-chunk matrix A[t][s], hi/lo planes
+            uint16_t a_lo[kTileElems];
+        };
+        uint16_t stage[3][kStageElems];  // raw r, k, w rows of the chunk (until the first barrier)
+    };
     alignas(16) float bonus_part[4][kChunk];   // per-wave partial sums of r.u.k per token
     alignas(16) float row_exp2ref[kHeadDim];   // 2^{R_i}
     alignas(16) float row_dec[kHeadDim];       // 2^{Lam_63,i}
@@ -334,34 +346,30 @@ __global__ __launch_bounds__(256, 2) void wkv_chunk_kernel(Geometry g, Tensors t
     if (M == Mode::Main) u4 = *reinterpret_cast<const f32x4 *>(t.u + (size_t)h * kHeadDim + c0);
     float lam_seg[4] = {0.f, 0.f, 0.f, 0.f};                // State: segment log2-decay per channel
 
-    if (M == Mode::Main) {
-        // A is zero above the diagonal tiles that the A.v product reads
-        const u32x2 z = {0u, 0u};
-        if (wave == 2 || wave == 3) {
-            const int TB = wave == 2 ? 0 : 2, SB = TB + 1;
-            lds_write_b64(sm.a_hi, lb.aw[SB] + 1024 * TB, z);
-            lds_write_b64(sm.a_lo, lb.aw[SB] + 1024 * TB, z);
-        }
-    }
 
     const uint16_t *gr = static_cast<const uint16_t *>(t.r);
     const uint16_t *gk = static_cast<const uint16_t *>(t.k);
     const uint16_t *gw = static_cast<const uint16_t *>(t.w);
 
     // ---- global -> register prefetch of one chunk ------------------------------
-    // r, k, w straight into the pre-processing layout (8-byte pieces); v in row
-    // order (16-byte pieces: rows tid/8 and tid/8 + 32) for the LDS tile.  Rows
-    // past the segment end read as zero (buffer range check); w's padding
-    // value 1 is substituted after arrival.
+    // r, k, w, v as whole-row 16-byte pieces (rows tid/8 and tid/8 + 32); r, k,
+    // w go through the staging tiles into the pre-processing layout, v into
+    // its operand tile.  Rows past the segment end read as zero (buffer range
+    // check); w's padding value 1 is substituted after the staging read.
     const int ld_row = tid >> 3;
     const int ld_col = (tid & 7) * 8;
     constexpr int kRowIn = kHeadDim * 2;                 // bytes of one bf16 token row of a head
     constexpr int kRowOut = kHeadDim * 4;                // bytes of one fp32 token row of a head
-    int off_in[4], off_vin[2];
+    int off_vin[2], st_wr[2], st_rd[4];
     #pragma unroll
-    for (int a = 0; a < 4; ++a) off_in[a] = (4 * i16 + a) * H * kRowIn + 2 * c0;
+    for (int m = 0; m < 2; ++m) {
+        off_vin[m] = (ld_row + 32 * m) * H * kRowIn + 2 * ld_col;
+        st_wr[m] = off_stage(ld_row + 32 * m, tid & 7);
+    }
+    // pre-processing read of rows 4*i16 + a, channels c0..c0+3: half (grp & 1)
+    // of 16-byte piece 2*wave + grp/2
     #pragma unroll
-    for (int m = 0; m < 2; ++m) off_vin[m] = (ld_row + 32 * m) * H * kRowIn + 2 * ld_col;
+    for (int a = 0; a < 4; ++a) st_rd[a] = off_stage(4 * i16 + a, 2 * wave + (grp >> 1)) + 4 * (grp & 1);
     int off_out[4];                                      // o rows 16*tb + i16, columns 16*wave + 4*grp
     #pragma unroll
     for (int tb = 0; tb < 4; ++tb) off_out[tb] = (16 * tb + i16) * H * kRowOut + 4 * (16 * wave + 4 * grp);
@@ -373,15 +381,14 @@ __global__ __launch_bounds__(256, 2) void wkv_chunk_kernel(Geometry g, Tensors t
         if (M == Mode::Main) {
             const Rsrc rr = chunk_rsrc(t.r, tc, rows, H, h, kRowIn);
             #pragma unroll
-            for (int a = 0; a < 4; ++a) P.r[a] = __builtin_amdgcn_raw_buffer_load_b64(rr, off_in[a], 0, 0);
+            for (int m = 0; m < 2; ++m) P.r[m] = __builtin_amdgcn_raw_buffer_load_b128(rr, off_vin[m], 0, 0);
         }
         #pragma unroll
-        for (int a = 0; a < 4; ++a) {
-            P.k[a] = __builtin_amdgcn_raw_buffer_load_b64(rk, off_in[a], 0, 0);
-            P.w[a] = __builtin_amdgcn_raw_buffer_load_b64(rw, off_in[a], 0, 0);
+        for (int m = 0; m < 2; ++m) {
+            P.k[m] = __builtin_amdgcn_raw_buffer_load_b128(rk, off_vin[m], 0, 0);
+            P.w[m] = __builtin_amdgcn_raw_buffer_load_b128(rw, off_vin[m], 0, 0);
+            P.v[m] = __builtin_amdgcn_raw_buffer_load_b128(rv, off_vin[m], 0, 0);
         }
-        #pragma unroll
-        for (int m = 0; m < 2; ++m) P.v[m] = __builtin_amdgcn_raw_buffer_load_b128(rv, off_vin[m], 0, 0);
     };
 
     const int64_t n_tok = it.t1 - it.t0;
@@ -417,28 +424,43 @@ __global__ __launch_bounds__(256, 2) void wkv_chunk_kernel(Geometry g, Tensors t
         default: __builtin_amdgcn_s_setprio(0); break;
         }
 
-        // ---- stage v; unpack this chunk's r, k, w; prefetch the next chunk ---------
-        if (nt < kChunk) {                      // partial last chunk: w = 1 on padding rows
-            #pragma unroll
-            for (int a = 0; a < 4; ++a)
-                if (4 * i16 + a >= nt) P.w[a] = u32x2{kOnePair, kOnePair};
-        }
+        // ---- stage this chunk's rows; prefetch the next chunk --------------------
         #pragma unroll
-        for (int m = 0; m < 2; ++m) lds_write_b128(sm.v, lb.vw + 64 * 32 * m, P.v[m]);
-        float lam[4][4], kk_[4][4], rr[4][4];
-        #pragma unroll
-        for (int a = 0; a < 4; ++a) {
-            lam[a][0] = bf16_lo(P.w[a].x); lam[a][1] = bf16_hi(P.w[a].x);
-            lam[a][2] = bf16_lo(P.w[a].y); lam[a][3] = bf16_hi(P.w[a].y);
-            kk_[a][0] = bf16_lo(P.k[a].x); kk_[a][1] = bf16_hi(P.k[a].x);
-            kk_[a][2] = bf16_lo(P.k[a].y); kk_[a][3] = bf16_hi(P.k[a].y);
-            if (M == Mode::Main) {
-                rr[a][0] = bf16_lo(P.r[a].x); rr[a][1] = bf16_hi(P.r[a].x);
-                rr[a][2] = bf16_lo(P.r[a].y); rr[a][3] = bf16_hi(P.r[a].y);
-            }
+        for (int m = 0; m < 2; ++m) {
+            lds_write_b128(sm.v, lb.vw + 64 * 32 * m, P.v[m]);
+            lds_write_b128(sm.stage[1], st_wr[m], P.k[m]);
+            lds_write_b128(sm.stage[2], st_wr[m], P.w[m]);
+            if (M == Mode::Main) lds_write_b128(sm.stage[0], st_wr[m], P.r[m]);
         }
         if (M == Mode::Main && c > 0) store_o();
         if (c + 1 < n_chunks) issue_loads(P, tc + kChunk);
+        __syncthreads();
+
+        // ---- r, k, w of this lane's 4 tokens x 4 channels from the staging tiles ----
+        u32x2 pr[4], pk[4], pw[4];
+        #pragma unroll
+        for (int a = 0; a < 4; ++a) {
+            pk[a] = lds_read_b64(sm.stage[1], st_rd[a]);
+            pw[a] = lds_read_b64(sm.stage[2], st_rd[a]);
+            if (M == Mode::Main) pr[a] = lds_read_b64(sm.stage[0], st_rd[a]);
+        }
+        if (nt < kChunk) {                      // partial last chunk: w = 1 on padding rows
+            #pragma unroll
+            for (int a = 0; a < 4; ++a)
+                if (4 * i16 + a >= nt) pw[a] = u32x2{kOnePair, kOnePair};
+        }
+        float lam[4][4], kk_[4][4], rr[4][4];
+        #pragma unroll
+        for (int a = 0; a < 4; ++a) {
+            lam[a][0] = bf16_lo(pw[a].x); lam[a][1] = bf16_hi(pw[a].x);
+            lam[a][2] = bf16_lo(pw[a].y); lam[a][3] = bf16_hi(pw[a].y);
+            kk_[a][0] = bf16_lo(pk[a].x); kk_[a][1] = bf16_hi(pk[a].x);
+            kk_[a][2] = bf16_lo(pk[a].y); kk_[a][3] = bf16_hi(pk[a].y);
+            if (M == Mode::Main) {
+                rr[a][0] = bf16_lo(pr[a].x); rr[a][1] = bf16_hi(pr[a].x);
+                rr[a][2] = bf16_lo(pr[a].y); rr[a][3] = bf16_hi(pr[a].y);
+            }
+        }
 
         // ---- pre-processing: log-decay prefix, rescaled operands, bonus -------
         {
@@ -602,6 +624,14 @@ __global__ __launch_bounds__(256, 2) void wkv_chunk_kernel(Geometry g, Tensors t
                 acc[tb] = *reinterpret_cast<const f32x4 *>(&o_stage[(16 * tb + i16) * kHeadDim + 16 * wave + 4 * grp]);
         } else {
         // ---- in-chunk matrix A: 10 lower 16x16 tiles spread over the waves -------
+        // (the staging tiles share the A planes: the zero tiles above the
+        // diagonal ones that the A.v product reads are rewritten every chunk)
+        if (wave == 2 || wave == 3) {
+            const int TB = wave == 2 ? 0 : 2, SB = TB + 1;
+            const u32x2 z = {0u, 0u};
+            lds_write_b64(sm.a_hi, lb.aw[SB] + 1024 * TB, z);
+            lds_write_b64(sm.a_lo, lb.aw[SB] + 1024 * TB, z);
+        }
         if (wave == 0) {
             const int TB[3] = {0, 1, 2}, SB[3] = {0, 0, 0};
             a_tiles<3>(sm, lb, TB, SB, i16, grp);
@@ -653,25 +683,8 @@ __global__ __launch_bounds__(256, 2) void wkv_chunk_kernel(Geometry g, Tensors t
                 for (int tb = 0; tb < 4; ++tb) acc[tb] = mfma(s_lo[kk], r_hi[tb], acc[tb]);
             }
         }
-        __syncthreads();
-
-        // ---- in-chunk pairs: o^T += v^T A^T ----------------------------------------
-        // A is zero for s >= 32 when t < 32: K step 1 only for row blocks 2, 3
-        #pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {
-            bf16x8 a_hi[4], a_lo[4];
-            #pragma unroll
-            for (int tb = 2 * kk; tb < 4; ++tb) {
-                a_hi[tb] = row_op(sm.a_hi, lb.ro_x, tb, kk);
-                a_lo[tb] = row_op(sm.a_lo, lb.ro_x, tb, kk);
-            }
-            #pragma unroll
-            for (int tb = 2 * kk; tb < 4; ++tb) acc[tb] = mfma(vop[kk], a_hi[tb], acc[tb]);
-            #pragma unroll
-            for (int tb = 2 * kk; tb < 4; ++tb) acc[tb] = mfma(vop[kk], a_lo[tb], acc[tb]);
-        }
-
         // ---- state update: S = diag(2^Lam63) S + diag(2^{Lam63-R}) k~^T v --------
+        // (the read-out above has taken the old S; k~ and v are ready since B1)
         {
             f32x4 p[4];
             #pragma unroll
@@ -697,6 +710,25 @@ __global__ __launch_bounds__(256, 2) void wkv_chunk_kernel(Geometry g, Tensors t
                 for (int e = 0; e < 4; ++e) S[ib][e] = dec[e] * S[ib][e] + kf[e] * p[ib][e];
             }
         }
+
+        __syncthreads();
+
+        // ---- in-chunk pairs: o^T += v^T A^T ----------------------------------------
+        // A is zero for s >= 32 when t < 32: K step 1 only for row blocks 2, 3
+        #pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+            bf16x8 a_hi[4], a_lo[4];
+            #pragma unroll
+            for (int tb = 2 * kk; tb < 4; ++tb) {
+                a_hi[tb] = row_op(sm.a_hi, lb.ro_x, tb, kk);
+                a_lo[tb] = row_op(sm.a_lo, lb.ro_x, tb, kk);
+            }
+            #pragma unroll
+            for (int tb = 2 * kk; tb < 4; ++tb) acc[tb] = mfma(vop[kk], a_hi[tb], acc[tb]);
+            #pragma unroll
+            for (int tb = 2 * kk; tb < 4; ++tb) acc[tb] = mfma(vop[kk], a_lo[tb], acc[tb]);
+        }
+
         }
 
         // o of this chunk is stored early in the next iteration (see store_o)
