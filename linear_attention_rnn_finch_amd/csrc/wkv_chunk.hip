@@ -766,12 +766,13 @@ __global__ __launch_bounds__(256, 2) void wkv_chunk_kernel(Geometry g, Tensors t
 //   S_{p+1} = diag(2^{Lam_p}) S_p + B_p,   S_0 = state_in (or zeros),
 // a first-order recurrence per state entry.  Entries are independent: each
 // thread chains four neighbouring entries of one row (16-byte accesses), the
-// 4096 entries of a (sequence, head) spread over 4 workgroups of 256 threads,
+// 4096 entries of a (sequence, head) spread over 16 one-wave workgroups,
 // and the loads of a batch of segments are issued before the chain.
-constexpr int kScanSlices = 4;
+constexpr int kScanSlices = 16;
+constexpr int kScanThreads = 64;      // 16 workgroups x 64 threads x 4 entries = 4096
 constexpr int kScanBatch = 16;
 
-__global__ __launch_bounds__(256) void wkv_segment_scan_kernel(Geometry g, Tensors t, Workspace ws) {
+__global__ __launch_bounds__(kScanThreads) void wkv_segment_scan_kernel(Geometry g, Tensors t, Workspace ws) {
     const int nh = blockIdx.x / kScanSlices;
     const int n = nh / g.H;
     const int h = nh % g.H;
@@ -785,7 +786,7 @@ __global__ __launch_bounds__(256) void wkv_segment_scan_kernel(Geometry g, Tenso
         if (first < 0 || first + P > g.n_seg) return;
     }
     if (P <= 1) return;
-    const int idx = ((blockIdx.x % kScanSlices) * 256 + threadIdx.x) * 4;   // entries [i][j..j+3]
+    const int idx = ((blockIdx.x % kScanSlices) * kScanThreads + threadIdx.x) * 4;   // entries [i][j..j+3]
     const int row = idx >> 6;
     f32x4 S = {0.f, 0.f, 0.f, 0.f};
     if (t.state_in)
@@ -826,7 +827,7 @@ hipError_t launch_segment_states(const Geometry &g, const Tensors &t, const Work
     hipLaunchKernelGGL(wkv_chunk_kernel<Mode::State>, dim3((unsigned)items), dim3(256), 0, st, g, t, ws);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(wkv_segment_scan_kernel, dim3((unsigned)(g.n_seq * g.H * kScanSlices)), dim3(256), 0, st,
+    hipLaunchKernelGGL(wkv_segment_scan_kernel, dim3((unsigned)(g.n_seq * g.H * kScanSlices)), dim3(kScanThreads), 0, st,
                        g, t, ws);
     return hipGetLastError();
 }
