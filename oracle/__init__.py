@@ -24,6 +24,14 @@ Conventions (readings of the pages):
   o_t[j] = sum_i r_t[i] (S_{t-1}[i, j] + u[i] k_t[i] v_t[j]);
   S_t    = diag(w_t) S_{t-1} + k_t^T v_t.
 
+Selectable forms of the same section (keyword arguments of both functions):
+  decay="log"   the decay input holds d_t and w_t = exp(-exp(d_t))
+                (paragraph "Data-dependent decay");
+  variant="c2"  the Finch-C2 time mixer: the state takes k_t (1 - w_t), there
+                is no static bonus, and the second value u'_t (``second_value``,
+                same layout and type as r; None = absent) is added:
+                o_t = r_t S_{t-1} + u'_t.
+
 Parity status: every function here is pinned by the CPU tests in
 ``tests/test_oracle.py`` (brute force, no-decay closed form, constant-decay
 IIR filter, split/carry invariant, hand-worked fixture).
@@ -57,7 +65,7 @@ def build(force: bool = True) -> str:
         return _LIB_PATH
     tmp = _LIB_PATH + ".tmp%d" % os.getpid()
     cmd = ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-fopenmp",
-           "-ffp-contract=off", "-fno-fast-math", "-Wall", "-o", tmp, _SRC]
+           "-ffp-contract=off", "-fno-fast-math", "-Wall", "-o", tmp, _SRC, "-lm"]
     subprocess.run(cmd, check=True)
     os.replace(tmp, _LIB_PATH)
     return _LIB_PATH
@@ -75,6 +83,13 @@ def _load():
                 ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                 ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_int,
                 ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int]
+            lib.oracle_wkv_f64_ex.restype = ctypes.c_int
+            lib.oracle_wkv_f64_ex.argtypes = [
+                ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_int,
+                ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int]
             lib.oracle_max_threads.restype = ctypes.c_int
             _lib = lib
     return _lib
@@ -88,15 +103,27 @@ def _ptr(a):
     return None if a is None else a.ctypes.data
 
 
+DECAY_KINDS = {"w": 0, "log": 1}
+VARIANTS = {"finch": 0, "c2": 1}
+
+
 def wkv_scan(r, k, v, w, u, state_in=None, cu_seqlens=None, *, H=None,
-             slice_mask=None, want_o=True, threads=0):
+             slice_mask=None, want_o=True, threads=0, decay="w", variant="finch",
+             second_value=None):
     """Run the fp64 recurrence.
 
     ``r, k, v, w`` are numpy arrays of float32, or uint16 holding bf16 bit
     patterns, shaped [B, T, H, D] (fixed length) or [tokens, H, D] with
-    ``cu_seqlens`` ([N + 1] offsets).  Returns ``(o, state_out)`` as float64;
-    ``o`` has the input's shape (rows of slices not in ``slice_mask`` stay 0).
+    ``cu_seqlens`` ([N + 1] offsets).  ``w`` holds w_t, or d_t with
+    ``decay="log"``.  With ``variant="c2"``, ``u`` is ignored (may be None)
+    and ``second_value`` (like r, or None) is u'_t.  Returns ``(o,
+    state_out)`` as float64; ``o`` has the input's shape (rows of slices not
+    in ``slice_mask`` stay 0).
     """
+    if decay not in DECAY_KINDS or variant not in VARIANTS:
+        raise ValueError("decay must be one of %s, variant one of %s" % (list(DECAY_KINDS), list(VARIANTS)))
+    if variant != "c2" and second_value is not None:
+        raise ValueError("second_value belongs to the Finch-C2 variant")
     shape = r.shape
     if r.dtype == np.uint16:
         kind = KIND_BF16
@@ -104,8 +131,8 @@ def wkv_scan(r, k, v, w, u, state_in=None, cu_seqlens=None, *, H=None,
         kind = KIND_F32
     else:
         raise TypeError("inputs must be float32 or bf16 bit patterns (uint16)")
-    for name, a in (("k", k), ("v", v), ("w", w)):
-        if a.shape != shape or a.dtype != r.dtype:
+    for name, a in (("k", k), ("v", v), ("w", w), ("second_value", second_value)):
+        if a is not None and (a.shape != shape or a.dtype != r.dtype):
             raise ValueError("%s must match r in shape and dtype" % name)
     if cu_seqlens is None:
         if r.ndim != 4:
@@ -121,6 +148,9 @@ def wkv_scan(r, k, v, w, u, state_in=None, cu_seqlens=None, *, H=None,
             raise ValueError("cu_seqlens[-1] must equal the token count")
     N = len(cu) - 1
     r, k, v, w = (np.ascontiguousarray(a) for a in (r, k, v, w))
+    u2 = None if second_value is None else np.ascontiguousarray(second_value)
+    if variant == "c2" and u is None:
+        u = np.zeros((H_, D), dtype=np.float32)
     u = np.ascontiguousarray(u, dtype=np.float32).reshape(H_, D)
     s0 = None
     if state_in is not None:
@@ -130,9 +160,15 @@ def wkv_scan(r, k, v, w, u, state_in=None, cu_seqlens=None, *, H=None,
         mask = np.ascontiguousarray(slice_mask, dtype=np.uint8).reshape(N * H_)
     o = np.zeros(shape, dtype=np.float64) if want_o else None
     so = np.zeros((N, H_, D, D), dtype=np.float64)
-    rc = _load().oracle_wkv_f64(kind, _ptr(r), _ptr(k), _ptr(v), _ptr(w),
-                                _ptr(u), _ptr(s0), _ptr(cu), N, H_, D,
-                                _ptr(mask), _ptr(o), _ptr(so), int(threads))
+    if decay == "w" and variant == "finch":
+        rc = _load().oracle_wkv_f64(kind, _ptr(r), _ptr(k), _ptr(v), _ptr(w),
+                                    _ptr(u), _ptr(s0), _ptr(cu), N, H_, D,
+                                    _ptr(mask), _ptr(o), _ptr(so), int(threads))
+    else:
+        rc = _load().oracle_wkv_f64_ex(kind, DECAY_KINDS[decay], VARIANTS[variant],
+                                       _ptr(r), _ptr(k), _ptr(v), _ptr(w), _ptr(u),
+                                       _ptr(u2), _ptr(s0), _ptr(cu), N, H_, D,
+                                       _ptr(mask), _ptr(o), _ptr(so), int(threads))
     if rc != 0:
         raise ValueError("oracle rejected cu_seqlens")
     return o, so
@@ -151,7 +187,7 @@ def as_f64(a):
     return a.astype(np.float64)
 
 
-def wkv_sum_form(r, k, v, w, u, s0=None):
+def wkv_sum_form(r, k, v, w, u, s0=None, *, decay="w", variant="finch", second_value=None):
     """Brute-force closed sum for ONE (sequence, head) slice, fp64.
 
     Direct transcription of the definition (GoldFinch architecture summary,
@@ -162,11 +198,25 @@ def wkv_sum_form(r, k, v, w, u, s0=None):
 
     and o_t = r_t wkv_t + r_t diag(u) k_t^T v_t.  Every product of decays is
     formed explicitly for every (t, i) pair -- no recurrence, no reuse.
+    With decay="log" the w argument holds d and w = exp(-exp(d)) (paragraph
+    "Data-dependent decay"); with variant="c2" the keys in the sum are
+    k_i (1 - w_i) (paragraph "Key computation with normalization property")
+    and o_t = r_t wkv_t + u'_t (output equation; u'_t = second_value[t], or
+    no term when None).
     r, k, v, w: [T, D]; u: [D]; s0: [D, D] or None.  Returns (o [T, D],
     state after the last token [D, D]).
     """
-    r, k, v, w, u = (as_f64(a) for a in (r, k, v, w, u))
+    r, k, v, w = (as_f64(a) for a in (r, k, v, w))
     T, D = r.shape
+    if decay == "log":
+        w = np.exp(-np.exp(w))
+    if variant == "c2":
+        k = k * (1.0 - w)
+        u = np.zeros(D)
+        u2 = np.zeros((T, D)) if second_value is None else as_f64(second_value)
+    else:
+        u = as_f64(u)
+        u2 = np.zeros((T, D))
     S0 = np.zeros((D, D)) if s0 is None else np.asarray(s0, dtype=np.float64)
     o = np.zeros((T, D))
 
@@ -185,5 +235,5 @@ def wkv_sum_form(r, k, v, w, u, s0=None):
 
     for t in range(T):
         wkv = state_seen_by(t)
-        o[t] = r[t] @ wkv + (r[t] * u * k[t]).sum() * v[t]
+        o[t] = r[t] @ wkv + (r[t] * u * k[t]).sum() * v[t] + u2[t]
     return o, state_seen_by(T)

@@ -17,7 +17,7 @@ import numpy as np
 from .configs import WorkloadConfig, get_config
 
 # substream tags
-_R, _K, _V, _X, _U, _S0, _LEN = 1, 2, 3, 4, 5, 6, 7
+_R, _K, _V, _X, _U, _S0, _LEN, _U2 = 1, 2, 3, 4, 5, 6, 7, 8
 
 
 def f32_to_bf16_bits(x) -> np.ndarray:
@@ -59,6 +59,9 @@ class Workload:
     state0: Optional[np.ndarray]  # [N, H, D, D] float32 or None
     cu_seqlens: Optional[np.ndarray] = None   # [N + 1] int64 (packed only)
     meta: dict = field(default_factory=dict)
+    decay: str = "w"              # "w": the w array holds w; "log": it holds d (w = exp(-exp(d)))
+    variant: str = "finch"        # "finch" (bonus u) or "c2" (k scaled by 1 - w, second value u2)
+    u2: Optional[np.ndarray] = None   # Finch-C2 second value, like r (None: absent)
 
     @property
     def packed(self) -> bool:
@@ -85,7 +88,8 @@ def _default_workers() -> int:
 
 def make_workload(cfg, *, T: Optional[int] = None, B: Optional[int] = None,
                   H: Optional[int] = None, lengths=None, heads=None,
-                  seed: Optional[int] = None, workers: Optional[int] = None) -> Workload:
+                  seed: Optional[int] = None, workers: Optional[int] = None,
+                  decay: str = "w", variant: str = "finch") -> Workload:
     """Draw the inputs of ``cfg`` (an index, a name or a WorkloadConfig).
 
     ``T``, ``B``, ``H``, ``lengths`` and ``seed`` override the config's sizes
@@ -94,7 +98,13 @@ def make_workload(cfg, *, T: Optional[int] = None, B: Optional[int] = None,
     pair draws from its own substream, so a head's values do not depend on H,
     nor on ``workers`` (threads filling the (tensor, head) pairs in parallel;
     numpy releases the GIL while it draws).
+
+    ``decay="log"`` stores the decay draw x itself (the d of w = exp(-exp(d)))
+    instead of w; ``variant="c2"`` adds the second value u2 ~ N(0, rkv_sigma)
+    from its own substream.  Neither changes any other tensor's values.
     """
+    if decay not in ("w", "log") or variant not in ("finch", "c2"):
+        raise ValueError("decay must be 'w' or 'log', variant 'finch' or 'c2'")
     cfg = get_config(cfg)
     over = {}
     if T is not None:
@@ -132,12 +142,14 @@ def make_workload(cfg, *, T: Optional[int] = None, B: Optional[int] = None,
 
     def fn_w(g, s, lo=cfg.x_range[0], hi=cfg.x_range[1]):
         x = g.uniform(lo, hi, size=s)
-        return np.exp(-np.exp(x))
+        return x if decay == "log" else np.exp(-np.exp(x))
 
     def fn_rkv(g, s, sigma=cfg.rkv_sigma):
         return g.normal(0.0, sigma, size=s)
 
     tensors = (("r", _R), ("k", _K), ("v", _V), ("w", _X))
+    if variant == "c2":
+        tensors += (("u2", _U2),)
     out = {name: np.empty(shape, dtype=store) for name, _ in tensors}
 
     def fill(job):
@@ -162,7 +174,8 @@ def make_workload(cfg, *, T: Optional[int] = None, B: Optional[int] = None,
             state0[:, h] = _rng(cfg.seed, _S0, h).normal(
                 0.0, cfg.state_sigma, size=(n_seq, D, D)).astype(np.float32)
 
-    wl = Workload(cfg, out["r"], out["k"], out["v"], out["w"], u, state0, cu)
+    wl = Workload(cfg, out["r"], out["k"], out["v"], out["w"], u, state0, cu,
+                  decay=decay, variant=variant, u2=out.get("u2"))
     if heads is not None:
         wl = select_heads(wl, heads)
     return wl
@@ -172,10 +185,11 @@ def select_heads(wl: Workload, heads) -> Workload:
     heads = list(heads)
     sl = (Ellipsis, heads, slice(None))
     s0 = None if wl.state0 is None else np.ascontiguousarray(wl.state0[:, heads])
+    u2 = None if wl.u2 is None else np.ascontiguousarray(wl.u2[sl])
     return Workload(replace(wl.config, H=len(heads)),
                     *(np.ascontiguousarray(a[sl]) for a in (wl.r, wl.k, wl.v, wl.w)),
                     np.ascontiguousarray(wl.u[heads]), s0, wl.cu_seqlens,
-                    dict(wl.meta, heads=heads))
+                    dict(wl.meta, heads=heads), decay=wl.decay, variant=wl.variant, u2=u2)
 
 
 def random_slice(seed: int, T: int, D: int, *, dtype="f32", rkv_sigma=1.0,

@@ -27,6 +27,7 @@ def to_gpu(wl):
 
     out = {name: cvt(getattr(wl, name)) for name in ("r", "k", "v", "w")}
     out["u"] = torch.from_numpy(wl.u).to(dev)
+    out["u2"] = None if wl.u2 is None else cvt(wl.u2)
     out["state0"] = None if wl.state0 is None else torch.from_numpy(wl.state0).to(dev)
     if wl.packed:
         out["cu"] = torch.from_numpy(wl.cu_seqlens.astype(np.int32)).to(dev)
@@ -39,10 +40,16 @@ def run_gpu(wl, g=None, state_in="default", **kw):
     import linear_attention_rnn_finch_amd as fw
     g = g or to_gpu(wl)
     s0 = g["state0"] if isinstance(state_in, str) else state_in
+    if wl.variant == "c2":
+        kw.setdefault("variant", "c2")
+        kw.setdefault("second_value", g["u2"])
+    if wl.decay == "log":
+        kw.setdefault("decay", "log")
+    u = None if wl.variant == "c2" else g["u"]
     if wl.packed:
-        return fw.prefill_varlen(g["r"], g["k"], g["v"], g["w"], g["u"], g["cu"], s0,
+        return fw.prefill_varlen(g["r"], g["k"], g["v"], g["w"], u, g["cu"], s0,
                                  cu_seqlens_host=g["cu_host"], **kw)
-    return fw.prefill(g["r"], g["k"], g["v"], g["w"], g["u"], s0, **kw)
+    return fw.prefill(g["r"], g["k"], g["v"], g["w"], u, s0, **kw)
 
 
 def run_oracle(wl, heads=None, want_o=True):
@@ -50,7 +57,8 @@ def run_oracle(wl, heads=None, want_o=True):
     computed and returned (arrays hold just the selected heads, in order)."""
     sub = wl if heads is None else select_heads(wl, heads)
     return oracle.wkv_scan(sub.r, sub.k, sub.v, sub.w, sub.u, sub.state0, sub.cu_seqlens,
-                           want_o=want_o)
+                           want_o=want_o, decay=sub.decay, variant=sub.variant,
+                           second_value=sub.u2)
 
 
 def _host(x, heads, axis):
