@@ -40,8 +40,9 @@
  * and any other buffer is rejected with WKV_EINVAL (checked on the address
  * ranges).
  *
- * Domain: 0 < w <= 1 (w == 1 exactly is legal).  Values outside it, NaN or Inf
- * are not checked and propagate.  Finite |r|, |k| below 2^31 are required
+ * Domain: 0 < w <= 1 (w == 1 exactly is legal); any d, including +-inf, with
+ * WKV_FLAG_DECAY_LOG.  Values outside it and NaN are not checked and
+ * propagate.  Finite |r|, |k| below 2^31 are required
  * (the chunked evaluation rescales them by powers of two up to 2^96).
  *
  * Errors: every entry point validates its arguments before touching the GPU
@@ -59,7 +60,7 @@
 extern "C" {
 #endif
 
-#define FINCH_WKV_ABI_VERSION 1
+#define FINCH_WKV_ABI_VERSION 2
 
 typedef enum {
     WKV_OK = 0,
@@ -73,6 +74,26 @@ typedef enum {
     WKV_F32 = 0,
     WKV_BF16 = 1
 } wkv_dtype_t;
+
+/* Flags of wkv_prefill_ex / wkv_prefill_varlen_ex (bitwise OR; 0 = the plain
+ * entry points' behaviour). */
+typedef enum {
+    /* The decay argument holds d_t instead of w_t, and w_t = exp(-exp(d_t))
+     * (section 3.4, paragraph "Data-dependent decay").  Any d_t is legal:
+     * -inf gives w = 1, +inf gives w = 0.  A bf16 d keeps the relative
+     * precision of decays close to 1, which a bf16 w rounds to exactly 1. */
+    WKV_FLAG_DECAY_LOG = 1,
+    /* The Finch-C2 time mixer (section 3.4, paragraphs "Key computation with
+     * normalization property", "Receptance, value, and the new second value"
+     * and the output equation, per head, before LayerNorm and W_O):
+     *   o_t[j]   = sum_i r_t[i] * S[i][j] + u2_t[j]
+     *   S[i][j] <- w_t[i] * S[i][j] + k_t[i] * (1 - w_t[i]) * v_t[j]
+     * i.e. k is the key projection BEFORE the (1 - w_t) factor, which the
+     * library applies; there is no static bonus (u is ignored and may be
+     * NULL); u2 = second_value is the data-dependent second value u'_t, or
+     * NULL for none (the pages' ablation without it). */
+    WKV_FLAG_FINCH_C2 = 2
+} wkv_flag_t;
 
 /* FINCH_WKV_ABI_VERSION of the loaded library. */
 int wkv_abi_version(void);
@@ -139,6 +160,38 @@ wkv_status_t wkv_prefill_varlen(const void *r, const void *k, const void *v,
                                 int H, int D, wkv_dtype_t in_dtype,
                                 void *workspace, size_t workspace_bytes,
                                 void *stream);
+
+/*
+ * Extended entry points: the plain ones with a flags word (wkv_flag_t) and
+ * the Finch-C2 second value.
+ *   decay         w_t, or d_t with WKV_FLAG_DECAY_LOG; same layout and type
+ *                 as r
+ *   u             [H, D] fp32 bonus; required unless WKV_FLAG_FINCH_C2 (then
+ *                 ignored, may be NULL)
+ *   second_value  with WKV_FLAG_FINCH_C2: u'_t, same layout and type as r, or
+ *                 NULL (no second value); without the flag it must be NULL
+ *   flags         unknown bits -> WKV_EUNSUPPORTED
+ * Everything else (layouts, workspace size, aliasing, errors, T == 0, ragged
+ * offsets) is exactly as for wkv_prefill / wkv_prefill_varlen, whose
+ * workspace queries also size these calls.  wkv_prefill(...) is
+ * wkv_prefill_ex(..., u, NULL, ..., flags = 0, ...).
+ */
+wkv_status_t wkv_prefill_ex(const void *r, const void *k, const void *v,
+                            const void *decay, const float *u, const void *second_value,
+                            const float *state_in, float *o, float *state_out,
+                            int B, int T, int H, int D, wkv_dtype_t in_dtype,
+                            unsigned flags, void *workspace, size_t workspace_bytes,
+                            void *stream);
+
+wkv_status_t wkv_prefill_varlen_ex(const void *r, const void *k, const void *v,
+                                   const void *decay, const float *u,
+                                   const void *second_value,
+                                   const int32_t *cu_seqlens_dev,
+                                   const int32_t *cu_seqlens_host, int N,
+                                   const float *state_in, float *o, float *state_out,
+                                   int H, int D, wkv_dtype_t in_dtype, unsigned flags,
+                                   void *workspace, size_t workspace_bytes,
+                                   void *stream);
 
 /*
  * Kernel timing hook for profiling tools (the benchmark uses it).  When

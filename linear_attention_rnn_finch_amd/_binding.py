@@ -18,7 +18,10 @@ LIBRARY_PATH = os.path.join(_PKG, "libfinch_wkv.so")
 
 WKV_OK, WKV_EINVAL, WKV_EUNSUPPORTED, WKV_EWORKSPACE, WKV_EHIP = range(5)
 WKV_F32, WKV_BF16 = 0, 1
+WKV_FLAG_DECAY_LOG, WKV_FLAG_FINCH_C2 = 1, 2
 HEAD_DIM = 64
+DECAYS = ("w", "log")            # decay argument holds w_t, or d_t with w_t = exp(-exp(d_t))
+VARIANTS = ("finch", "c2")       # base Finch (bonus u) or the Finch-C2 time mixer
 
 if not os.path.exists(LIBRARY_PATH):
     raise ImportError(
@@ -44,6 +47,12 @@ _lib.wkv_prefill.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
 _lib.wkv_prefill_varlen.restype = _i
 _lib.wkv_prefill_varlen.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i,
                                     _vp, _vp, _vp, _i, _i, _i, _vp, _sz, _vp]
+_lib.wkv_prefill_ex.restype = _i
+_lib.wkv_prefill_ex.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                _i, _i, _i, _i, _i, ctypes.c_uint, _vp, _sz, _vp]
+_lib.wkv_prefill_varlen_ex.restype = _i
+_lib.wkv_prefill_varlen_ex.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i,
+                                       _vp, _vp, _vp, _i, _i, _i, ctypes.c_uint, _vp, _sz, _vp]
 
 
 class WkvError(RuntimeError):
@@ -102,6 +111,25 @@ def varlen_workspace_bytes(cu_seqlens_host, H: int, D: int = HEAD_DIM, dtype=tor
     return int(_lib.wkv_prefill_varlen_workspace_bytes(cu.data_ptr(), cu.numel() - 1, H, D, code))
 
 
+def _flags(decay, variant, u, second_value, r):
+    """Flags word of the extended entry points; checks u / second_value."""
+    if decay not in DECAYS:
+        raise ValueError("decay must be one of %s" % (DECAYS,))
+    if variant not in VARIANTS:
+        raise ValueError("variant must be one of %s" % (VARIANTS,))
+    flags = (WKV_FLAG_DECAY_LOG if decay == "log" else 0) | (WKV_FLAG_FINCH_C2 if variant == "c2" else 0)
+    if variant == "c2":
+        if second_value is not None:
+            _device_tensor("second_value", second_value, r.dtype)
+            if second_value.shape != r.shape:
+                raise ValueError("second_value must have r's shape")
+    else:
+        if second_value is not None:
+            raise ValueError("second_value belongs to the Finch-C2 variant")
+        _device_tensor("u", u, torch.float32)
+    return flags
+
+
 def _workspace(nbytes, device, given):
     if nbytes == 0:
         return None, 0
@@ -111,13 +139,16 @@ def _workspace(nbytes, device, given):
 
 
 def prefill(r, k, v, w, u, state_in=None, *, o=None, state_out=None, want_state=True,
-            workspace=None, stream=None):
+            workspace=None, stream=None, decay="w", variant="finch", second_value=None):
     """Finch WKV pre-fill of a fixed-length batch on the GPU.
 
     r, k, v, w: [B, T, H, 64] bfloat16 (or float32), contiguous, same device.
     u: [H, 64] float32.  state_in: [B, H, 64, 64] float32 or None (zeros).
     Returns (o [B, T, H, 64] float32, state_out [B, H, 64, 64] float32 or None).
     ``state_out`` may be ``state_in`` (carried state, updated in place).
+    ``decay="log"``: w holds d with w = exp(-exp(d)).  ``variant="c2"``: the
+    Finch-C2 mixer (k is taken before its (1 - w) factor, u is unused and may
+    be None, ``second_value`` like r or None).
     """
     for name, t in (("r", r), ("k", k), ("v", v), ("w", w)):
         _device_tensor(name, t, r.dtype)
@@ -127,9 +158,11 @@ def prefill(r, k, v, w, u, state_in=None, *, o=None, state_out=None, want_state=
     for name, t in (("k", k), ("v", v), ("w", w)):
         if t.shape != r.shape:
             raise ValueError("%s shape %s != r shape %s" % (name, tuple(t.shape), tuple(r.shape)))
-    _device_tensor("u", u, torch.float32)
-    if tuple(u.shape) != (H, D):
+    flags = _flags(decay, variant, u, second_value, r)
+    if variant == "finch" and tuple(u.shape) != (H, D):
         raise ValueError("u must be [H, D] = %s" % ((H, D),))
+    if variant == "c2":
+        u = None
     if state_in is not None:
         _device_tensor("state_in", state_in, torch.float32)
         if tuple(state_in.shape) != (B, H, D, D):
@@ -150,20 +183,23 @@ def prefill(r, k, v, w, u, state_in=None, *, o=None, state_out=None, want_state=
     need = int(_lib.wkv_prefill_workspace_bytes(B, T, H, D, code))
     ws, ws_bytes = _workspace(need, r.device, workspace)
     with torch.cuda.device(r.device):
-        status = _lib.wkv_prefill(_ptr(r), _ptr(k), _ptr(v), _ptr(w), _ptr(u), _ptr(state_in),
-                                  _ptr(o), _ptr(state_out), B, T, H, D, code, _ptr(ws),
-                                  ws_bytes, _stream_handle(stream))
+        status = _lib.wkv_prefill_ex(_ptr(r), _ptr(k), _ptr(v), _ptr(w), _ptr(u),
+                                     _ptr(second_value), _ptr(state_in), _ptr(o),
+                                     _ptr(state_out), B, T, H, D, code, flags, _ptr(ws),
+                                     ws_bytes, _stream_handle(stream))
     _check(status)
     return o, state_out
 
 
 def prefill_varlen(r, k, v, w, u, cu_seqlens, state_in=None, *, cu_seqlens_host=None, o=None,
-                   state_out=None, want_state=True, workspace=None, stream=None):
+                   state_out=None, want_state=True, workspace=None, stream=None, decay="w",
+                   variant="finch", second_value=None):
     """Finch WKV pre-fill of N packed sequences.
 
     r, k, v, w: [total_tokens, H, 64]; cu_seqlens: [N + 1] int32 offsets on the
     GPU; cu_seqlens_host: the same offsets on the host (copied from the device,
     with a synchronisation, when omitted).  state_in/state_out: [N, H, 64, 64].
+    ``decay``, ``variant`` and ``second_value`` as for ``prefill``.
     """
     for name, t in (("r", r), ("k", k), ("v", v), ("w", w)):
         _device_tensor(name, t, r.dtype)
@@ -173,7 +209,9 @@ def prefill_varlen(r, k, v, w, u, cu_seqlens, state_in=None, *, cu_seqlens_host=
     for name, t in (("k", k), ("v", v), ("w", w)):
         if t.shape != r.shape:
             raise ValueError("%s shape differs from r" % name)
-    _device_tensor("u", u, torch.float32)
+    flags = _flags(decay, variant, u, second_value, r)
+    if variant == "c2":
+        u = None
     _device_tensor("cu_seqlens", cu_seqlens, torch.int32)
     N = cu_seqlens.numel() - 1
     if cu_seqlens_host is None:
@@ -195,9 +233,10 @@ def prefill_varlen(r, k, v, w, u, cu_seqlens, state_in=None, *, cu_seqlens_host=
     need = int(_lib.wkv_prefill_varlen_workspace_bytes(cu_host.data_ptr(), N, H, D, code))
     ws, ws_bytes = _workspace(need, r.device, workspace)
     with torch.cuda.device(r.device):
-        status = _lib.wkv_prefill_varlen(_ptr(r), _ptr(k), _ptr(v), _ptr(w), _ptr(u),
-                                         _ptr(cu_seqlens), cu_host.data_ptr(), N, _ptr(state_in),
-                                         _ptr(o), _ptr(state_out), H, D, code, _ptr(ws),
-                                         ws_bytes, _stream_handle(stream))
+        status = _lib.wkv_prefill_varlen_ex(_ptr(r), _ptr(k), _ptr(v), _ptr(w), _ptr(u),
+                                            _ptr(second_value), _ptr(cu_seqlens),
+                                            cu_host.data_ptr(), N, _ptr(state_in), _ptr(o),
+                                            _ptr(state_out), H, D, code, flags, _ptr(ws),
+                                            ws_bytes, _stream_handle(stream))
     _check(status)
     return o, state_out

@@ -169,24 +169,26 @@ bool overlaps(const Range &a, const Range &b) {
     return a.lo < a.hi && b.lo < b.hi && a.lo < b.hi && b.lo < a.hi;
 }
 
-wkv_status_t check_pointers(const Plan &p, const void *r, const void *k, const void *v,
-                            const void *w, const float *u, const float *state_in, const float *o,
-                            const float *state_out, const void *ws, size_t ws_bytes,
-                            const int32_t *cu_dev) {
+wkv_status_t check_pointers(const Plan &p, const Variant &var, const void *r, const void *k,
+                            const void *v, const void *w, const float *u, const void *u2,
+                            const float *state_in, const float *o, const float *state_out,
+                            const void *ws, size_t ws_bytes, const int32_t *cu_dev) {
     const int64_t tokens = p.g.total_tokens;
     const size_t elt = p.bf16 ? 2 : 4;
     const size_t in_bytes = (size_t)tokens * p.g.H * kHeadDim * elt;
     const size_t o_bytes = (size_t)tokens * p.g.H * kHeadDim * sizeof(float);
     const size_t st_bytes = (size_t)p.g.n_seq * p.g.H * kHeadDim * kHeadDim * sizeof(float);
+    if (var.c2) u = nullptr;                           // the bonus is not part of Finch-C2
+    else if (u2) return fail(WKV_EINVAL, "second_value is only defined for the Finch-C2 variant");
     if (tokens > 0) {
         const void *need[] = {r, k, v, w, u, o};
         const char *names[] = {"r", "k", "v", "w", "u", "o"};
         for (int i = 0; i < 6; ++i)
-            if (!need[i]) return fail(WKV_EINVAL, "%s is NULL", names[i]);
+            if (!need[i] && !(i == 4 && var.c2)) return fail(WKV_EINVAL, "%s is NULL", names[i]);
     }
-    const void *al[] = {r, k, v, w, u, state_in, o, state_out};
-    const char *aln[] = {"r", "k", "v", "w", "u", "state_in", "o", "state_out"};
-    for (int i = 0; i < 8; ++i)
+    const void *al[] = {r, k, v, w, u, state_in, o, state_out, u2};
+    const char *aln[] = {"r", "k", "v", "w", "u", "state_in", "o", "state_out", "second_value"};
+    for (int i = 0; i < 9; ++i)
         if (misaligned(al[i], 16)) return fail(WKV_EINVAL, "%s is not 16-byte aligned", aln[i]);
     if (misaligned(cu_dev, 4)) return fail(WKV_EINVAL, "cu_seqlens_dev is not 4-byte aligned");
     if (misaligned(ws, 256)) return fail(WKV_EINVAL, "workspace is not 256-byte aligned");
@@ -198,6 +200,7 @@ wkv_status_t check_pointers(const Plan &p, const void *r, const void *k, const v
     Range ins[] = {range_of("r", r, in_bytes), range_of("k", k, in_bytes),
                    range_of("v", v, in_bytes), range_of("w", w, in_bytes),
                    range_of("u", u, (size_t)p.g.H * kHeadDim * sizeof(float)),
+                   range_of("second_value", u2, in_bytes),
                    range_of("state_in", state_in, state_in ? st_bytes : 0),
                    range_of("cu_seqlens_dev", cu_dev, n_cu),
                    range_of("workspace", ws, p.bytes)};
@@ -219,7 +222,7 @@ wkv_status_t check_pointers(const Plan &p, const void *r, const void *k, const v
 
 // ---- execution --------------------------------------------------------------
 
-wkv_status_t run(const Plan &p, const Tensors &t, void *ws, hipStream_t st) {
+wkv_status_t run(const Plan &p, const Tensors &t, const Variant &var, void *ws, hipStream_t st) {
     Geometry g = p.g;
     char *base = static_cast<char *>(ws);
     hipError_t e;
@@ -235,7 +238,7 @@ wkv_status_t run(const Plan &p, const Tensors &t, void *ws, hipStream_t st) {
     }
     const KernelTiming tm{g_ev_before, g_ev_after};
     if (!p.bf16) {
-        if ((e = launch_serial(g, t, false, st, tm)) != hipSuccess) return fail_hip(e, "scan launch");
+        if ((e = launch_serial(g, t, false, var, st, tm)) != hipSuccess) return fail_hip(e, "scan launch");
         return WKV_OK;
     }
     Workspace w{};
@@ -243,10 +246,54 @@ wkv_status_t run(const Plan &p, const Tensors &t, void *ws, hipStream_t st) {
         w.seg_state = reinterpret_cast<float *>(base + p.off_seg_state);
         w.seg_start = reinterpret_cast<float *>(base + p.off_seg_start);
     }
-    if (p.split && (e = launch_segment_states(g, t, w, st)) != hipSuccess)
+    if (p.split && (e = launch_segment_states(g, t, w, var, st)) != hipSuccess)
         return fail_hip(e, "segment-state launch");
-    if ((e = launch_chunked_main(g, t, w, st, tm)) != hipSuccess) return fail_hip(e, "scan launch");
+    if ((e = launch_chunked_main(g, t, w, var, st, tm)) != hipSuccess) return fail_hip(e, "scan launch");
     return WKV_OK;
+}
+
+constexpr unsigned kKnownFlags = WKV_FLAG_DECAY_LOG | WKV_FLAG_FINCH_C2;
+
+wkv_status_t variant_of(unsigned flags, Variant &v) {
+    if (flags & ~kKnownFlags) return fail(WKV_EUNSUPPORTED, "unknown flags 0x%x", flags & ~kKnownFlags);
+    v.log_decay = (flags & WKV_FLAG_DECAY_LOG) != 0;
+    v.c2 = (flags & WKV_FLAG_FINCH_C2) != 0;
+    return WKV_OK;
+}
+
+wkv_status_t prefill_fixed(const void *r, const void *k, const void *v, const void *w,
+                           const float *u, const void *u2, const float *state_in, float *o,
+                           float *state_out, int B, int T, int H, int D, wkv_dtype_t dt,
+                           unsigned flags, void *ws, size_t ws_bytes, void *stream) {
+    g_last_error.clear();
+    Variant var;
+    if (wkv_status_t s = variant_of(flags, var)) return s;
+    Plan p;
+    if (wkv_status_t s = plan_fixed(B, T, H, D, dt, p)) return s;
+    if (wkv_status_t s = check_pointers(p, var, r, k, v, w, u, u2, state_in, o, state_out, ws,
+                                        ws_bytes, nullptr))
+        return s;
+    Tensors t{r, k, v, w, var.c2 ? nullptr : u, state_in, o, state_out, u2};
+    return run(p, t, var, ws, static_cast<hipStream_t>(stream));
+}
+
+wkv_status_t prefill_varlen(const void *r, const void *k, const void *v, const void *w,
+                            const float *u, const void *u2, const int32_t *cu_dev,
+                            const int32_t *cu_host, int N, const float *state_in, float *o,
+                            float *state_out, int H, int D, wkv_dtype_t dt, unsigned flags,
+                            void *ws, size_t ws_bytes, void *stream) {
+    g_last_error.clear();
+    Variant var;
+    if (wkv_status_t s = variant_of(flags, var)) return s;
+    Plan p;
+    if (wkv_status_t s = plan_varlen(cu_host, N, H, D, dt, p)) return s;
+    if (N > 0 && !cu_dev) return fail(WKV_EINVAL, "cu_seqlens_dev is NULL");
+    if (wkv_status_t s = check_pointers(p, var, r, k, v, w, u, u2, state_in, o, state_out, ws,
+                                        ws_bytes, cu_dev))
+        return s;
+    p.g.cu = cu_dev;
+    Tensors t{r, k, v, w, var.c2 ? nullptr : u, state_in, o, state_out, u2};
+    return run(p, t, var, ws, static_cast<hipStream_t>(stream));
 }
 
 }  // namespace
@@ -298,30 +345,33 @@ wkv_status_t wkv_prefill(const void *r, const void *k, const void *v, const void
                          const float *u, const float *state_in, float *o, float *state_out,
                          int B, int T, int H, int D, wkv_dtype_t dt, void *ws, size_t ws_bytes,
                          void *stream) {
-    g_last_error.clear();
-    Plan p;
-    if (wkv_status_t s = plan_fixed(B, T, H, D, dt, p)) return s;
-    if (wkv_status_t s = check_pointers(p, r, k, v, w, u, state_in, o, state_out, ws, ws_bytes,
-                                        nullptr))
-        return s;
-    Tensors t{r, k, v, w, u, state_in, o, state_out};
-    return run(p, t, ws, static_cast<hipStream_t>(stream));
+    return prefill_fixed(r, k, v, w, u, nullptr, state_in, o, state_out, B, T, H, D, dt, 0u, ws,
+                         ws_bytes, stream);
+}
+
+wkv_status_t wkv_prefill_ex(const void *r, const void *k, const void *v, const void *w,
+                            const float *u, const void *u2, const float *state_in, float *o,
+                            float *state_out, int B, int T, int H, int D, wkv_dtype_t dt,
+                            unsigned flags, void *ws, size_t ws_bytes, void *stream) {
+    return prefill_fixed(r, k, v, w, u, u2, state_in, o, state_out, B, T, H, D, dt, flags, ws,
+                         ws_bytes, stream);
 }
 
 wkv_status_t wkv_prefill_varlen(const void *r, const void *k, const void *v, const void *w,
                                 const float *u, const int32_t *cu_dev, const int32_t *cu_host,
                                 int N, const float *state_in, float *o, float *state_out, int H,
                                 int D, wkv_dtype_t dt, void *ws, size_t ws_bytes, void *stream) {
-    g_last_error.clear();
-    Plan p;
-    if (wkv_status_t s = plan_varlen(cu_host, N, H, D, dt, p)) return s;
-    if (N > 0 && !cu_dev) return fail(WKV_EINVAL, "cu_seqlens_dev is NULL");
-    if (wkv_status_t s = check_pointers(p, r, k, v, w, u, state_in, o, state_out, ws, ws_bytes,
-                                        cu_dev))
-        return s;
-    p.g.cu = cu_dev;
-    Tensors t{r, k, v, w, u, state_in, o, state_out};
-    return run(p, t, ws, static_cast<hipStream_t>(stream));
+    return prefill_varlen(r, k, v, w, u, nullptr, cu_dev, cu_host, N, state_in, o, state_out, H,
+                          D, dt, 0u, ws, ws_bytes, stream);
+}
+
+wkv_status_t wkv_prefill_varlen_ex(const void *r, const void *k, const void *v, const void *w,
+                                   const float *u, const void *u2, const int32_t *cu_dev,
+                                   const int32_t *cu_host, int N, const float *state_in,
+                                   float *o, float *state_out, int H, int D, wkv_dtype_t dt,
+                                   unsigned flags, void *ws, size_t ws_bytes, void *stream) {
+    return prefill_varlen(r, k, v, w, u, u2, cu_dev, cu_host, N, state_in, o, state_out, H, D,
+                          dt, flags, ws, ws_bytes, stream);
 }
 
 }  // extern "C"

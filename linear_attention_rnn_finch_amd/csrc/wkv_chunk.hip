@@ -18,6 +18,16 @@
 // about 16 significant bits per product.  The 64x64 fp32 state stays in
 // registers for the whole segment.
 //
+// Two further forms of the same section are compile-time switches:
+//  - LOGD: the decay input holds d with w = exp(-exp(d)) (paragraph
+//    "Data-dependent decay"), so log2 w = -exp(d) log2(e) is formed directly
+//    (one exponential instead of a logarithm; no precision is lost to w
+//    rounding to 1 in bf16);
+//  - C2: the Finch-C2 mixer -- keys enter as k (1 - w) (paragraph "Key
+//    computation with normalization property"), no static bonus (the
+//    diagonal of A is zero), and the second value u'_t (a fifth input stream,
+//    staged like the others) is added to o (output equation).
+//
 // A chunk in which some channel decays by more than 2^96 over half a chunk
 // ("stiff") would push the rescaling factors out of range; such a chunk is
 // evaluated token by token instead (exact, same registers), so the result is
@@ -51,17 +61,24 @@ typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 constexpr float kStiffLog2 = 96.f;            // largest |half-chunk log2 decay| rescaled
 constexpr float kLog2Floor = -127.f;          // log2 w below this only occurs in stiff chunks
 constexpr unsigned kOnePair = 0x3F803F80u;    // two bf16 1.0 (padding value of w)
+constexpr unsigned kNegInfPair = 0xFF80FF80u;  // two bf16 -inf (padding value of d: w = 1)
+constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kTileElems = kChunk * kHeadDim; // one 64 x 64 bf16 tile
 constexpr int kStageRow = 72;                  // staging row pitch in bf16 (144 B)
 constexpr int kStageElems = kChunk * kStageRow;
 
 enum class Mode { Main, State };
 
-// Registers holding one prefetched chunk: r, k, w, v as 16-byte pieces of
-// whole token rows (rows tid/8 and tid/8 + 32, piece tid%8), so that every load
-// instruction covers complete 128-byte lines.
+// Registers holding one prefetched chunk: r, k, w, v (and the C2 second
+// value) as 16-byte pieces of whole token rows (rows tid/8 and tid/8 + 32,
+// piece tid%8), so that every load instruction covers complete 128-byte lines.
+template <bool C2>
 struct ChunkRegs {
     u32x4 r[2], k[2], w[2], v[2];
+};
+template <>
+struct ChunkRegs<true> {
+    u32x4 r[2], k[2], w[2], v[2], u2[2];
 };
 
 // ---- LDS tile layouts ---------------------------------------------------------
@@ -97,6 +114,7 @@ __device__ __forceinline__ Rsrc chunk_rsrc(const void *base, int64_t row0, int r
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<char *>(p), (short)0, bytes, kRsrcWord3);
 }
 
+template <int NStage>
 struct Smem {
     uint16_t v[kTileElems];          // values of the chunk
     uint16_t rt_hi[kTileElems];      // r~ = r 2^{Lam_{t-1}-R}, bf16 hi/lo planes
@@ -108,7 +126,7 @@ struct Smem {
             uint16_t a_hi[kTileElems];   // in-chunk matrix A[t][s], hi/lo planes
             uint16_t a_lo[kTileElems];
         };
-        uint16_t stage[3][kStageElems];  // raw r, k, w rows of the chunk (until the first barrier)
+        uint16_t stage[NStage][kStageElems];  // raw r, k, w (, u') rows of the chunk (until the first barrier)
     };
     alignas(16) float bonus_part[4][kChunk];   // per-wave partial sums of r.u.k per token
     alignas(16) float row_exp2ref[kHeadDim];   // 2^{R_i}
@@ -117,8 +135,12 @@ struct Smem {
     int stiff[4];
 };
 // the token-serial path stages 64 x 64 fp32 outputs across rt_hi and rt_lo
-static_assert(offsetof(Smem, rt_lo) == offsetof(Smem, rt_hi) + sizeof(uint16_t) * kTileElems,
+static_assert(offsetof(Smem<3>, rt_lo) == offsetof(Smem<3>, rt_hi) + sizeof(uint16_t) * kTileElems,
               "rt planes must be adjacent");
+static_assert(offsetof(Smem<4>, rt_lo) == offsetof(Smem<4>, rt_hi) + sizeof(uint16_t) * kTileElems,
+              "rt planes must be adjacent");
+// two workgroups per compute unit (160 KB of LDS)
+static_assert(sizeof(Smem<4>) <= 80 * 1024, "two workgroups per CU");
 
 using lds_i16x4 = __attribute__((address_space(3))) i16x4;
 using lds_u32x2 = __attribute__((address_space(3))) u32x2;
@@ -260,8 +282,8 @@ __device__ __forceinline__ float sum_rows4(float x) {
 // (SB <= TB), computed as A^T = k~ r~^T and masked on diagonal blocks (bonus
 // on the diagonal, zeros above), split and stored.  NT tiles are processed
 // together so that their MFMA chains interleave.
-template <int NT>
-__device__ __forceinline__ void a_tiles(Smem &sm, const LdsBases &lb, const int (&TB)[NT],
+template <bool Bonus, int NT, typename SM>
+__device__ __forceinline__ void a_tiles(SM &sm, const LdsBases &lb, const int (&TB)[NT],
                                         const int (&SB)[NT], int i16, int grp) {
     f32x4 a[NT];
     #pragma unroll
@@ -288,7 +310,8 @@ __device__ __forceinline__ void a_tiles(Smem &sm, const LdsBases &lb, const int 
         // a[n][e] = A[t][s], t = 16*TB + i16, s = 16*SB + 4*grp + e
         const int t = 16 * TB[n] + i16;
         if (SB[n] == TB[n]) {
-            const float b = sm.bonus_part[0][t] + sm.bonus_part[1][t] + sm.bonus_part[2][t] + sm.bonus_part[3][t];
+            const float b = Bonus ? sm.bonus_part[0][t] + sm.bonus_part[1][t] + sm.bonus_part[2][t] + sm.bonus_part[3][t]
+                                  : 0.f;
             #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int s_loc = 4 * grp + e;
@@ -303,9 +326,19 @@ __device__ __forceinline__ void a_tiles(Smem &sm, const LdsBases &lb, const int 
     }
 }
 
-template <Mode M>
+// 1 - w for the key factor of Finch-C2, from the decay input x (w itself, or
+// d with e = exp(d) already formed): exact for a bf16 w; for d it is
+// -expm1(-e), accurate also when w is close to 1.
+template <bool LOGD>
+__device__ __forceinline__ float one_minus_w(float x, float e) {
+    return LOGD ? -expm1f(-e) : 1.f - x;
+}
+
+template <Mode M, bool LOGD, bool C2>
 __global__ __launch_bounds__(256, 2) void wkv_chunk_kernel(Geometry g, Tensors t, Workspace ws) {
-    __shared__ Smem sm;
+    constexpr bool kU2 = M == Mode::Main && C2;            // second value staged and added
+    using SM = Smem<kU2 ? 4 : 3>;
+    __shared__ SM sm;
 
     const int item = blockIdx.x;
     const int h = item % g.H;
@@ -343,7 +376,7 @@ __global__ __launch_bounds__(256, 2) void wkv_chunk_kernel(Geometry g, Tensors t
     // pre-processing layout: channels c0..c0+3, tokens 4*i16 .. 4*i16+3
     const int c0 = 16 * wave + 4 * grp;
     f32x4 u4 = {0.f, 0.f, 0.f, 0.f};
-    if (M == Mode::Main) u4 = *reinterpret_cast<const f32x4 *>(t.u + (size_t)h * kHeadDim + c0);
+    if (M == Mode::Main && !C2) u4 = *reinterpret_cast<const f32x4 *>(t.u + (size_t)h * kHeadDim + c0);
     float lam_seg[4] = {0.f, 0.f, 0.f, 0.f};                // State: segment log2-decay per channel
 
 
@@ -370,10 +403,15 @@ __global__ __launch_bounds__(256, 2) void wkv_chunk_kernel(Geometry g, Tensors t
     // of 16-byte piece 2*wave + grp/2
     #pragma unroll
     for (int a = 0; a < 4; ++a) st_rd[a] = off_stage(4 * i16 + a, 2 * wave + (grp >> 1)) + 4 * (grp & 1);
+    // second value in the accumulator layout: rows 16*tb + i16, channels
+    // 16*wave + 4*grp .. +3
+    int st_u2[4];
+    #pragma unroll
+    for (int tb = 0; tb < 4; ++tb) st_u2[tb] = off_stage(16 * tb + i16, 2 * wave + (grp >> 1)) + 4 * (grp & 1);
     int off_out[4];                                      // o rows 16*tb + i16, columns 16*wave + 4*grp
     #pragma unroll
     for (int tb = 0; tb < 4; ++tb) off_out[tb] = (16 * tb + i16) * H * kRowOut + 4 * (16 * wave + 4 * grp);
-    auto issue_loads = [&](ChunkRegs &P, int64_t tc) {
+    auto issue_loads = [&](ChunkRegs<kU2> &P, int64_t tc) {
         const int rows = (int)min<int64_t>(kChunk, it.t1 - tc);
         const Rsrc rk = chunk_rsrc(t.k, tc, rows, H, h, kRowIn);
         const Rsrc rw = chunk_rsrc(t.w, tc, rows, H, h, kRowIn);
@@ -382,6 +420,13 @@ __global__ __launch_bounds__(256, 2) void wkv_chunk_kernel(Geometry g, Tensors t
             const Rsrc rr = chunk_rsrc(t.r, tc, rows, H, h, kRowIn);
             #pragma unroll
             for (int m = 0; m < 2; ++m) P.r[m] = __builtin_amdgcn_raw_buffer_load_b128(rr, off_vin[m], 0, 0);
+        }
+        if constexpr (kU2) {
+            // no second value: a resource with no records (every load reads 0)
+            const Rsrc ru = t.u2 ? chunk_rsrc(t.u2, tc, rows, H, h, kRowIn)
+                                 : __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(t.v), (short)0, 0, kRsrcWord3);
+            #pragma unroll
+            for (int m = 0; m < 2; ++m) P.u2[m] = __builtin_amdgcn_raw_buffer_load_b128(ru, off_vin[m], 0, 0);
         }
         #pragma unroll
         for (int m = 0; m < 2; ++m) {
@@ -407,7 +452,7 @@ __global__ __launch_bounds__(256, 2) void wkv_chunk_kernel(Geometry g, Tensors t
             __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, o_pend[tb]), ro, off_out[tb], 0, 0);
     };
 
-    ChunkRegs P;
+    ChunkRegs<kU2> P;
     if (n_chunks > 0) issue_loads(P, it.t0);
 
     for (int c = 0; c < n_chunks; ++c) {
@@ -431,6 +476,7 @@ __global__ __launch_bounds__(256, 2) void wkv_chunk_kernel(Geometry g, Tensors t
             lds_write_b128(sm.stage[1], st_wr[m], P.k[m]);
             lds_write_b128(sm.stage[2], st_wr[m], P.w[m]);
             if (M == Mode::Main) lds_write_b128(sm.stage[0], st_wr[m], P.r[m]);
+            if constexpr (kU2) lds_write_b128(sm.stage[3], st_wr[m], P.u2[m]);
         }
         if (M == Mode::Main && c > 0) store_o();
         if (c + 1 < n_chunks) issue_loads(P, tc + kChunk);
@@ -444,10 +490,16 @@ __global__ __launch_bounds__(256, 2) void wkv_chunk_kernel(Geometry g, Tensors t
             pw[a] = lds_read_b64(sm.stage[2], st_rd[a]);
             if (M == Mode::Main) pr[a] = lds_read_b64(sm.stage[0], st_rd[a]);
         }
+        u32x2 pu2[4];
+        if constexpr (kU2) {
+            #pragma unroll
+            for (int tb = 0; tb < 4; ++tb) pu2[tb] = lds_read_b64(sm.stage[3], st_u2[tb]);
+        }
         if (nt < kChunk) {                      // partial last chunk: w = 1 on padding rows
+            constexpr unsigned kPad = LOGD ? kNegInfPair : kOnePair;
             #pragma unroll
             for (int a = 0; a < 4; ++a)
-                if (4 * i16 + a >= nt) pw[a] = u32x2{kOnePair, kOnePair};
+                if (4 * i16 + a >= nt) pw[a] = u32x2{kPad, kPad};
         }
         float lam[4][4], kk_[4][4], rr[4][4];
         #pragma unroll
@@ -464,10 +516,16 @@ __global__ __launch_bounds__(256, 2) void wkv_chunk_kernel(Geometry g, Tensors t
 
         // ---- pre-processing: log-decay prefix, rescaled operands, bonus -------
         {
+            // lam holds the decay input (w, or d); it becomes log2 w, floored
             #pragma unroll
             for (int a = 0; a < 4; ++a)
                 #pragma unroll
-                for (int q = 0; q < 4; ++q) lam[a][q] = fmaxf(__builtin_amdgcn_logf(lam[a][q]), kLog2Floor);
+                for (int q = 0; q < 4; ++q) {
+                    const float x = lam[a][q];
+                    const float e = LOGD ? __builtin_amdgcn_exp2f(x * kLog2e) : 0.f;   // exp(d)
+                    if (C2) kk_[a][q] *= one_minus_w<LOGD>(x, e);
+                    lam[a][q] = fmaxf(LOGD ? -e * kLog2e : __builtin_amdgcn_logf(x), kLog2Floor);
+                }
             // inclusive prefix over the chunk: in-lane over 4 tokens, then across
             // the 16 lanes; lam becomes E_t = Lam_t - reference (Main: R = Lam_31,
             // State: Lam_63), and off = E_{t-1} for the first token of the lane
@@ -511,7 +569,7 @@ __global__ __launch_bounds__(256, 2) void wkv_chunk_kernel(Geometry g, Tensors t
                         const float e_prev = a == 0 ? off[q] : lam[a - 1][q];   // Lam_{t-1} - R
                         rs[q] = rr[a][q] * __builtin_amdgcn_exp2f(e_prev);
                         ks[q] = kk_[a][q] * __builtin_amdgcn_exp2f(-lam[a][q]);  // R - Lam_t
-                        bp[a] += rr[a][q] * u4[q] * kk_[a][q];
+                        if (!C2) bp[a] += rr[a][q] * u4[q] * kk_[a][q];
                     }
                     u32x2 rh, rl, kh, kl;
                     split4(rs[0], rs[1], rs[2], rs[3], rh, rl);
@@ -520,9 +578,9 @@ __global__ __launch_bounds__(256, 2) void wkv_chunk_kernel(Geometry g, Tensors t
                     lds_write_b64(sm.rt_lo, lb.pw_rt[a], rl);
                     lds_write_b64(sm.kt_hi, lb.pw_kt[a], kh);
                     lds_write_b64(sm.kt_lo, lb.pw_kt[a], kl);
-                    bp[a] = sum_rows4(bp[a]);
+                    if (!C2) bp[a] = sum_rows4(bp[a]);
                 }
-                if (grp == 0) {
+                if (!C2 && grp == 0) {
                     f32x4 b4 = {bp[0], bp[1], bp[2], bp[3]};
                     *reinterpret_cast<f32x4 *>(&sm.bonus_part[wave][4 * i16]) = b4;
                 }
@@ -605,13 +663,19 @@ __global__ __launch_bounds__(256, 2) void wkv_chunk_kernel(Geometry g, Tensors t
                     kv[ib][0] = bf16_lo(b.x); kv[ib][1] = bf16_hi(b.x); kv[ib][2] = bf16_lo(b.y); kv[ib][3] = bf16_hi(b.y);
                     wv[ib][0] = bf16_lo(d.x); wv[ib][1] = bf16_hi(d.x); wv[ib][2] = bf16_lo(d.y); wv[ib][3] = bf16_hi(d.y);
                     #pragma unroll
-                    for (int e = 0; e < 4; ++e) part += rv[e] * S[ib][e];
+                    for (int e = 0; e < 4; ++e) {
+                        part += rv[e] * S[ib][e];
+                        const float x = wv[ib][e];
+                        const float ex = LOGD ? __builtin_amdgcn_exp2f(x * kLog2e) : 0.f;
+                        if (C2) kv[ib][e] *= one_minus_w<LOGD>(x, ex);
+                        if (LOGD) wv[ib][e] = __builtin_amdgcn_exp2f(-ex * kLog2e);
+                    }
                 }
                 part = sum_rows4(part);
                 const unsigned vbits = sm.v[off_v(tt, 16 * wave + i16)];
                 const float vj = __uint_as_float(vbits << 16);
-                const float b = sm.bonus_part[0][tt] + sm.bonus_part[1][tt] +
-                                sm.bonus_part[2][tt] + sm.bonus_part[3][tt];
+                const float b = C2 ? 0.f : sm.bonus_part[0][tt] + sm.bonus_part[1][tt] +
+                                           sm.bonus_part[2][tt] + sm.bonus_part[3][tt];
                 if (grp == (tt & 3)) o_stage[tt * kHeadDim + 16 * wave + i16] = part + b * vj;
                 #pragma unroll
                 for (int ib = 0; ib < 4; ++ib)
@@ -634,16 +698,16 @@ __global__ __launch_bounds__(256, 2) void wkv_chunk_kernel(Geometry g, Tensors t
         }
         if (wave == 0) {
             const int TB[3] = {0, 1, 2}, SB[3] = {0, 0, 0};
-            a_tiles<3>(sm, lb, TB, SB, i16, grp);
+            a_tiles<!C2, 3>(sm, lb, TB, SB, i16, grp);
         } else if (wave == 1) {
             const int TB[3] = {1, 2, 3}, SB[3] = {1, 1, 0};
-            a_tiles<3>(sm, lb, TB, SB, i16, grp);
+            a_tiles<!C2, 3>(sm, lb, TB, SB, i16, grp);
         } else if (wave == 2) {
             const int TB[2] = {2, 3}, SB[2] = {2, 1};
-            a_tiles<2>(sm, lb, TB, SB, i16, grp);
+            a_tiles<!C2, 2>(sm, lb, TB, SB, i16, grp);
         } else {
             const int TB[2] = {3, 3}, SB[2] = {3, 2};
-            a_tiles<2>(sm, lb, TB, SB, i16, grp);
+            a_tiles<!C2, 2>(sm, lb, TB, SB, i16, grp);
         }
 
         // ---- read-out of the carried state: o^T = (2^R S)^T r~^T ------------------
@@ -732,6 +796,15 @@ __global__ __launch_bounds__(256, 2) void wkv_chunk_kernel(Geometry g, Tensors t
         }
 
         // o of this chunk is stored early in the next iteration (see store_o)
+        if constexpr (kU2) {                               // + u'_t (Finch-C2 output)
+            #pragma unroll
+            for (int tb = 0; tb < 4; ++tb) {
+                acc[tb][0] += bf16_lo(pu2[tb].x);
+                acc[tb][1] += bf16_hi(pu2[tb].x);
+                acc[tb][2] += bf16_lo(pu2[tb].y);
+                acc[tb][3] += bf16_hi(pu2[tb].y);
+            }
+        }
         #pragma unroll
         for (int tb = 0; tb < 4; ++tb) o_pend[tb] = acc[tb];
         tc_pend = tc;
@@ -818,13 +891,23 @@ __global__ __launch_bounds__(kScanThreads) void wkv_segment_scan_kernel(Geometry
     }
 }
 
+template <Mode M>
+using ChunkKernel = void (*)(Geometry, Tensors, Workspace);
+
+template <Mode M>
+ChunkKernel<M> chunk_kernel_for(Variant v) {
+    if (v.log_decay)
+        return v.c2 ? wkv_chunk_kernel<M, true, true> : wkv_chunk_kernel<M, true, false>;
+    return v.c2 ? wkv_chunk_kernel<M, false, true> : wkv_chunk_kernel<M, false, false>;
+}
+
 }  // namespace
 
 hipError_t launch_segment_states(const Geometry &g, const Tensors &t, const Workspace &ws,
-                                 hipStream_t st) {
+                                 Variant v, hipStream_t st) {
     const int64_t items = (int64_t)g.n_seg * g.H;
     if (items <= 0) return hipSuccess;
-    hipLaunchKernelGGL(wkv_chunk_kernel<Mode::State>, dim3((unsigned)items), dim3(256), 0, st, g, t, ws);
+    hipLaunchKernelGGL(chunk_kernel_for<Mode::State>(v), dim3((unsigned)items), dim3(256), 0, st, g, t, ws);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(wkv_segment_scan_kernel, dim3((unsigned)(g.n_seq * g.H * kScanSlices)), dim3(kScanThreads), 0, st,
@@ -833,14 +916,14 @@ hipError_t launch_segment_states(const Geometry &g, const Tensors &t, const Work
 }
 
 hipError_t launch_chunked_main(const Geometry &g, const Tensors &t, const Workspace &ws,
-                               hipStream_t st, KernelTiming tm) {
+                               Variant v, hipStream_t st, KernelTiming tm) {
     const int64_t items = (int64_t)g.n_seg * g.H;
     if (items <= 0) return hipSuccess;
+    const ChunkKernel<Mode::Main> kern = chunk_kernel_for<Mode::Main>(v);
     if (tm.start || tm.stop)
-        hipExtLaunchKernelGGL(wkv_chunk_kernel<Mode::Main>, dim3((unsigned)items), dim3(256), 0, st,
-                              tm.start, tm.stop, 0, g, t, ws);
+        hipExtLaunchKernelGGL(kern, dim3((unsigned)items), dim3(256), 0, st, tm.start, tm.stop, 0, g, t, ws);
     else
-        hipLaunchKernelGGL(wkv_chunk_kernel<Mode::Main>, dim3((unsigned)items), dim3(256), 0, st, g, t, ws);
+        hipLaunchKernelGGL(kern, dim3((unsigned)items), dim3(256), 0, st, g, t, ws);
     return hipGetLastError();
 }
 

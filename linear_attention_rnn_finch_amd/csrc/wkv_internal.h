@@ -75,13 +75,20 @@ __device__ inline ItemRange decode_segment(const Geometry &g, int s) {
     return it;
 }
 
-// Tensors of one call.  r, k, v, w are bf16 bit patterns or fp32.
+// Tensors of one call.  r, k, v, w (and u2) are bf16 bit patterns or fp32.
 struct Tensors {
-    const void *r, *k, *v, *w;
-    const float *u;          // [H, D]
+    const void *r, *k, *v, *w;   // w holds w_t, or d_t when the decay is given as d
+    const float *u;          // [H, D] static bonus (base Finch; unused by Finch-C2)
     const float *state_in;   // [n_seq, H, D, D] or null
     float *o;                // [tokens, H, D]
     float *state_out;        // [n_seq, H, D, D] or null
+    const void *u2;          // Finch-C2 second value [tokens, H, D], or null
+};
+
+// Form of the recurrence (compile-time switches of the kernels).
+struct Variant {
+    bool log_decay = false;  // decay input d_t, w_t = exp(-exp(d_t))
+    bool c2 = false;         // Finch-C2: keys times (1 - w_t), no bonus, + u2
 };
 
 // Workspace views (fp32).  seg_state[item]: the segment's zero-start end state
@@ -103,14 +110,14 @@ struct KernelTiming {
     hipEvent_t start = nullptr, stop = nullptr;
 };
 
-hipError_t launch_serial(const Geometry &g, const Tensors &t, bool bf16, hipStream_t st,
+hipError_t launch_serial(const Geometry &g, const Tensors &t, bool bf16, Variant v, hipStream_t st,
                          KernelTiming tm = {});
 // bf16 path: state pass + segment scan (only when some sequence is split), then
 // the main chunked scan.
 hipError_t launch_segment_states(const Geometry &g, const Tensors &t, const Workspace &ws,
-                                 hipStream_t st);
+                                 Variant v, hipStream_t st);
 hipError_t launch_chunked_main(const Geometry &g, const Tensors &t, const Workspace &ws,
-                               hipStream_t st, KernelTiming tm = {});
+                               Variant v, hipStream_t st, KernelTiming tm = {});
 hipError_t launch_plan_varlen(const Geometry &g, int32_t *seg_off, int32_t *seg_seq,
                               hipStream_t st);
 

@@ -7,6 +7,11 @@
 // normwise) leaves no room for the bf16 matrix-core splits of the chunked
 // kernel.  One workgroup per (sequence, head); the 64x64 state lives in
 // registers: thread (q, j) owns rows 16q .. 16q+15 of value column j.
+//
+// LOGD: the decay input is d_t and w_t = exp(-exp(d_t)) (paragraph
+// "Data-dependent decay").  C2: the Finch-C2 mixer -- the state takes
+// k_t (1 - w_t), there is no bonus, and the second value u'_t is added:
+// o_t = r_t S + u'_t.
 #include <hip/hip_ext.h>
 
 #include "wkv_internal.h"
@@ -21,7 +26,7 @@ __device__ inline float load_in(const uint16_t *p, size_t i) {
     return __uint_as_float((uint32_t)p[i] << 16);
 }
 
-template <typename In>
+template <typename In, bool LOGD, bool C2>
 __global__ __launch_bounds__(256) void wkv_serial_kernel(Geometry g, Tensors t) {
     const int item = blockIdx.x;
     const int h = item % g.H;
@@ -44,26 +49,31 @@ __global__ __launch_bounds__(256) void wkv_serial_kernel(Geometry g, Tensors t) 
     const In *kp = static_cast<const In *>(t.k);
     const In *vp = static_cast<const In *>(t.v);
     const In *wp = static_cast<const In *>(t.w);
+    const In *u2p = static_cast<const In *>(t.u2);
 
     float S[16];
     const size_t state_off = ((size_t)it.n * g.H + h) * (kHeadDim * kHeadDim);
     #pragma unroll
     for (int e = 0; e < 16; ++e)
         S[e] = t.state_in ? t.state_in[state_off + (16 * q + e) * kHeadDim + j] : 0.f;
-    if (tid < kHeadDim) us[tid] = t.u[(size_t)h * kHeadDim + tid];
+    if (tid < kHeadDim) us[tid] = C2 ? 0.f : t.u[(size_t)h * kHeadDim + tid];
 
     for (int64_t tb = it.t0; tb < it.t1; tb += kBlockTokens) {
         const int nt = (int)min<int64_t>(kBlockTokens, it.t1 - tb);
         __syncthreads();                        // previous block fully consumed
         for (int row = q; row < nt; row += 4) {
             const size_t idx = ((size_t)(tb + row) * g.H + h) * kHeadDim + j;
+            const float x = load_in(wp, idx);
+            const float e = LOGD ? expf(x) : 0.f;                   // exp(d)
+            const float w = LOGD ? expf(-e) : x;
+            const float kf = C2 ? (LOGD ? -expm1f(-e) : 1.f - x) : 1.f;
             tr[row][j] = load_in(rp, idx);
-            tk[row][j] = load_in(kp, idx);
+            tk[row][j] = load_in(kp, idx) * kf;
             tv[row][j] = load_in(vp, idx);
-            tw[row][j] = load_in(wp, idx);
+            tw[row][j] = w;
         }
         __syncthreads();
-        if (tid < nt) {                         // bonus r_t . u . k_t per token
+        if (!C2 && tid < nt) {                  // bonus r_t . u . k_t per token
             float b = 0.f;
             for (int i = 0; i < kHeadDim; ++i) b += tr[tid][i] * us[i] * tk[tid][i];
             bonus[tid] = b;
@@ -80,9 +90,14 @@ __global__ __launch_bounds__(256) void wkv_serial_kernel(Geometry g, Tensors t) 
         }
         __syncthreads();
         for (int row = q; row < nt; row += 4) {
-            const float o = part[0][row][j] + part[1][row][j] + part[2][row][j] +
-                            part[3][row][j] + bonus[row] * tv[row][j];
-            t.o[((size_t)(tb + row) * g.H + h) * kHeadDim + j] = o;
+            const size_t idx = ((size_t)(tb + row) * g.H + h) * kHeadDim + j;
+            const float rs = part[0][row][j] + part[1][row][j] + part[2][row][j] + part[3][row][j];
+            float o;
+            if (C2)
+                o = rs + (u2p ? load_in(u2p, idx) : 0.f);
+            else
+                o = rs + bonus[row] * tv[row][j];
+            t.o[idx] = o;
         }
     }
     if (t.state_out && it.p == it.P - 1) {
@@ -92,17 +107,24 @@ __global__ __launch_bounds__(256) void wkv_serial_kernel(Geometry g, Tensors t) 
     }
 }
 
+template <typename In>
+void (*serial_kernel_for(Variant v))(Geometry, Tensors) {
+    if (v.log_decay)
+        return v.c2 ? wkv_serial_kernel<In, true, true> : wkv_serial_kernel<In, true, false>;
+    return v.c2 ? wkv_serial_kernel<In, false, true> : wkv_serial_kernel<In, false, false>;
+}
+
 }  // namespace
 
-hipError_t launch_serial(const Geometry &g, const Tensors &t, bool bf16, hipStream_t st,
+hipError_t launch_serial(const Geometry &g, const Tensors &t, bool bf16, Variant v, hipStream_t st,
                          KernelTiming tm) {
     const int64_t items = (int64_t)g.n_seg * g.H;
     if (items <= 0) return hipSuccess;
     const dim3 grid((unsigned)items), block(256);
     if (bf16)
-        hipExtLaunchKernelGGL(wkv_serial_kernel<uint16_t>, grid, block, 0, st, tm.start, tm.stop, 0, g, t);
+        hipExtLaunchKernelGGL(serial_kernel_for<uint16_t>(v), grid, block, 0, st, tm.start, tm.stop, 0, g, t);
     else
-        hipExtLaunchKernelGGL(wkv_serial_kernel<float>, grid, block, 0, st, tm.start, tm.stop, 0, g, t);
+        hipExtLaunchKernelGGL(serial_kernel_for<float>(v), grid, block, 0, st, tm.start, tm.stop, 0, g, t);
     return hipGetLastError();
 }
 

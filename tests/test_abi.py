@@ -39,6 +39,10 @@ def lib():
     L.wkv_prefill_workspace_bytes.argtypes = [i] * 5
     L.wkv_prefill_varlen_workspace_bytes.restype = sz
     L.wkv_prefill_varlen_workspace_bytes.argtypes = [vp, i, i, i, i]
+    L.wkv_prefill_ex.restype = i
+    L.wkv_prefill_ex.argtypes = [vp] * 9 + [i] * 5 + [ctypes.c_uint, vp, sz, vp]
+    L.wkv_prefill_varlen_ex.restype = i
+    L.wkv_prefill_varlen_ex.argtypes = [vp] * 8 + [i, vp, vp, vp, i, i, i, ctypes.c_uint, vp, sz, vp]
     L.wkv_last_error.restype = ctypes.c_char_p
     L.wkv_status_string.restype = ctypes.c_char_p
     L.wkv_status_string.argtypes = [i]
@@ -53,7 +57,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_abi_version_and_status_strings(lib):
-    assert lib.wkv_abi_version() == 1
+    assert lib.wkv_abi_version() == 2
     for s in range(5):
         assert lib.wkv_status_string(s)
     assert lib.wkv_status_string(99) == b"unknown status"
@@ -160,3 +164,40 @@ def test_varlen_workspace_grows_with_segments(lib):
     b = lib.wkv_prefill_varlen_workspace_bytes(big.ctypes.data, 3, 32, 64, BF16)
     assert 0 < a < b
     assert a % 256 == 0 and b % 256 == 0
+
+
+U2 = A * 30
+LOG, C2 = 1, 2
+
+
+def call_ex(lib, flags, u=U, u2=None, B=1, T=128, H=4, dt=BF16, o=O, ws=WS):
+    ws_bytes = lib.wkv_prefill_workspace_bytes(B, T, H, 64, dt)
+    st = lib.wkv_prefill_ex(R, K, V, W, u, u2, S_IN, o, S_OUT, B, T, H, 64, dt, flags, ws,
+                            ws_bytes, None)
+    return st, lib.wkv_last_error().decode()
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(flags=4), EUNSUP),                          # unknown flag bit
+    (dict(flags=LOG | 8), EUNSUP),
+    (dict(flags=0, u2=U2), EINVAL),                   # second value without C2
+    (dict(flags=LOG, u=None), EINVAL),                # base Finch needs its bonus
+    (dict(flags=C2, u2=U2 + 8), EINVAL),              # misaligned second value
+    (dict(flags=C2, u2=U2, o=U2 + 64), EINVAL),       # o overlaps the second value
+    (dict(flags=C2 | LOG, u2=U2, o=None), EINVAL),
+])
+def test_extended_validation(lib, kw, expect):
+    st, msg = call_ex(lib, **kw)
+    assert st == expect, (st, msg)
+    assert msg
+
+
+def test_extended_varlen_validation(lib):
+    cu = np.asarray([0, 100, 300], dtype=np.int32)
+    ws_bytes = lib.wkv_prefill_varlen_workspace_bytes(cu.ctypes.data, 2, 4, 64, BF16)
+    st = lib.wkv_prefill_varlen_ex(R, K, V, W, U, None, A * 20, cu.ctypes.data, 2, S_IN, O, S_OUT,
+                                   4, 64, BF16, 16, WS, ws_bytes, None)
+    assert st == EUNSUP
+    st = lib.wkv_prefill_varlen_ex(R, K, V, W, U, U2, A * 20, cu.ctypes.data, 2, S_IN, O, S_OUT,
+                                   4, 64, BF16, LOG, WS, ws_bytes, None)
+    assert st == EINVAL and b"Finch-C2" in lib.wkv_last_error()
