@@ -2,6 +2,7 @@
 """Finch WKV pre-fill benchmark on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 1]
+                    [--decay w|log] [--variant finch|c2]
 
 One step = one complete pre-fill call (segment state pass, segment scan and
 the chunked scan: every step of the path) over the synthetic workload, inputs
@@ -11,6 +12,9 @@ not part of the figure.  The main chunked-scan kernel is also timed per launch
 with HIP events attached to its dispatch (through the library's timing hook),
 which gives the roofline figure.  The fp64 CPU oracle is timed on the
 host cores over a bounded sample of the same workload (cpu_baseline).
+``--decay log`` feeds the decay as d (w = exp(-exp(d))) and ``--variant c2``
+runs the Finch-C2 mixer (with its second-value stream); each such form is
+its own workload name ("<config>+logdecay", "<config>+c2", ...).
 
 Prints ONE JSON line.
 """
@@ -31,19 +35,28 @@ METRIC = "WKV pre-fill tokens/s at d_model 2048, T=4096; % of HBM/MFMA roofline"
 HBM_PEAK_GBS = 8000.0            # MI355X HBM3E, GB/s
 
 
-def algorithmic_bytes(cfg, tokens, n_seq, has_state_in):
-    """r, k, v, w in (bf16 or fp32) + o out (fp32) per token and head, plus the
-    fp32 state out (and in, when given) per (sequence, head)."""
+def algorithmic_bytes(cfg, tokens, n_seq, has_state_in, variant="finch"):
+    """r, k, v, w (and the Finch-C2 second value) in (bf16 or fp32) + o out
+    (fp32) per token and head, plus the fp32 state out (and in, when given)
+    per (sequence, head)."""
     elt = 2 if cfg.dtype == "bf16" else 4
-    per_token = cfg.H * cfg.D * (4 * elt + 4)
+    n_in = 5 if variant == "c2" else 4
+    per_token = cfg.H * cfg.D * (n_in * elt + 4)
     per_state = cfg.D * cfg.D * 4 * (2 if has_state_in else 1)
     return tokens * per_token + n_seq * cfg.H * per_state
 
 
 # HBM traffic of the main kernel, from rocprofv3 FETCH_SIZE / WRITE_SIZE passes
-# (scaled by a plain copy of known size); valid only for the kernel source the
-# counters were taken on
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "wkv_chunk_main_layer_1p5b_t4096_traffic.md")
+# (scaled by a plain copy of known size); valid only for the workload and the
+# kernel source the counters were taken on
+def traffic_file(workload_name):
+    return os.path.join(ROOT, "profiles", "wkv_chunk_main_%s_traffic.md" % workload_name.replace("+", "_"))
+
+
+def workload_name(cfg_name, decay, variant):
+    return cfg_name + ("+c2" if variant == "c2" else "") + ("+logdecay" if decay == "log" else "")
+
+
 KERNEL_SOURCES = ("linear_attention_rnn_finch_amd/csrc/wkv_chunk.hip",
                   "linear_attention_rnn_finch_amd/csrc/wkv_internal.h")
 
@@ -60,7 +73,7 @@ def measured_traffic(workload_name):
     """HBM bytes per launch of the main kernel recorded for this workload and
     this exact kernel source, else None."""
     try:
-        text = open(TRAFFIC_FILE).read()
+        text = open(traffic_file(workload_name)).read()
     except OSError:
         return None
     fields = {}
@@ -148,7 +161,8 @@ def cpu_baseline(wl, target_seconds):
     passes, t0, out = 0, time.perf_counter(), None
     while True:
         out = oracle.wkv_scan(wl.r, wl.k, wl.v, wl.w, wl.u, wl.state0, wl.cu_seqlens,
-                              threads=threads)
+                              threads=threads, decay=wl.decay, variant=wl.variant,
+                              second_value=wl.u2)
         passes += 1
         el = time.perf_counter() - t0
         if el >= target_seconds or passes >= 100000:
@@ -157,7 +171,8 @@ def cpu_baseline(wl, target_seconds):
     rec = {"value": tokens / el, "unit": "tokens/s", "cores": threads, "kind": "oracle",
            "sample": "%d full pass(es) of the %s workload (%d tokens x %d heads), fp64 "
                      "sequential recurrence, OpenMP over (sequence, head) slices, %.1f s"
-                     % (passes, wl.config.name, wl.tokens, wl.u.shape[0], el)}
+                     % (passes, workload_name(wl.config.name, wl.decay, wl.variant), wl.tokens,
+                        wl.u.shape[0], el)}
     return rec, out
 
 
@@ -174,6 +189,10 @@ def main():
                     help="time eager calls instead of a graph replay (for profiler runs)")
     ap.add_argument("--copy-mb", type=int, default=0,
                     help="first run a plain device copy of this many MiB (counter calibration)")
+    ap.add_argument("--decay", choices=("w", "log"), default="w",
+                    help="decay input: w itself, or d with w = exp(-exp(d))")
+    ap.add_argument("--variant", choices=("finch", "c2"), default="finch",
+                    help="base Finch (static bonus) or the Finch-C2 time mixer")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -188,7 +207,8 @@ def main():
     from synth import make_workload, get_config, max_block_error
 
     cfg = get_config(int(args.config) if args.config.isdigit() else args.config)
-    wl = make_workload(cfg)
+    wl = make_workload(cfg, decay=args.decay, variant=args.variant)
+    name = workload_name(cfg.name, args.decay, args.variant)
     dev = torch.device("cuda", 0)
 
     def cvt(a):
@@ -197,7 +217,9 @@ def main():
         return torch.from_numpy(a).to(dev)
 
     r, k, v, w = (cvt(getattr(wl, n)) for n in ("r", "k", "v", "w"))
-    u = torch.from_numpy(wl.u).to(dev)
+    u = None if args.variant == "c2" else torch.from_numpy(wl.u).to(dev)
+    u2 = None if wl.u2 is None else cvt(wl.u2)
+    form = dict(decay=args.decay, variant=args.variant, second_value=u2)
     s0 = None if wl.state0 is None else torch.from_numpy(wl.state0).to(dev)
     n_seq = wl.n_seq
     if wl.packed:
@@ -214,9 +236,9 @@ def main():
     def call():
         if wl.packed:
             fw.prefill_varlen(r, k, v, w, u, cu, s0, cu_seqlens_host=cu_host, o=o,
-                              state_out=st, workspace=ws)
+                              state_out=st, workspace=ws, **form)
         else:
-            fw.prefill(r, k, v, w, u, s0, o=o, state_out=st, workspace=ws)
+            fw.prefill(r, k, v, w, u, s0, o=o, state_out=st, workspace=ws, **form)
 
     if args.copy_mb > 0:                          # known-size copy for counter scaling
         src = torch.empty(args.copy_mb << 20, dtype=torch.uint8, device=dev)
@@ -265,7 +287,7 @@ def main():
     lib = _binding._lib
     lib.wkv_set_kernel_timing_events.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
     k_avg_ms, k_med_ms = time_main_kernel(call, args.kernel_samples, hip, lib, torch)
-    alg = algorithmic_bytes(cfg, wl.tokens, n_seq, s0 is not None)
+    alg = algorithmic_bytes(cfg, wl.tokens, n_seq, s0 is not None, args.variant)
     achieved = alg / (k_avg_ms * 1e-3) / 1e9
     step_gbs = alg / (ms_per_step * 1e-3) / 1e9
     copy_gbs = copy_bandwidth(torch)
@@ -283,13 +305,14 @@ def main():
         "vs_baseline": None,
         "dtype": cfg.dtype,
         "data": "synthetic",
-        "config": {"workload": cfg.name, "B": cfg.B, "T": cfg.T, "H": cfg.H, "D": cfg.D,
+        "config": {"workload": name, "B": cfg.B, "T": cfg.T, "H": cfg.H, "D": cfg.D,
+                   "decay": args.decay, "variant": args.variant,
                    "d_model": cfg.H * cfg.D, "tokens": wl.tokens,
                    "timing": ("eager calls" if args.no_graph else
                               "HIP graph of %d captured calls, one replay" % args.steps)},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": measured_traffic(cfg.name),
+                     "traffic": measured_traffic(name),
                      "kernel": "wkv_chunk_kernel<Main>",
                      "kernel_avg_us": round(k_avg_ms * 1e3, 2),
                      "kernel_median_us": round(k_med_ms * 1e3, 2),

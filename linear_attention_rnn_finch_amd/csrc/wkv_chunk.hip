@@ -327,11 +327,16 @@ __device__ __forceinline__ void a_tiles(SM &sm, const LdsBases &lb, const int (&
 }
 
 // 1 - w for the key factor of Finch-C2, from the decay input x (w itself, or
-// d with e = exp(d) already formed): exact for a bf16 w; for d it is
-// -expm1(-e), accurate also when w is close to 1.
+// d with e = exp(d) already formed).  Exact for a bf16 w.  For d it is
+// 1 - exp(-e): below e = 1/32 from its Taylor series (four terms, truncation
+// below 1e-8 relative), above from 1 - 2^{-e log2 e} (relative error a few
+// 1e-6, since 1 - w > 0.03 there).
 template <bool LOGD>
 __device__ __forceinline__ float one_minus_w(float x, float e) {
-    return LOGD ? -expm1f(-e) : 1.f - x;
+    if (!LOGD) return 1.f - x;
+    const float series = e * (1.f - 0.5f * e * (1.f - e * (1.f / 3.f) * (1.f - 0.25f * e)));
+    const float direct = 1.f - __builtin_amdgcn_exp2f(-e * kLog2e);
+    return e < 0.03125f ? series : direct;
 }
 
 template <Mode M, bool LOGD, bool C2>
