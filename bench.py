@@ -6,7 +6,10 @@
 
 One step = one complete pre-fill call (segment state pass, segment scan and
 the chunked scan: every step of the path) over the synthetic workload, inputs
-already resident in HBM.  The K timed steps are captured once into a HIP graph
+already resident in HBM.  Successive calls rotate over several independent
+copies of the inputs, outputs and states, together larger than 1 GiB (four
+times the GPU's 256 MB last-level cache), so that every call reads and writes
+HBM rather than what the previous call left in the cache.  The K timed steps are captured once into a HIP graph
 and replayed, bracketed by device synchronisations, so host launch overhead is
 not part of the figure.  The main chunked-scan kernel is also timed per launch
 with HIP events attached to its dispatch (through the library's timing hook),
@@ -32,6 +35,8 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "WKV pre-fill tokens/s at d_model 2048, T=4096; % of HBM/MFMA roofline"
+OTHER_METRIC = "WKV tokens/s (workload in config); % of HBM/MFMA roofline"
+STEP_MAX_T = 16                  # calls with no longer sequence run the recurrent-step kernel
 HBM_PEAK_GBS = 8000.0            # MI355X HBM3E, GB/s
 
 
@@ -49,8 +54,9 @@ def algorithmic_bytes(cfg, tokens, n_seq, has_state_in, variant="finch"):
 # HBM traffic of the main kernel, from rocprofv3 FETCH_SIZE / WRITE_SIZE passes
 # (scaled by a plain copy of known size); valid only for the workload and the
 # kernel source the counters were taken on
-def traffic_file(workload_name):
-    return os.path.join(ROOT, "profiles", "wkv_chunk_main_%s_traffic.md" % workload_name.replace("+", "_"))
+def traffic_file(workload_name, kernel_name):
+    stem = "wkv_decode" if kernel_name.startswith("wkv_decode") else "wkv_chunk_main"
+    return os.path.join(ROOT, "profiles", "%s_%s_traffic.md" % (stem, workload_name.replace("+", "_")))
 
 
 def workload_name(cfg_name, decay, variant):
@@ -58,10 +64,13 @@ def workload_name(cfg_name, decay, variant):
 
 
 KERNEL_SOURCES = ("linear_attention_rnn_finch_amd/csrc/wkv_chunk.hip",
+                  "linear_attention_rnn_finch_amd/csrc/wkv_decode.hip",
+                  "linear_attention_rnn_finch_amd/csrc/wkv_serial.hip",
                   "linear_attention_rnn_finch_amd/csrc/wkv_internal.h")
 
 
 def kernel_source_digest():
+    """SHA-256 over every kernel source (any kernel change voids the records)."""
     h = hashlib.sha256()
     for rel in KERNEL_SOURCES:
         with open(os.path.join(ROOT, rel), "rb") as f:
@@ -69,11 +78,11 @@ def kernel_source_digest():
     return h.hexdigest()
 
 
-def measured_traffic(workload_name):
+def measured_traffic(workload_name, kernel_name):
     """HBM bytes per launch of the main kernel recorded for this workload and
     this exact kernel source, else None."""
     try:
-        text = open(traffic_file(workload_name)).read()
+        text = open(traffic_file(workload_name, kernel_name)).read()
     except OSError:
         return None
     fields = {}
@@ -193,6 +202,8 @@ def main():
                     help="decay input: w itself, or d with w = exp(-exp(d))")
     ap.add_argument("--variant", choices=("finch", "c2"), default="finch",
                     help="base Finch (static bonus) or the Finch-C2 time mixer")
+    ap.add_argument("--rotate", type=int, default=0,
+                    help="buffer sets the calls cycle through (0: enough for 1 GiB, at most 16)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -216,29 +227,46 @@ def main():
             return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
         return torch.from_numpy(a).to(dev)
 
-    r, k, v, w = (cvt(getattr(wl, n)) for n in ("r", "k", "v", "w"))
+    host = {n: getattr(wl, n) for n in ("r", "k", "v", "w", "u2")}
     u = None if args.variant == "c2" else torch.from_numpy(wl.u).to(dev)
-    u2 = None if wl.u2 is None else cvt(wl.u2)
-    form = dict(decay=args.decay, variant=args.variant, second_value=u2)
-    s0 = None if wl.state0 is None else torch.from_numpy(wl.state0).to(dev)
     n_seq = wl.n_seq
+    in_dtype = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
     if wl.packed:
         cu = torch.from_numpy(wl.cu_seqlens.astype(np.int32)).to(dev)
         cu_host = torch.from_numpy(wl.cu_seqlens.astype(np.int32))
-        o = torch.empty((wl.tokens, cfg.H, cfg.D), dtype=torch.float32, device=dev)
-        ws_bytes = fw.varlen_workspace_bytes(cu_host, cfg.H, cfg.D, r.dtype)
+        o_shape = (wl.tokens, cfg.H, cfg.D)
+        ws_bytes = fw.varlen_workspace_bytes(cu_host, cfg.H, cfg.D, in_dtype)
     else:
-        o = torch.empty((cfg.B, cfg.T, cfg.H, cfg.D), dtype=torch.float32, device=dev)
-        ws_bytes = fw.workspace_bytes(cfg.B, cfg.T, cfg.H, cfg.D, r.dtype)
-    st = torch.empty((n_seq, cfg.H, cfg.D, cfg.D), dtype=torch.float32, device=dev)
-    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+        o_shape = (cfg.B, cfg.T, cfg.H, cfg.D)
+        ws_bytes = fw.workspace_bytes(cfg.B, cfg.T, cfg.H, cfg.D, in_dtype)
+    elt = 2 if cfg.dtype == "bf16" else 4
+    n_in = 5 if args.variant == "c2" else 4
+    set_bytes = (wl.tokens * cfg.H * cfg.D * (n_in * elt + 4) + ws_bytes +
+                 n_seq * cfg.H * cfg.D * cfg.D * 4 * (2 if wl.state0 is not None else 1))
+    n_sets = args.rotate if args.rotate > 0 else max(1, min(16, -(-(1 << 30) // set_bytes)))
+
+    def make_set():
+        t = {n: (None if a is None else cvt(a)) for n, a in host.items()}
+        t["s0"] = None if wl.state0 is None else torch.from_numpy(wl.state0).to(dev)
+        t["o"] = torch.empty(o_shape, dtype=torch.float32, device=dev)
+        t["st"] = torch.empty((n_seq, cfg.H, cfg.D, cfg.D), dtype=torch.float32, device=dev)
+        t["ws"] = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+        return t
+
+    sets = [make_set() for _ in range(n_sets)]
+    turn = [0]
 
     def call():
+        t = sets[turn[0] % n_sets]
+        turn[0] += 1
+        form = dict(decay=args.decay, variant=args.variant, second_value=t["u2"])
         if wl.packed:
-            fw.prefill_varlen(r, k, v, w, u, cu, s0, cu_seqlens_host=cu_host, o=o,
-                              state_out=st, workspace=ws, **form)
+            fw.prefill_varlen(t["r"], t["k"], t["v"], t["w"], u, cu, t["s0"], cu_seqlens_host=cu_host,
+                              o=t["o"], state_out=t["st"], workspace=t["ws"], **form)
         else:
-            fw.prefill(r, k, v, w, u, s0, o=o, state_out=st, workspace=ws, **form)
+            fw.prefill(t["r"], t["k"], t["v"], t["w"], u, t["s0"], o=t["o"], state_out=t["st"],
+                       workspace=t["ws"], **form)
+        return t
 
     if args.copy_mb > 0:                          # known-size copy for counter scaling
         src = torch.empty(args.copy_mb << 20, dtype=torch.uint8, device=dev)
@@ -279,6 +307,13 @@ def main():
         torch.cuda.synchronize()
         t1 = time.perf_counter()
     ms_per_step = (t1 - t0) * 1e3 / args.steps
+    max_len = int(np.diff(wl.cu_seqlens).max()) if wl.packed else cfg.T
+    if max_len <= STEP_MAX_T:
+        kernel_name = "wkv_decode_kernel"
+    elif cfg.dtype != "bf16":
+        kernel_name = "wkv_serial_kernel"
+    else:
+        kernel_name = "wkv_chunk_kernel<Main>"
     tokens_per_step = wl.tokens
     value = tokens_per_step / (ms_per_step * 1e-3)
 
@@ -287,13 +322,13 @@ def main():
     lib = _binding._lib
     lib.wkv_set_kernel_timing_events.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
     k_avg_ms, k_med_ms = time_main_kernel(call, args.kernel_samples, hip, lib, torch)
-    alg = algorithmic_bytes(cfg, wl.tokens, n_seq, s0 is not None, args.variant)
+    alg = algorithmic_bytes(cfg, wl.tokens, n_seq, wl.state0 is not None, args.variant)
     achieved = alg / (k_avg_ms * 1e-3) / 1e9
     step_gbs = alg / (ms_per_step * 1e-3) / 1e9
     copy_gbs = copy_bandwidth(torch)
 
     rec = {
-        "metric": METRIC,
+        "metric": METRIC if cfg.name == "layer_1p5b_t4096" else OTHER_METRIC,
         "value": round(value, 1),
         "unit": "tokens/s",
         "n_gpus": 1,
@@ -309,11 +344,12 @@ def main():
                    "decay": args.decay, "variant": args.variant,
                    "d_model": cfg.H * cfg.D, "tokens": wl.tokens,
                    "timing": ("eager calls" if args.no_graph else
-                              "HIP graph of %d captured calls, one replay" % args.steps)},
+                              "HIP graph of %d captured calls, one replay" % args.steps),
+                   "buffer_sets": n_sets},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": measured_traffic(name),
-                     "kernel": "wkv_chunk_kernel<Main>",
+                     "traffic": measured_traffic(name, kernel_name),
+                     "kernel": kernel_name,
                      "kernel_avg_us": round(k_avg_ms * 1e3, 2),
                      "kernel_median_us": round(k_med_ms * 1e3, 2),
                      "algorithmic_bytes_per_launch": alg,
@@ -326,11 +362,11 @@ def main():
     if not args.no_cpu_baseline:
         cpu_rec, (o_ref, s_ref) = cpu_baseline(wl, args.cpu_seconds)
         rec["cpu_baseline"] = cpu_rec
-        call()
+        t = call()
         torch.cuda.synchronize()
         rec["parity"] = {
-            "max_block_err_o": float(max_block_error(o.cpu().numpy(), o_ref, wl.cu_seqlens)),
-            "max_block_err_state": float(max_block_error(st.cpu().numpy(), s_ref, kind="state")),
+            "max_block_err_o": float(max_block_error(t["o"].cpu().numpy(), o_ref, wl.cu_seqlens)),
+            "max_block_err_state": float(max_block_error(t["st"].cpu().numpy(), s_ref, kind="state")),
             "tol": cfg.tolerance}
     print(json.dumps(rec), flush=True)
 

@@ -15,7 +15,10 @@
  *   token and leaves a fixed-size state that later tokens continue from
  *   (abstract; section 3.4 "Training and Inference Procedures", inference
  *   pre-fill).  Carrying state_out into the next call as state_in continues
- *   the same sequence exactly.
+ *   the same sequence exactly.  Calls in which no sequence has more than 16
+ *   tokens -- recurrent generation steps continuing a pre-filled state --
+ *   compute the same result with a kernel built to stream the states, which
+ *   are then most of the traffic.
  *
  * Layouts (all row-major, D fastest, no padding):
  *   r, k, v, w : [B, T, H, D] (fixed length) or [total_tokens, H, D] (packed)
@@ -198,7 +201,8 @@ wkv_status_t wkv_prefill_varlen_ex(const void *r, const void *k, const void *v,
  * event_before/event_after (hipEvent_t, cast to void *) are non-NULL, every
  * later pre-fill call made from the calling thread attaches them to the launch
  * of its main scan kernel (the chunked kernel for bf16, the token-serial one
- * for fp32): event_before takes that kernel's start timestamp and event_after
+ * for fp32, the recurrent-step kernel when no sequence of the call has more
+ * than 16 tokens): event_before takes that kernel's start timestamp and event_after
  * its end timestamp, so hipEventElapsedTime gives the kernel's own duration,
  * free of queue and launch gaps.  Pass NULL, NULL to stop.  The events are
  * owned by the caller, must be created with timing enabled and must outlive the

@@ -61,6 +61,7 @@ int64_t choose_segment(int64_t work, int64_t max_len, bool bf16) {
 
 struct Plan {
     Geometry g{};
+    int64_t max_len = 0;             // longest sequence of the call
     bool bf16 = false;
     bool split = false;              // some sequence has more than one segment
     size_t off_seg_state = 0, off_seg_start = 0, off_seg_off = 0, off_seg_seq = 0;
@@ -111,6 +112,7 @@ wkv_status_t plan_fixed(int B, int T, int H, int D, wkv_dtype_t dt, Plan &p) {
     p.g.total_tokens = tokens;
     p.g.uniform_T = T;
     p.g.segs_per_seq = (int)per;
+    p.max_len = T;
     p.split = per > 1;
     layout_workspace(p, false);
     return WKV_OK;
@@ -146,6 +148,7 @@ wkv_status_t plan_varlen(const int32_t *cu_host, int N, int H, int D, wkv_dtype_
     p.g.total_tokens = tokens;
     p.g.uniform_T = -1;
     p.g.segs_per_seq = 0;
+    p.max_len = max_len;
     p.split = split;
     layout_workspace(p, true);
     return WKV_OK;
@@ -237,6 +240,10 @@ wkv_status_t run(const Plan &p, const Tensors &t, const Variant &var, void *ws, 
         g.seg_seq = seg_seq;
     }
     const KernelTiming tm{g_ev_before, g_ev_after};
+    if (p.max_len <= kDecodeMaxT && !p.split) {       // recurrent steps: state-streaming kernel
+        if ((e = launch_decode(g, t, p.bf16, var, st, tm)) != hipSuccess) return fail_hip(e, "step launch");
+        return WKV_OK;
+    }
     if (!p.bf16) {
         if ((e = launch_serial(g, t, false, var, st, tm)) != hipSuccess) return fail_hip(e, "scan launch");
         return WKV_OK;

@@ -9,6 +9,7 @@ namespace finch {
 
 constexpr int kHeadDim = 64;     // D: the only head size the kernels are built for
 constexpr int kChunk = 64;       // tokens per chunk of the chunked scan
+constexpr int kDecodeMaxT = 16;  // calls whose sequences all have at most this many tokens take the step kernel
 
 // Geometry of one launch.  A "segment" is a run of at most seg_len tokens of
 // one sequence; a work item is one (segment, head) pair and is processed by
@@ -111,6 +112,10 @@ struct KernelTiming {
 };
 
 hipError_t launch_serial(const Geometry &g, const Tensors &t, bool bf16, Variant v, hipStream_t st,
+                         KernelTiming tm = {});
+// short sequences (at most kDecodeMaxT tokens each, never split): one wave per
+// (sequence, head), fp32 state in registers
+hipError_t launch_decode(const Geometry &g, const Tensors &t, bool bf16, Variant v, hipStream_t st,
                          KernelTiming tm = {});
 // bf16 path: state pass + segment scan (only when some sequence is split), then
 // the main chunked scan.

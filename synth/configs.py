@@ -1,8 +1,11 @@
-"""The five workloads of the Finch WKV pre-fill, with their input recipes.
+"""The workloads of the Finch WKV pre-fill, with their input recipes.
 
 Shapes follow the pages' model sizes: the 1.5B-class layer (24 layers,
 d_model 2048) of the GoldFinch experiments and the 32-layer, d_model 4096,
-256k-context point of the cache-size table; the head size is 64.  The pages
+256k-context point of the cache-size table; the head size is 64.  The last
+two are recurrent generation steps of the 1.5B-class layer: a batch of 128
+sequences continuing from pre-filled states (random fp32 here), one and
+sixteen tokens per call.  The pages
 give no head size and no input distributions: those below are the stated
 workload recipes, drawn from fixed seeds.
 
@@ -57,6 +60,12 @@ CONFIGS = (
                    rkv_sigma=1.0 / 8.0, x_range=(-8.0, -0.5), u_sigma=0.5,
                    state_sigma=0.1, ragged_lengths=(1024, 32768),
                    seed=_BASE_SEED + 4),
+    WorkloadConfig(5, "step_b128_t1", B=128, T=1, H=32, D=64, dtype="bf16",
+                   rkv_sigma=1.0 / 8.0, x_range=(-8.0, -0.5), u_sigma=0.5,
+                   state_sigma=0.1, seed=_BASE_SEED + 5),
+    WorkloadConfig(6, "step_b128_t16", B=128, T=16, H=32, D=64, dtype="bf16",
+                   rkv_sigma=1.0 / 8.0, x_range=(-8.0, -0.5), u_sigma=0.5,
+                   state_sigma=0.1, seed=_BASE_SEED + 6),
 )
 
 
