@@ -55,6 +55,8 @@ def algorithmic_bytes(cfg, tokens, n_seq, has_state_in, variant="finch"):
 # (scaled by a plain copy of known size); valid only for the workload and the
 # kernel source the counters were taken on
 def traffic_file(workload_name, kernel_name):
+    if workload_name.startswith(("layernorm_heads", "gold_compress")):
+        return os.path.join(ROOT, "profiles", "%s_traffic.md" % workload_name)
     stem = "wkv_decode" if kernel_name.startswith("wkv_decode") else "wkv_chunk_main"
     return os.path.join(ROOT, "profiles", "%s_%s_traffic.md" % (stem, workload_name.replace("+", "_")))
 
@@ -63,16 +65,23 @@ def workload_name(cfg_name, decay, variant):
     return cfg_name + ("+c2" if variant == "c2" else "") + ("+logdecay" if decay == "log" else "")
 
 
-KERNEL_SOURCES = ("linear_attention_rnn_finch_amd/csrc/wkv_chunk.hip",
-                  "linear_attention_rnn_finch_amd/csrc/wkv_decode.hip",
-                  "linear_attention_rnn_finch_amd/csrc/wkv_serial.hip",
-                  "linear_attention_rnn_finch_amd/csrc/wkv_internal.h")
+# kernel sources behind each family of traffic records
+KERNEL_SOURCES = {
+    "scan": ("linear_attention_rnn_finch_amd/csrc/wkv_chunk.hip",
+             "linear_attention_rnn_finch_amd/csrc/wkv_decode.hip",
+             "linear_attention_rnn_finch_amd/csrc/wkv_serial.hip"),
+    "epilogue": ("linear_attention_rnn_finch_amd/csrc/wkv_epilogue.hip",),
+}
 
 
-def kernel_source_digest():
-    """SHA-256 over every kernel source (any kernel change voids the records)."""
+def kernel_family(workload_name):
+    return "epilogue" if workload_name.startswith(("layernorm_heads", "gold_compress")) else "scan"
+
+
+def kernel_source_digest(family):
+    """SHA-256 over the family's kernel sources (any change voids its records)."""
     h = hashlib.sha256()
-    for rel in KERNEL_SOURCES:
+    for rel in KERNEL_SOURCES[family]:
         with open(os.path.join(ROOT, rel), "rb") as f:
             h.update(f.read())
     return h.hexdigest()
@@ -92,7 +101,7 @@ def measured_traffic(workload_name, kernel_name):
             fields[key.strip()] = val.strip().strip("`")
     if fields.get("workload") != workload_name:
         return None
-    if fields.get("kernel_source_sha256") != kernel_source_digest():
+    if fields.get("kernel_source_sha256") != kernel_source_digest(kernel_family(workload_name)):
         return None
     try:
         return int(fields["traffic_bytes_per_launch"])
@@ -204,12 +213,17 @@ def main():
                     help="base Finch (static bonus) or the Finch-C2 time mixer")
     ap.add_argument("--rotate", type=int, default=0,
                     help="buffer sets the calls cycle through (0: enough for 1 GiB, at most 16)")
+    ap.add_argument("--op", choices=("wkv", "layernorm", "compress"), default="wkv",
+                    help="the pre-fill scan (default), or one epilogue step on the 1.5B layer "
+                         "shape: LayerNorm over heads, GOLD key compression")
     args = ap.parse_args()
 
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(--gpus %d requested)" % args.gpus, file=sys.stderr)
         sys.exit(2)
+    if args.op != "wkv":
+        return bench_epilogue(args)
 
     import numpy as np
     import torch
@@ -368,6 +382,165 @@ def main():
             "max_block_err_o": float(max_block_error(t["o"].cpu().numpy(), o_ref, wl.cu_seqlens)),
             "max_block_err_state": float(max_block_error(t["st"].cpu().numpy(), s_ref, kind="state")),
             "tol": cfg.tolerance}
+    print(json.dumps(rec), flush=True)
+
+
+def bench_epilogue(args):
+    """One epilogue step on the 1.5B-class layer shape (4096 tokens, d_model
+    2048): the LayerNorm over heads (fp32 in, bf16 out) or the GOLD key
+    compression (bf16 in, fp32 out).  Same timing rules as the scan."""
+    import numpy as np
+    import torch
+    import linear_attention_rnn_finch_amd as fw
+    from linear_attention_rnn_finch_amd import _binding
+    from synth import make_norm_inputs, make_compress_inputs, bf16_bits_to_f32
+
+    tokens, width = 4096, 2048
+    dev = torch.device("cuda", 0)
+
+    def cvt(a):
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(a).to(dev)
+
+    if args.op == "layernorm":
+        x, gamma, beta = make_norm_inputs(tokens, width)
+        name, kernel = "layernorm_heads_t4096_w2048", "layernorm_rows_kernel<bf16 out>"
+        alg = tokens * width * (4 + 2) + 2 * width * 4
+        set_bytes = tokens * width * 6
+        dtype = "f32 in, bf16 out"
+        g_d, b_d = cvt(gamma), cvt(beta)
+
+        def make_set():
+            return {"x": cvt(x), "y": torch.empty((tokens, width), dtype=torch.bfloat16, device=dev)}
+
+        def run(t):
+            fw.layernorm_heads(t["x"], g_d, b_d, 1e-5, out_dtype=torch.bfloat16, y=t["y"])
+
+        def reference():
+            from oracle import epilogue
+            return epilogue.layernorm_heads(x, gamma, beta, 1e-5)
+
+        def result(t):
+            return bf16_bits_to_f32(t["y"].view(torch.int16).cpu().numpy().view(np.uint16))
+    else:
+        x, w = make_compress_inputs(tokens, width)
+        name, kernel = "gold_compress_t4096_d2048", "gold_compress_kernel<f32 out>"
+        n_out = width // 16
+        alg = tokens * width * 2 + n_out * width * 2 + tokens * n_out * 4
+        set_bytes = tokens * width * 2 + tokens * n_out * 4
+        dtype = "bf16 in, fp32 accumulate and out"
+        w_d = cvt(w)
+
+        def make_set():
+            return {"x": cvt(x), "c": torch.empty((tokens, n_out), dtype=torch.float32, device=dev)}
+
+        def run(t):
+            fw.gold_compress(t["x"], w_d, out_dtype=torch.float32, c=t["c"])
+
+        def reference():
+            from oracle import epilogue
+            return epilogue.gold_compress(x, w)
+
+        def result(t):
+            return t["c"].cpu().numpy()
+
+    n_sets = args.rotate if args.rotate > 0 else max(1, min(16, -(-(1 << 30) // set_bytes)))
+    sets = [make_set() for _ in range(n_sets)]
+    turn = [0]
+
+    def call():
+        t = sets[turn[0] % n_sets]
+        turn[0] += 1
+        run(t)
+        return t
+
+    if args.copy_mb > 0:                          # known-size copy for counter scaling
+        src = torch.empty(args.copy_mb << 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+    for _ in range(args.warmup):
+        call()
+    torch.cuda.synchronize()
+    if args.no_graph:
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            call()
+        torch.cuda.synchronize()
+    else:
+        graph = torch.cuda.CUDAGraph()
+        cap = torch.cuda.Stream()
+        cap.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(cap):
+            call()
+            torch.cuda.synchronize()
+            with torch.cuda.graph(graph, stream=cap):
+                for _ in range(args.steps):
+                    call()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        graph.replay()
+        torch.cuda.synchronize()
+    ms_per_step = (time.perf_counter() - t0) * 1e3 / args.steps
+    hip = hip_runtime()
+    lib = _binding._lib
+    lib.wkv_set_kernel_timing_events.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+    k_avg_ms, k_med_ms = time_main_kernel(call, args.kernel_samples, hip, lib, torch)
+    achieved = alg / (k_avg_ms * 1e-3) / 1e9
+    copy_gbs = copy_bandwidth(torch)
+    rec = {
+        "metric": OTHER_METRIC,
+        "value": round(tokens / (ms_per_step * 1e-3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": dtype, "data": "synthetic",
+        "config": {"workload": name, "tokens": tokens, "d_model": width, "buffer_sets": n_sets,
+                   "timing": ("eager calls" if args.no_graph else
+                              "HIP graph of %d captured calls, one replay" % args.steps)},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": measured_traffic(name, kernel),
+                     "kernel": kernel, "kernel_avg_us": round(k_avg_ms * 1e3, 2),
+                     "kernel_median_us": round(k_med_ms * 1e3, 2),
+                     "algorithmic_bytes_per_launch": alg,
+                     "measured_copy_GBps": round(copy_gbs, 1),
+                     "kernel_frac_of_copy": round(achieved / copy_gbs, 4)},
+    }
+    if args.op == "compress":
+        flops = 2 * tokens * width * (width // 16)
+        rec["roofline"]["flops_per_launch"] = flops
+        rec["roofline"]["mfma_frac_bf16"] = round(flops / (k_avg_ms * 1e-3) / 2.5e15, 4)
+    if not args.no_cpu_baseline:
+        passes, t0, ref = 0, time.perf_counter(), None
+        while True:
+            ref = reference()
+            passes += 1
+            el = time.perf_counter() - t0
+            if el >= args.cpu_seconds:
+                break
+        cores = 1
+        if args.op == "compress":                 # the fp64 product runs on the BLAS thread pool
+            try:
+                from threadpoolctl import threadpool_info
+                cores = max([p["num_threads"] for p in threadpool_info() if p.get("user_api") == "blas"] or [1])
+            except ImportError:
+                cores = len(os.sched_getaffinity(0))
+        rec["cpu_baseline"] = {"value": tokens * passes / el, "unit": "tokens/s", "cores": cores,
+                               "kind": "oracle",
+                               "sample": "%d full pass(es) of %s (%d tokens), fp64 numpy, %.1f s"
+                                         % (passes, name, tokens, el)}
+        t = call()
+        torch.cuda.synchronize()
+        got = result(t).astype(np.float64)
+        rec["parity"] = {"max_row_err": float((np.abs(got - ref).max(-1) /
+                                               np.abs(ref).max(-1)).max())}
     print(json.dumps(rec), flush=True)
 
 

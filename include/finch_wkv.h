@@ -197,12 +197,47 @@ wkv_status_t wkv_prefill_varlen_ex(const void *r, const void *k, const void *v,
                                    void *stream);
 
 /*
+ * LayerNorm over the concatenated heads of each token: the normalisation of
+ * the Finch-C2 output equation (section 3.4, output equation, applied to
+ * r_t wkv_t + u'_t of all heads before W_O).  Per row of `width` values:
+ *   y = (x - mean) / sqrt(var + eps) * gamma + beta
+ * with the population mean and variance of the row.
+ *   x          device, [tokens, width] fp32 (e.g. o of a pre-fill call seen as
+ *              [tokens, H * D])
+ *   gamma,beta device, [width] fp32
+ *   y          device, [tokens, width] of out_dtype (WKV_BF16: round to
+ *              nearest even; WKV_F32)
+ *   width      multiple of 1024, at most 8192; eps finite, >= 0
+ * 16-byte aligned pointers; y must not overlap an input.  Asynchronous on
+ * `stream`; validation errors as for wkv_prefill.
+ */
+wkv_status_t wkv_layernorm_heads(const float *x, const float *gamma, const float *beta, float eps,
+                                 void *y, wkv_dtype_t out_dtype, int64_t tokens, int width,
+                                 void *stream);
+
+/*
+ * GOLD key compression c_t = x_t W_KD, d_model -> d_model / 16 (section "GOLD
+ * Key Compression and TokenCat Decompression", compression step; x_t is the
+ * output of the last Finch-C2 layer).
+ *   x      device, [tokens, d_model] bf16
+ *   w_kd   device, [d_model / 16, d_model] bf16: W_KD TRANSPOSED (the
+ *          output-major layout of a linear layer's weight)
+ *   c      device, [tokens, d_model / 16] of out_dtype (fp32, or bf16
+ *          rounded to nearest even); fp32 accumulation
+ *   d_model multiple of 1024, at most 65536; tokens <= 2^31 - 1
+ * 16-byte aligned pointers; c must not overlap an input.
+ */
+wkv_status_t wkv_gold_compress(const void *x, const void *w_kd, void *c, wkv_dtype_t out_dtype,
+                               int64_t tokens, int d_model, void *stream);
+
+/*
  * Kernel timing hook for profiling tools (the benchmark uses it).  When
  * event_before/event_after (hipEvent_t, cast to void *) are non-NULL, every
  * later pre-fill call made from the calling thread attaches them to the launch
  * of its main scan kernel (the chunked kernel for bf16, the token-serial one
  * for fp32, the recurrent-step kernel when no sequence of the call has more
- * than 16 tokens): event_before takes that kernel's start timestamp and event_after
+ * than 16 tokens; the one kernel of wkv_layernorm_heads and of
+ * wkv_gold_compress): event_before takes that kernel's start timestamp and event_after
  * its end timestamp, so hipEventElapsedTime gives the kernel's own duration,
  * free of queue and launch gaps.  Pass NULL, NULL to stop.  The events are
  * owned by the caller, must be created with timing enabled and must outlive the

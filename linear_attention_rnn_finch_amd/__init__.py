@@ -6,5 +6,5 @@ behind a C ABI (include/finch_wkv.h, libfinch_wkv.so).  This package is the
 thin Python binding over that library.
 """
 from ._binding import (  # noqa: F401
-    HEAD_DIM, LIBRARY_PATH, WkvError, abi_version, prefill, prefill_varlen,
-    varlen_workspace_bytes, workspace_bytes)
+    HEAD_DIM, LIBRARY_PATH, WkvError, abi_version, gold_compress, layernorm_heads, prefill,
+    prefill_varlen, varlen_workspace_bytes, workspace_bytes)

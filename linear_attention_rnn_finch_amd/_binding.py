@@ -50,6 +50,10 @@ _lib.wkv_prefill_varlen.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i,
 _lib.wkv_prefill_ex.restype = _i
 _lib.wkv_prefill_ex.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                 _i, _i, _i, _i, _i, ctypes.c_uint, _vp, _sz, _vp]
+_lib.wkv_layernorm_heads.restype = _i
+_lib.wkv_layernorm_heads.argtypes = [_vp, _vp, _vp, ctypes.c_float, _vp, _i, ctypes.c_int64, _i, _vp]
+_lib.wkv_gold_compress.restype = _i
+_lib.wkv_gold_compress.argtypes = [_vp, _vp, _vp, _i, ctypes.c_int64, _i, _vp]
 _lib.wkv_prefill_varlen_ex.restype = _i
 _lib.wkv_prefill_varlen_ex.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i,
                                        _vp, _vp, _vp, _i, _i, _i, ctypes.c_uint, _vp, _sz, _vp]
@@ -240,3 +244,64 @@ def prefill_varlen(r, k, v, w, u, cu_seqlens, state_in=None, *, cu_seqlens_host=
                                             ws_bytes, _stream_handle(stream))
     _check(status)
     return o, state_out
+
+
+def _out_code(dtype):
+    if dtype == torch.bfloat16:
+        return WKV_BF16
+    if dtype == torch.float32:
+        return WKV_F32
+    raise TypeError("output dtype must be bfloat16 or float32, got %s" % dtype)
+
+
+def layernorm_heads(x, gamma, beta, eps=1e-5, *, out_dtype=torch.bfloat16, y=None, stream=None):
+    """LayerNorm over the concatenated heads of each token (Finch-C2 output).
+
+    x: [..., W] float32 (e.g. the pre-fill output o viewed as [tokens, H*64]),
+    W a multiple of 1024 up to 8192; gamma, beta: [W] float32.  Returns y with
+    x's shape in ``out_dtype`` (bfloat16 or float32)."""
+    _device_tensor("x", x, torch.float32)
+    W = x.shape[-1]
+    for name, t in (("gamma", gamma), ("beta", beta)):
+        _device_tensor(name, t, torch.float32)
+        if tuple(t.shape) != (W,):
+            raise ValueError("%s must be [%d]" % (name, W))
+    code = _out_code(out_dtype)
+    if y is None:
+        y = torch.empty(x.shape, dtype=out_dtype, device=x.device)
+    else:
+        _device_tensor("y", y, out_dtype)
+        if y.shape != x.shape:
+            raise ValueError("y must have x's shape")
+    tokens = x.numel() // W if W else 0
+    with torch.cuda.device(x.device):
+        status = _lib.wkv_layernorm_heads(_ptr(x), _ptr(gamma), _ptr(beta), float(eps), _ptr(y), code,
+                                          tokens, W, _stream_handle(stream))
+    _check(status)
+    return y
+
+
+def gold_compress(x, w_kd, *, out_dtype=torch.float32, c=None, stream=None):
+    """GOLD key compression c = x W_KD (d_model -> d_model/16).
+
+    x: [tokens, d_model] bfloat16; w_kd: [d_model/16, d_model] bfloat16, i.e.
+    W_KD transposed (a linear layer's weight layout).  Returns c
+    [tokens, d_model/16] in ``out_dtype`` (float32 or bfloat16)."""
+    _device_tensor("x", x, torch.bfloat16)
+    _device_tensor("w_kd", w_kd, torch.bfloat16)
+    if x.dim() != 2:
+        raise ValueError("x must be [tokens, d_model]")
+    tokens, D = x.shape
+    if tuple(w_kd.shape) != (D // 16, D):
+        raise ValueError("w_kd must be [d_model/16, d_model] = %s" % ((D // 16, D),))
+    code = _out_code(out_dtype)
+    if c is None:
+        c = torch.empty((tokens, D // 16), dtype=out_dtype, device=x.device)
+    else:
+        _device_tensor("c", c, out_dtype)
+        if tuple(c.shape) != (tokens, D // 16):
+            raise ValueError("c must be [tokens, d_model/16]")
+    with torch.cuda.device(x.device):
+        status = _lib.wkv_gold_compress(_ptr(x), _ptr(w_kd), _ptr(c), code, tokens, D, _stream_handle(stream))
+    _check(status)
+    return c

@@ -372,6 +372,65 @@ wkv_status_t wkv_prefill_varlen(const void *r, const void *k, const void *v, con
                           D, dt, 0u, ws, ws_bytes, stream);
 }
 
+wkv_status_t wkv_layernorm_heads(const float *x, const float *gamma, const float *beta, float eps,
+                                 void *y, wkv_dtype_t out_dtype, int64_t tokens, int width,
+                                 void *stream) {
+    g_last_error.clear();
+    if (out_dtype != WKV_F32 && out_dtype != WKV_BF16)
+        return fail(WKV_EUNSUPPORTED, "unknown out_dtype %d", (int)out_dtype);
+    if (width < 1024 || width > kMaxNormWidth || width % 1024 != 0)
+        return fail(WKV_EUNSUPPORTED, "width=%d must be a multiple of 1024 in [1024, %d]", width, kMaxNormWidth);
+    if (tokens < 0) return fail(WKV_EINVAL, "tokens=%lld must be >= 0", (long long)tokens);
+    if (!(eps >= 0.f) || eps > 1e30f) return fail(WKV_EINVAL, "eps must be finite and >= 0");
+    if (tokens == 0) return WKV_OK;
+    const void *need[] = {x, gamma, beta, y};
+    const char *names[] = {"x", "gamma", "beta", "y"};
+    for (int i = 0; i < 4; ++i) {
+        if (!need[i]) return fail(WKV_EINVAL, "%s is NULL", names[i]);
+        if (misaligned(need[i], 16)) return fail(WKV_EINVAL, "%s is not 16-byte aligned", names[i]);
+    }
+    const size_t n = (size_t)tokens * width;
+    const Range out = range_of("y", y, n * (out_dtype == WKV_BF16 ? 2 : 4));
+    const Range ins[] = {range_of("x", x, n * 4), range_of("gamma", gamma, (size_t)width * 4),
+                         range_of("beta", beta, (size_t)width * 4)};
+    for (const Range &in : ins)
+        if (overlaps(out, in)) return fail(WKV_EINVAL, "output y overlaps %s", in.name);
+    const KernelTiming tm{g_ev_before, g_ev_after};
+    if (hipError_t e = launch_layernorm_rows(x, gamma, beta, eps, y, out_dtype == WKV_BF16, tokens, width,
+                                             static_cast<hipStream_t>(stream), tm))
+        return fail_hip(e, "layernorm launch");
+    return WKV_OK;
+}
+
+wkv_status_t wkv_gold_compress(const void *x, const void *w_kd, void *c, wkv_dtype_t out_dtype,
+                               int64_t tokens, int d_model, void *stream) {
+    g_last_error.clear();
+    if (out_dtype != WKV_F32 && out_dtype != WKV_BF16)
+        return fail(WKV_EUNSUPPORTED, "unknown out_dtype %d", (int)out_dtype);
+    if (d_model < 1024 || d_model > 65536 || d_model % 1024 != 0)
+        return fail(WKV_EUNSUPPORTED, "d_model=%d must be a multiple of 1024 in [1024, 65536]", d_model);
+    if (tokens < 0 || tokens > INT32_MAX) return fail(WKV_EINVAL, "tokens=%lld out of range", (long long)tokens);
+    if (tokens == 0) return WKV_OK;
+    const void *need[] = {x, w_kd, c};
+    const char *names[] = {"x", "w_kd", "c"};
+    for (int i = 0; i < 3; ++i) {
+        if (!need[i]) return fail(WKV_EINVAL, "%s is NULL", names[i]);
+        if (misaligned(need[i], 16)) return fail(WKV_EINVAL, "%s is not 16-byte aligned", names[i]);
+    }
+    const int n_out = d_model / 16;
+    const Range out = range_of("c", c, (size_t)tokens * n_out * (out_dtype == WKV_BF16 ? 2 : 4));
+    const Range ins[] = {range_of("x", x, (size_t)tokens * d_model * 2),
+                         range_of("w_kd", w_kd, (size_t)n_out * d_model * 2)};
+    for (const Range &in : ins)
+        if (overlaps(out, in)) return fail(WKV_EINVAL, "output c overlaps %s", in.name);
+    const KernelTiming tm{g_ev_before, g_ev_after};
+    if (hipError_t e = launch_gold_compress(static_cast<const uint16_t *>(x), static_cast<const uint16_t *>(w_kd),
+                                            c, out_dtype == WKV_BF16, tokens, d_model, n_out,
+                                            static_cast<hipStream_t>(stream), tm))
+        return fail_hip(e, "compression launch");
+    return WKV_OK;
+}
+
 wkv_status_t wkv_prefill_varlen_ex(const void *r, const void *k, const void *v, const void *w,
                                    const float *u, const void *u2, const int32_t *cu_dev,
                                    const int32_t *cu_host, int N, const float *state_in,

@@ -10,6 +10,7 @@ namespace finch {
 constexpr int kHeadDim = 64;     // D: the only head size the kernels are built for
 constexpr int kChunk = 64;       // tokens per chunk of the chunked scan
 constexpr int kDecodeMaxT = 16;  // calls whose sequences all have at most this many tokens take the step kernel
+constexpr int kMaxNormWidth = 8192;   // widest row of the LayerNorm over heads (d_model)
 
 // Geometry of one launch.  A "segment" is a run of at most seg_len tokens of
 // one sequence; a work item is one (segment, head) pair and is processed by
@@ -123,6 +124,11 @@ hipError_t launch_segment_states(const Geometry &g, const Tensors &t, const Work
                                  Variant v, hipStream_t st);
 hipError_t launch_chunked_main(const Geometry &g, const Tensors &t, const Workspace &ws,
                                Variant v, hipStream_t st, KernelTiming tm = {});
+// epilogue of Finch-C2 pre-fill: LayerNorm over heads, GOLD key compression
+hipError_t launch_layernorm_rows(const float *x, const float *gamma, const float *beta, float eps, void *y,
+                                 bool out_bf16, int64_t rows, int width, hipStream_t st, KernelTiming tm = {});
+hipError_t launch_gold_compress(const uint16_t *x, const uint16_t *w, void *c, bool out_bf16, int64_t M, int K,
+                                int N, hipStream_t st, KernelTiming tm = {});
 hipError_t launch_plan_varlen(const Geometry &g, int32_t *seg_off, int32_t *seg_seq,
                               hipStream_t st);
 

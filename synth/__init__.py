@@ -7,5 +7,6 @@ values.
 """
 from .configs import CONFIGS, WorkloadConfig, get_config  # noqa: F401
 from .gen import (Workload, make_workload, f32_to_bf16_bits,  # noqa: F401
-                  bf16_bits_to_f32, random_slice, select_heads)
+                  bf16_bits_to_f32, random_slice, select_heads, make_norm_inputs,
+                  make_compress_inputs)
 from .compare import block_errors, max_block_error  # noqa: F401

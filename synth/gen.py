@@ -203,3 +203,26 @@ def random_slice(seed: int, T: int, D: int, *, dtype="f32", rkv_sigma=1.0,
     if dtype == "bf16":
         r, k, v, w = (f32_to_bf16_bits(a) for a in (r, k, v, w))
     return r, k, v, w, u, s0
+
+
+def make_norm_inputs(tokens: int, width: int, seed: int = 7001):
+    """Rows for the LayerNorm over heads: each row has its own offset
+    mu ~ N(0, 0.5) and scale sigma ~ U(0.05, 1) (x = mu + sigma N(0, 1)), so
+    both the centring and the scaling matter; gamma = 1 + N(0, 0.1),
+    beta ~ N(0, 0.1).  All float32."""
+    g = _rng(seed, 1)
+    mu = g.normal(0.0, 0.5, size=(tokens, 1))
+    sd = g.uniform(0.05, 1.0, size=(tokens, 1))
+    x = (mu + sd * _rng(seed, 2).normal(size=(tokens, width))).astype(np.float32)
+    gamma = (1.0 + _rng(seed, 3).normal(0.0, 0.1, size=width)).astype(np.float32)
+    beta = _rng(seed, 4).normal(0.0, 0.1, size=width).astype(np.float32)
+    return x, gamma, beta
+
+
+def make_compress_inputs(tokens: int, d_model: int, seed: int = 7002):
+    """Hidden states x ~ N(0, 1) [tokens, d_model] and a compression weight
+    W_KD ~ N(0, 1/d_model) stored transposed [d_model/16, d_model], both as
+    bf16 bit patterns."""
+    x = _rng(seed, 1).normal(size=(tokens, d_model)).astype(np.float32)
+    w = _rng(seed, 2).normal(0.0, d_model ** -0.5, size=(d_model // 16, d_model)).astype(np.float32)
+    return f32_to_bf16_bits(x), f32_to_bf16_bits(w)

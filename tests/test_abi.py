@@ -39,6 +39,10 @@ def lib():
     L.wkv_prefill_workspace_bytes.argtypes = [i] * 5
     L.wkv_prefill_varlen_workspace_bytes.restype = sz
     L.wkv_prefill_varlen_workspace_bytes.argtypes = [vp, i, i, i, i]
+    L.wkv_layernorm_heads.restype = i
+    L.wkv_layernorm_heads.argtypes = [vp, vp, vp, ctypes.c_float, vp, i, ctypes.c_int64, i, vp]
+    L.wkv_gold_compress.restype = i
+    L.wkv_gold_compress.argtypes = [vp, vp, vp, i, ctypes.c_int64, i, vp]
     L.wkv_prefill_ex.restype = i
     L.wkv_prefill_ex.argtypes = [vp] * 9 + [i] * 5 + [ctypes.c_uint, vp, sz, vp]
     L.wkv_prefill_varlen_ex.restype = i
@@ -201,3 +205,38 @@ def test_extended_varlen_validation(lib):
     st = lib.wkv_prefill_varlen_ex(R, K, V, W, U, U2, A * 20, cu.ctypes.data, 2, S_IN, O, S_OUT,
                                    4, 64, BF16, LOG, WS, ws_bytes, None)
     assert st == EINVAL and b"Finch-C2" in lib.wkv_last_error()
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(width=2048 + 512), EUNSUP),
+    (dict(width=16384), EUNSUP),
+    (dict(out=7), EUNSUP),
+    (dict(tokens=-1), EINVAL),
+    (dict(eps=-1.0), EINVAL),
+    (dict(eps=float("nan")), EINVAL),
+    (dict(x=None), EINVAL),
+    (dict(y=R + 8), EINVAL),                         # misaligned
+    (dict(y=R + 4096), EINVAL),                      # y overlaps x
+])
+def test_layernorm_validation(lib, kw, expect):
+    a = dict(x=R, g=K, b=V, eps=1e-5, y=O, out=BF16, tokens=4096, width=2048)
+    a.update(kw)
+    st = lib.wkv_layernorm_heads(a["x"], a["g"], a["b"], a["eps"], a["y"], a["out"], a["tokens"],
+                                 a["width"], None)
+    assert st == expect, lib.wkv_last_error()
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(d=2048 + 64), EUNSUP),
+    (dict(d=512), EUNSUP),
+    (dict(out=3), EUNSUP),
+    (dict(tokens=-5), EINVAL),
+    (dict(w=None), EINVAL),
+    (dict(c=O + 2), EINVAL),
+    (dict(c=W + 64), EINVAL),                        # c overlaps the weight
+])
+def test_compress_validation(lib, kw, expect):
+    a = dict(x=R, w=W, c=O, out=F32, tokens=4096, d=2048)
+    a.update(kw)
+    st = lib.wkv_gold_compress(a["x"], a["w"], a["c"], a["out"], a["tokens"], a["d"], None)
+    assert st == expect, lib.wkv_last_error()
