@@ -6,8 +6,9 @@
 //   GroupNorm).  It cannot ride along with the scan's store: a scan workgroup
 //   owns one head of a segment, and a token's statistics need every head.  So
 //   it is its own bandwidth-bound pass: persistent workgroups, one token row at
-//   a time, the row held in registers between the two reductions (mean, then
-//   variance about the mean), the scale and shift loaded once per workgroup.
+//   a time (the next one already loading), the row held in registers between
+//   the two reductions (mean, then variance about the mean), the scale and
+//   shift loaded once per workgroup.
 //
 // - GOLD key compression c_t = x_t W_KD, D -> D/16 (same page, "GOLD Key
 //   Compression and TokenCat Decompression", compression step).  A small
@@ -31,7 +32,7 @@ typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kLnThreads = 256;
-constexpr int kLnMaxVec = kMaxNormWidth / (4 * kLnThreads);   // float4 per thread at the widest row
+static_assert(kMaxNormWidth == 8 * 4 * kLnThreads, "the LayerNorm kernels are built for up to 8 float4 per thread");
 
 __device__ inline float wave_sum(float x) {
     #pragma unroll
@@ -49,59 +50,74 @@ __device__ inline float block_sum(float x, float *red) {
     return red[0] + red[1] + red[2] + red[3];
 }
 
-template <bool OutBf16>
+// NV = float4 per thread in a row (width = 1024 * NV).  The next row's loads
+// are issued before the current row's reductions, so one row's memory latency
+// hides behind the previous row's arithmetic.
+template <int NV, bool OutBf16>
 __global__ __launch_bounds__(kLnThreads) void layernorm_rows_kernel(const float *x, const float *gamma,
                                                                    const float *beta, float eps, void *y,
                                                                    int64_t rows, int width) {
     __shared__ float red[4];
-    const int nv = width / (4 * kLnThreads);           // float4 per thread in a row
     const int tid = threadIdx.x;
-    f32x4 g[kLnMaxVec], b[kLnMaxVec];
+    f32x4 g[NV], b[NV], v[NV], vn[NV];
     #pragma unroll
-    for (int i = 0; i < kLnMaxVec; ++i) {
-        if (i < nv) {
-            g[i] = *reinterpret_cast<const f32x4 *>(gamma + 4 * (tid + kLnThreads * i));
-            b[i] = *reinterpret_cast<const f32x4 *>(beta + 4 * (tid + kLnThreads * i));
-        }
+    for (int i = 0; i < NV; ++i) {
+        g[i] = *reinterpret_cast<const f32x4 *>(gamma + 4 * (tid + kLnThreads * i));
+        b[i] = *reinterpret_cast<const f32x4 *>(beta + 4 * (tid + kLnThreads * i));
     }
     const float inv_w = 1.f / (float)width;
-    for (int64_t row = blockIdx.x; row < rows; row += gridDim.x) {
-        const float *xr = x + row * width;
-        f32x4 v[kLnMaxVec];
+    int64_t row = blockIdx.x;
+    if (row < rows) {
+        #pragma unroll
+        for (int i = 0; i < NV; ++i) v[i] = *reinterpret_cast<const f32x4 *>(x + row * width + 4 * (tid + kLnThreads * i));
+    }
+    for (; row < rows; row += gridDim.x) {
+        const int64_t next = row + gridDim.x;
+        if (next < rows) {
+            #pragma unroll
+            for (int i = 0; i < NV; ++i)
+                vn[i] = *reinterpret_cast<const f32x4 *>(x + next * width + 4 * (tid + kLnThreads * i));
+        }
         float s = 0.f;
         #pragma unroll
-        for (int i = 0; i < kLnMaxVec; ++i) {
-            if (i < nv) {
-                v[i] = *reinterpret_cast<const f32x4 *>(xr + 4 * (tid + kLnThreads * i));
-                s += (v[i][0] + v[i][1]) + (v[i][2] + v[i][3]);
-            }
-        }
+        for (int i = 0; i < NV; ++i) s += (v[i][0] + v[i][1]) + (v[i][2] + v[i][3]);
         const float mean = block_sum(s, red) * inv_w;
         float q = 0.f;
         #pragma unroll
-        for (int i = 0; i < kLnMaxVec; ++i) {
-            if (i < nv) {
-                #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    v[i][e] -= mean;
-                    q += v[i][e] * v[i][e];
-                }
+        for (int i = 0; i < NV; ++i)
+            #pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                v[i][e] -= mean;
+                q += v[i][e] * v[i][e];
             }
-        }
         const float rstd = 1.f / sqrtf(block_sum(q, red) * inv_w + eps);
         #pragma unroll
-        for (int i = 0; i < kLnMaxVec; ++i) {
-            if (i < nv) {
-                f32x4 o;
-                #pragma unroll
-                for (int e = 0; e < 4; ++e) o[e] = v[i][e] * rstd * g[i][e] + b[i][e];
-                const int64_t at = row * width + 4 * (tid + kLnThreads * i);
-                if (OutBf16)
-                    *reinterpret_cast<bf16x4 *>(static_cast<uint16_t *>(y) + at) = __builtin_convertvector(o, bf16x4);
-                else
-                    *reinterpret_cast<f32x4 *>(static_cast<float *>(y) + at) = o;
-            }
+        for (int i = 0; i < NV; ++i) {
+            f32x4 o;
+            #pragma unroll
+            for (int e = 0; e < 4; ++e) o[e] = v[i][e] * rstd * g[i][e] + b[i][e];
+            const int64_t at = row * width + 4 * (tid + kLnThreads * i);
+            if (OutBf16)
+                *reinterpret_cast<bf16x4 *>(static_cast<uint16_t *>(y) + at) = __builtin_convertvector(o, bf16x4);
+            else
+                *reinterpret_cast<f32x4 *>(static_cast<float *>(y) + at) = o;
         }
+        #pragma unroll
+        for (int i = 0; i < NV; ++i) v[i] = vn[i];
+    }
+}
+
+template <bool OutBf16>
+void (*layernorm_kernel_for(int nv))(const float *, const float *, const float *, float, void *, int64_t, int) {
+    switch (nv) {
+    case 1: return layernorm_rows_kernel<1, OutBf16>;
+    case 2: return layernorm_rows_kernel<2, OutBf16>;
+    case 3: return layernorm_rows_kernel<3, OutBf16>;
+    case 4: return layernorm_rows_kernel<4, OutBf16>;
+    case 5: return layernorm_rows_kernel<5, OutBf16>;
+    case 6: return layernorm_rows_kernel<6, OutBf16>;
+    case 7: return layernorm_rows_kernel<7, OutBf16>;
+    default: return layernorm_rows_kernel<8, OutBf16>;
     }
 }
 
@@ -193,12 +209,13 @@ __global__ __launch_bounds__(64 * kCmpWaves) void gold_compress_kernel(const uin
 hipError_t launch_layernorm_rows(const float *x, const float *gamma, const float *beta, float eps, void *y,
                                  bool out_bf16, int64_t rows, int width, hipStream_t st, KernelTiming tm) {
     if (rows <= 0) return hipSuccess;
-    const unsigned grid = (unsigned)std::min<int64_t>(rows, 2048);
+    const unsigned grid = (unsigned)std::min<int64_t>(rows, 4096);
+    const int nv = width / (4 * kLnThreads);
     if (out_bf16)
-        hipExtLaunchKernelGGL(layernorm_rows_kernel<true>, dim3(grid), dim3(kLnThreads), 0, st, tm.start, tm.stop, 0,
+        hipExtLaunchKernelGGL(layernorm_kernel_for<true>(nv), dim3(grid), dim3(kLnThreads), 0, st, tm.start, tm.stop, 0,
                               x, gamma, beta, eps, y, rows, width);
     else
-        hipExtLaunchKernelGGL(layernorm_rows_kernel<false>, dim3(grid), dim3(kLnThreads), 0, st, tm.start, tm.stop, 0,
+        hipExtLaunchKernelGGL(layernorm_kernel_for<false>(nv), dim3(grid), dim3(kLnThreads), 0, st, tm.start, tm.stop, 0,
                               x, gamma, beta, eps, y, rows, width);
     return hipGetLastError();
 }
