@@ -36,11 +36,15 @@
 // Workgroup = 4 waves, one (segment, head) work item.  Wave w owns value
 // columns 16w..16w+15 of the state and of o; lane (i16 = lane%16, grp =
 // lane/16) holds S[16*ib + 4*grp + e][16*w + i16] for ib, e in 0..3 (the
-// accumulator layout of the 16x16 MFMA).  r, k, w are loaded from memory
-// straight into the pre-processing layout; LDS holds every MFMA operand tile
-// row-major [token][channel] with a row-dependent XOR swizzle of its column
-// units (bank-conflict free); operands contracted over tokens are read with
-// ds_read_b64_tr_b16.
+// accumulator layout of the 16x16 MFMA).  Every input is loaded as whole
+// 128-byte token rows (16 bytes per lane, the next chunk prefetched into
+// registers while the current one is processed); r, k, w (and u') pass
+// through padded staging tiles in LDS into the pre-processing layout, v goes
+// to its operand tile.  LDS holds every MFMA operand tile row-major
+// [token][channel] with a row-dependent XOR swizzle of its column units
+// (bank-conflict free); operands contracted over tokens are read with
+// ds_read_b64_tr_b16.  Segments of a long sequence are independent work items
+// whose starting states come from a state pass and a scan over segments.
 #include <cstddef>
 
 #include <hip/hip_ext.h>

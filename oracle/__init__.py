@@ -15,7 +15,7 @@ Two implementations of the same definition live here:
   evaluated by brute force in numpy, O(T^2 D^2).  Tiny inputs only; it pins
   the recurrence.
 
-Conventions (readings of the pages):
+Conventions (readings of the pages where they leave a choice open):
   r, k, v, w : [tokens, H, D] packed rows (a batch is a packed set with
                offsets ``cu_seqlens``); D is the head size.
   u          : [H, D] static per-channel bonus (base Finch).
