@@ -2,16 +2,18 @@
 //
 // The recurrence of the GoldFinch architecture summary (section 3.4,
 // "Recurrent state update and output") is evaluated 64 tokens at a time.
-// Within a chunk, with Lam_t = sum_{j<=t} log2 w_j (per key channel, from the
-// chunk start) and a per-channel reference R = Lam_31:
+// Within a chunk, with P_t = w_0 w_1 ... w_t (per key channel, from the chunk
+// start; P_{-1} = 1):
 //
-//   o_t   = sum_i (r_t[i] 2^{Lam_{t-1}-R}) (2^R S)[i,:]              read-out of the carried state
+//   o_t   = sum_i r~_t[i] S[i,:]                                     read-out of the carried state
 //         + sum_{s<t} A_ts v_s,  A_ts = sum_i r~_t[i] k~_s[i]        in-chunk pairs
 //         + (r_t . u . k_t) v_t                                       bonus
-//   S_end = diag(2^{Lam_63}) S + diag(2^{Lam_63-R}) sum_s k~_s^T v_s
+//   S_end = diag(P_63) (S + sum_s k~_s^T v_s)
 //
-// with r~_t = r_t 2^{Lam_{t-1}-R} and k~_s = k_s 2^{R-Lam_s}: their product is
-// exactly the decay product of the pages' state equation, w_{s+1}...w_{t-1}.
+// with r~_t = r_t P_{t-1} and k~_s = k_s / P_s: their product is exactly the
+// decay product of the pages' state equation, w_{s+1}...w_{t-1}.  The
+// products come from an in-lane and a cross-lane (DPP) scan; only k~ needs a
+// reciprocal, no logarithm or exponential is taken.
 // All four contractions run on v_mfma_f32_16x16x32_bf16 with fp32
 // accumulation; every fp32 operand is split into bf16 hi + lo parts (three
 // products, or two when the other operand is an exact bf16 input), which keeps
@@ -20,18 +22,19 @@
 //
 // Two further forms of the same section are compile-time switches:
 //  - LOGD: the decay input holds d with w = exp(-exp(d)) (paragraph
-//    "Data-dependent decay"), so log2 w = -exp(d) log2(e) is formed directly
-//    (one exponential instead of a logarithm; no precision is lost to w
-//    rounding to 1 in bf16);
+//    "Data-dependent decay"), w = 2^{-e^d log2(e)} (no precision is lost to
+//    w rounding to 1 in bf16);
 //  - C2: the Finch-C2 mixer -- keys enter as k (1 - w) (paragraph "Key
 //    computation with normalization property"), no static bonus (the
 //    diagonal of A is zero), and the second value u'_t (a fifth input stream,
 //    staged like the others) is added to o (output equation).
 //
-// A chunk in which some channel decays by more than 2^96 over half a chunk
-// ("stiff") would push the rescaling factors out of range; such a chunk is
+// A chunk in which some channel decays by more than 2^96 over the chunk
+// ("stiff": P_63 < 2^-96) would push 1/P out of range; such a chunk is
 // evaluated token by token instead (exact, same registers), so the result is
-// defined for every 0 < w <= 1.
+// defined for every 0 < w <= 1.  The state pass, which needs only
+// diag(P_63) S + sum_s (P_63 / P_s) k_s^T v_s, forms those factors (all <= 1)
+// from log2 prefix sums and needs no such fallback.
 //
 // Workgroup = 4 waves, one (segment, head) work item.  Wave w owns value
 // columns 16w..16w+15 of the state and of o; lane (i16 = lane%16, grp =
@@ -62,8 +65,8 @@ typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
-constexpr float kStiffLog2 = 96.f;            // largest |half-chunk log2 decay| rescaled
-constexpr float kLog2Floor = -127.f;          // log2 w below this only occurs in stiff chunks
+constexpr float kMinChunkDecay = 0x1p-96f;    // smaller chunk decay products take the token-serial path
+constexpr float kLog2Floor = -127.f;          // floor of log2 w in the state pass (w = 0 stays finite)
 constexpr unsigned kOnePair = 0x3F803F80u;    // two bf16 1.0 (padding value of w)
 constexpr unsigned kNegInfPair = 0xFF80FF80u;  // two bf16 -inf (padding value of d: w = 1)
 constexpr float kLog2e = 1.4426950408889634f;
@@ -121,9 +124,9 @@ __device__ __forceinline__ Rsrc chunk_rsrc(const void *base, int64_t row0, int r
 template <int NStage>
 struct Smem {
     uint16_t v[kTileElems];          // values of the chunk
-    uint16_t rt_hi[kTileElems];      // r~ = r 2^{Lam_{t-1}-R}, bf16 hi/lo planes
+    uint16_t rt_hi[kTileElems];      // r~ = r P_{t-1}, bf16 hi/lo planes
     uint16_t rt_lo[kTileElems];
-    uint16_t kt_hi[kTileElems];      // k~ = k 2^{R-Lam_s} (state pass: k 2^{Lam_63-Lam_s})
+    uint16_t kt_hi[kTileElems];      // k~ = k / P_s (state pass: k 2^{Lam_63-Lam_s})
     uint16_t kt_lo[kTileElems];
     union {
         struct {
@@ -133,9 +136,7 @@ struct Smem {
         uint16_t stage[NStage][kStageElems];  // raw r, k, w (, u') rows of the chunk (until the first barrier)
     };
     alignas(16) float bonus_part[4][kChunk];   // per-wave partial sums of r.u.k per token
-    alignas(16) float row_exp2ref[kHeadDim];   // 2^{R_i}
-    alignas(16) float row_dec[kHeadDim];       // 2^{Lam_63,i}
-    alignas(16) float row_kfac[kHeadDim];      // 2^{Lam_63,i - R_i}
+    alignas(16) float row_dec[kHeadDim];       // decay of the whole chunk per key channel
     int stiff[4];
 };
 // the token-serial path stages 64 x 64 fp32 outputs across rt_hi and rt_lo
@@ -265,6 +266,22 @@ __device__ __forceinline__ float row_scan16(float x) {
     v = __float_as_int(__int_as_float(v) + __int_as_float(__builtin_amdgcn_update_dpp(0, v, 0x114, 0xF, 0xF, true)));
     v = __float_as_int(__int_as_float(v) + __int_as_float(__builtin_amdgcn_update_dpp(0, v, 0x118, 0xF, 0xF, true)));
     return __int_as_float(v);
+}
+
+// Inclusive product over the 16 lanes of each DPP row (lanes without a
+// source keep the old value, 1).
+__device__ __forceinline__ float row_prod16(float x) {
+    const int one = __float_as_int(1.f);
+    x *= __int_as_float(__builtin_amdgcn_update_dpp(one, __float_as_int(x), 0x111, 0xF, 0xF, false));
+    x *= __int_as_float(__builtin_amdgcn_update_dpp(one, __float_as_int(x), 0x112, 0xF, 0xF, false));
+    x *= __int_as_float(__builtin_amdgcn_update_dpp(one, __float_as_int(x), 0x114, 0xF, 0xF, false));
+    x *= __int_as_float(__builtin_amdgcn_update_dpp(one, __float_as_int(x), 0x118, 0xF, 0xF, false));
+    return x;
+}
+
+// Value of the previous lane of the 16-lane row; 1 in its first lane.
+__device__ __forceinline__ float row_prev(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(1.f), __float_as_int(x), 0x111, 0xF, 0xF, false));
 }
 
 // Value of lane N of this lane's 16-lane row (DPP row_newbcast).
@@ -523,9 +540,72 @@ __global__ __launch_bounds__(256, 2) void wkv_chunk_kernel(Geometry g, Tensors t
             }
         }
 
-        // ---- pre-processing: log-decay prefix, rescaled operands, bonus -------
-        {
-            // lam holds the decay input (w, or d); it becomes log2 w, floored
+        // ---- pre-processing: decay prefix, rescaled operands, bonus ----------
+        if (M == Mode::Main) {
+            // Products of the decays from the chunk start, P_t = w_0 ... w_t per key
+            // channel: r~_t = r_t P_{t-1} and k~_s = k_s / P_s multiply to the decay
+            // w_{s+1} ... w_{t-1} of the state equation.  lam holds the decay
+            // inputs (w, or d); pw becomes the in-lane inclusive products.
+            float pw[4][4];
+            #pragma unroll
+            for (int a = 0; a < 4; ++a)
+                #pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const float x = lam[a][q];
+                    const float e = LOGD ? __builtin_amdgcn_exp2f(x * kLog2e) : 0.f;   // exp(d)
+                    if (C2) kk_[a][q] *= one_minus_w<LOGD>(x, e);
+                    pw[a][q] = LOGD ? __builtin_amdgcn_exp2f(-e * kLog2e) : x;
+                }
+            // in-lane products over 4 tokens, then across the 16 lanes: excl =
+            // P before the lane's first token, total = P_63
+            float excl[4], total[4];
+            bool stiff = false;
+            #pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                pw[1][q] *= pw[0][q];
+                pw[2][q] *= pw[1][q];
+                pw[3][q] *= pw[2][q];
+                const float incl = row_prod16(pw[3][q]);
+                excl[q] = row_prev(incl);
+                total[q] = row_bcast<15>(incl);
+                stiff |= !(total[q] >= kMinChunkDecay);
+            }
+            stiff = __any(stiff);
+            if (lane == 0) sm.stiff[wave] = stiff ? 1 : 0;
+            if (i16 == 15) {
+                #pragma unroll
+                for (int q = 0; q < 4; ++q) sm.row_dec[c0 + q] = total[q];
+            }
+            float bp[4];
+            #pragma unroll
+            for (int a = 0; a < 4; ++a) {
+                float rs[4], ks[4];
+                bp[a] = 0.f;
+                #pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const float p_prev = a == 0 ? excl[q] : excl[q] * pw[a - 1][q];   // P_{t-1}
+                    const float p_cur = excl[q] * pw[a][q];                            // P_t
+                    rs[q] = rr[a][q] * p_prev;
+                    ks[q] = kk_[a][q] * __builtin_amdgcn_rcpf(p_cur);
+                    if (!C2) bp[a] += rr[a][q] * u4[q] * kk_[a][q];
+                }
+                u32x2 rh, rl, kh, kl;
+                split4(rs[0], rs[1], rs[2], rs[3], rh, rl);
+                split4(ks[0], ks[1], ks[2], ks[3], kh, kl);
+                lds_write_b64(sm.rt_hi, lb.pw_rt[a], rh);
+                lds_write_b64(sm.rt_lo, lb.pw_rt[a], rl);
+                lds_write_b64(sm.kt_hi, lb.pw_kt[a], kh);
+                lds_write_b64(sm.kt_lo, lb.pw_kt[a], kl);
+                if (!C2) bp[a] = sum_rows4(bp[a]);
+            }
+            if (!C2 && grp == 0) {
+                f32x4 b4 = {bp[0], bp[1], bp[2], bp[3]};
+                *reinterpret_cast<f32x4 *>(&sm.bonus_part[wave][4 * i16]) = b4;
+            }
+        } else {
+            // State pass: log2 decays relative to the chunk end, k~_s = k_s
+            // 2^{Lam_63 - Lam_s} <= k_s (no factor exceeds 1, so it needs no
+            // token-serial fallback).  lam holds the decay inputs (w, or d).
             #pragma unroll
             for (int a = 0; a < 4; ++a)
                 #pragma unroll
@@ -536,9 +616,8 @@ __global__ __launch_bounds__(256, 2) void wkv_chunk_kernel(Geometry g, Tensors t
                     lam[a][q] = fmaxf(LOGD ? -e * kLog2e : __builtin_amdgcn_logf(x), kLog2Floor);
                 }
             // inclusive prefix over the chunk: in-lane over 4 tokens, then across
-            // the 16 lanes; lam becomes E_t = Lam_t - reference (Main: R = Lam_31,
-            // State: Lam_63), and off = E_{t-1} for the first token of the lane
-            float off[4], total[4], ref[4];
+            // the 16 lanes; lam becomes Lam_t - Lam_63
+            float total[4];
             #pragma unroll
             for (int q = 0; q < 4; ++q) {
                 lam[1][q] += lam[0][q];
@@ -546,72 +625,27 @@ __global__ __launch_bounds__(256, 2) void wkv_chunk_kernel(Geometry g, Tensors t
                 lam[3][q] += lam[2][q];
                 const float incl = row_scan16(lam[3][q]);
                 total[q] = row_bcast<15>(incl);                         // Lam_63
-                ref[q] = row_bcast<7>(incl);                            // Lam_31
-                off[q] = (incl - lam[3][q]) - (M == Mode::Main ? ref[q] : total[q]);
+                const float off = (incl - lam[3][q]) - total[q];
                 #pragma unroll
-                for (int a = 0; a < 4; ++a) lam[a][q] += off[q];
+                for (int a = 0; a < 4; ++a) lam[a][q] += off;
             }
-            if (M == Mode::Main) {
-                bool stiff = false;
+            if (i16 == 15) {
                 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
-                    const float h1 = -ref[q], h2 = ref[q] - total[q];
-                    stiff |= (h1 > kStiffLog2) | (h1 < -kStiffLog2) | (h2 > kStiffLog2) | (h2 < -kStiffLog2);
+                    sm.row_dec[c0 + q] = __builtin_amdgcn_exp2f(total[q]);
+                    lam_seg[q] += total[q];
                 }
-                stiff = __any(stiff);
-                if (lane == 0) sm.stiff[wave] = stiff ? 1 : 0;
-                if (i16 == 15) {
-                    #pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        sm.row_exp2ref[c0 + q] = __builtin_amdgcn_exp2f(ref[q]);
-                        sm.row_dec[c0 + q] = __builtin_amdgcn_exp2f(total[q]);
-                        sm.row_kfac[c0 + q] = __builtin_amdgcn_exp2f(total[q] - ref[q]);
-                    }
-                }
-                float bp[4];
+            }
+            #pragma unroll
+            for (int a = 0; a < 4; ++a) {
+                float ks[4];
                 #pragma unroll
-                for (int a = 0; a < 4; ++a) {
-                    float rs[4], ks[4];
-                    bp[a] = 0.f;
-                    #pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        const float e_prev = a == 0 ? off[q] : lam[a - 1][q];   // Lam_{t-1} - R
-                        rs[q] = rr[a][q] * __builtin_amdgcn_exp2f(e_prev);
-                        ks[q] = kk_[a][q] * __builtin_amdgcn_exp2f(-lam[a][q]);  // R - Lam_t
-                        if (!C2) bp[a] += rr[a][q] * u4[q] * kk_[a][q];
-                    }
-                    u32x2 rh, rl, kh, kl;
-                    split4(rs[0], rs[1], rs[2], rs[3], rh, rl);
-                    split4(ks[0], ks[1], ks[2], ks[3], kh, kl);
-                    lds_write_b64(sm.rt_hi, lb.pw_rt[a], rh);
-                    lds_write_b64(sm.rt_lo, lb.pw_rt[a], rl);
-                    lds_write_b64(sm.kt_hi, lb.pw_kt[a], kh);
-                    lds_write_b64(sm.kt_lo, lb.pw_kt[a], kl);
-                    if (!C2) bp[a] = sum_rows4(bp[a]);
-                }
-                if (!C2 && grp == 0) {
-                    f32x4 b4 = {bp[0], bp[1], bp[2], bp[3]};
-                    *reinterpret_cast<f32x4 *>(&sm.bonus_part[wave][4 * i16]) = b4;
-                }
-            } else {
-                if (i16 == 15) {
-                    #pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        sm.row_dec[c0 + q] = __builtin_amdgcn_exp2f(total[q]);
-                        lam_seg[q] += total[q];
-                    }
-                }
-                #pragma unroll
-                for (int a = 0; a < 4; ++a) {
-                    float ks[4];
-                    #pragma unroll
-                    for (int q = 0; q < 4; ++q)
-                        ks[q] = kk_[a][q] * __builtin_amdgcn_exp2f(-lam[a][q]);   // Lam_63 - Lam_t
-                    u32x2 kh, kl;
-                    split4(ks[0], ks[1], ks[2], ks[3], kh, kl);
-                    lds_write_b64(sm.kt_hi, lb.pw_kt[a], kh);
-                    lds_write_b64(sm.kt_lo, lb.pw_kt[a], kl);
-                }
+                for (int q = 0; q < 4; ++q)
+                    ks[q] = kk_[a][q] * __builtin_amdgcn_exp2f(-lam[a][q]);   // Lam_63 - Lam_t
+                u32x2 kh, kl;
+                split4(ks[0], ks[1], ks[2], ks[3], kh, kl);
+                lds_write_b64(sm.kt_hi, lb.pw_kt[a], kh);
+                lds_write_b64(sm.kt_lo, lb.pw_kt[a], kl);
             }
         }
         __syncthreads();
@@ -719,7 +753,7 @@ __global__ __launch_bounds__(256, 2) void wkv_chunk_kernel(Geometry g, Tensors t
             a_tiles<!C2, 2>(sm, lb, TB, SB, i16, grp);
         }
 
-        // ---- read-out of the carried state: o^T = (2^R S)^T r~^T ------------------
+        // ---- read-out of the carried state: o^T = S^T r~^T ---------------------------
         {
             bf16x8 s_hi[2], s_lo[2];
             #pragma unroll
@@ -728,9 +762,8 @@ __global__ __launch_bounds__(256, 2) void wkv_chunk_kernel(Geometry g, Tensors t
                 #pragma unroll
                 for (int half = 0; half < 2; ++half) {
                     const int ib = 2 * kk + half;
-                    const f32x4 er = *reinterpret_cast<const f32x4 *>(&sm.row_exp2ref[16 * ib + 4 * grp]);
-                    const HiLo x = split2(S[ib][0] * er[0], S[ib][1] * er[1]);
-                    const HiLo y = split2(S[ib][2] * er[2], S[ib][3] * er[3]);
+                    const HiLo x = split2(S[ib][0], S[ib][1]);
+                    const HiLo y = split2(S[ib][2], S[ib][3]);
                     hi[2 * half] = x.hi; lo[2 * half] = x.lo;
                     hi[2 * half + 1] = y.hi; lo[2 * half + 1] = y.lo;
                 }
@@ -778,9 +811,8 @@ __global__ __launch_bounds__(256, 2) void wkv_chunk_kernel(Geometry g, Tensors t
             #pragma unroll
             for (int ib = 0; ib < 4; ++ib) {
                 const f32x4 dec = *reinterpret_cast<const f32x4 *>(&sm.row_dec[16 * ib + 4 * grp]);
-                const f32x4 kf = *reinterpret_cast<const f32x4 *>(&sm.row_kfac[16 * ib + 4 * grp]);
                 #pragma unroll
-                for (int e = 0; e < 4; ++e) S[ib][e] = dec[e] * S[ib][e] + kf[e] * p[ib][e];
+                for (int e = 0; e < 4; ++e) S[ib][e] = dec[e] * (S[ib][e] + p[ib][e]);
             }
         }
 
