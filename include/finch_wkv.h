@@ -46,7 +46,7 @@
  * Domain: 0 < w <= 1 (w == 1 exactly is legal); any d, including +-inf, with
  * WKV_FLAG_DECAY_LOG.  Values outside it and NaN are not checked and
  * propagate.  Finite |r|, |k| below 2^31 are required
- * (the chunked evaluation rescales them by powers of two up to 2^96).
+ * (the chunked evaluation rescales them by decay factors up to 2^96).
  *
  * Errors: every entry point validates its arguments before touching the GPU
  * and returns a wkv_status_t; wkv_last_error() gives a human-readable detail
