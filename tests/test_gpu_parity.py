@@ -253,3 +253,13 @@ def test_stiff_decays(T, H):
 def test_f32_long_sequence():
     wl = make_workload(0, T=3000, H=3, B=2)
     _check(wl)
+
+
+@pytest.mark.timeout(600)
+def test_maximum_head_count():
+    """H = 65536, the largest the library accepts (64 rows x H x 256 B per
+    chunk must fit 32-bit offsets): T = 65 (a full chunk and a ragged one),
+    random states; sampled heads, including the last, against the oracle."""
+    wl = make_workload(3, T=65, H=65536)
+    heads = [0, 1, 4097, 32768, 65534, 65535]
+    _check(wl, heads=heads)
