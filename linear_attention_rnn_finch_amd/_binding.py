@@ -25,8 +25,8 @@ VARIANTS = ("finch", "c2")       # base Finch (bonus u) or the Finch-C2 time mix
 
 if not os.path.exists(LIBRARY_PATH):
     raise ImportError(
-        "libfinch_wkv.so is not built (%s); run `python -m "
-        "linear_attention_rnn_finch_amd.build_lib` or __graft_entry__.build()" % LIBRARY_PATH)
+        "libfinch_wkv.so is not built (%s); run `python "
+        "linear_attention_rnn_finch_amd/build_lib.py` or __graft_entry__.build()" % LIBRARY_PATH)
 
 _lib = ctypes.CDLL(LIBRARY_PATH)
 _vp, _sz, _i, _i32p = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int, ctypes.POINTER(ctypes.c_int32)

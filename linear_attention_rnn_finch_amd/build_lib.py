@@ -1,6 +1,6 @@
 """Build libfinch_wkv.so (gfx950) in-tree with hipcc.
 
-    python -m linear_attention_rnn_finch_amd.build_lib
+    python linear_attention_rnn_finch_amd/build_lib.py
 
 compiles every source under csrc/ for --offload-arch=gfx950 and links
 linear_attention_rnn_finch_amd/libfinch_wkv.so.  Packed fp32 vector ops are
