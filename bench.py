@@ -53,33 +53,37 @@ def algorithmic_bytes(cfg, tokens, n_seq, has_state_in, variant="finch"):
 
 # HBM traffic of the main kernel, from rocprofv3 FETCH_SIZE / WRITE_SIZE passes
 # (scaled by a plain copy of known size); valid only for the workload and the
-# kernel source the counters were taken on
-def traffic_file(workload_name, kernel_name):
+# kernel source the counters were taken on.  Records are kept per kernel:
+# "wkv_chunk_main" (chunked scan), "wkv_decode" (step kernel), "epilogue".
+def traffic_family(workload_name, kernel_name):
     if workload_name.startswith(("layernorm_heads", "gold_compress")):
+        return "epilogue"
+    return "wkv_decode" if kernel_name.startswith("wkv_decode") else "wkv_chunk_main"
+
+
+def traffic_file(workload_name, kernel_name):
+    family = traffic_family(workload_name, kernel_name)
+    if family == "epilogue":
         return os.path.join(ROOT, "profiles", "%s_traffic.md" % workload_name)
-    stem = "wkv_decode" if kernel_name.startswith("wkv_decode") else "wkv_chunk_main"
-    return os.path.join(ROOT, "profiles", "%s_%s_traffic.md" % (stem, workload_name.replace("+", "_")))
+    return os.path.join(ROOT, "profiles", "%s_%s_traffic.md" % (family, workload_name.replace("+", "_")))
 
 
 def workload_name(cfg_name, decay, variant):
     return cfg_name + ("+c2" if variant == "c2" else "") + ("+logdecay" if decay == "log" else "")
 
 
-# kernel sources behind each family of traffic records
+# sources behind each family of traffic records: the kernel, and for the
+# chunked scan the host plan that sizes its segments
 KERNEL_SOURCES = {
-    "scan": ("linear_attention_rnn_finch_amd/csrc/wkv_chunk.hip",
-             "linear_attention_rnn_finch_amd/csrc/wkv_decode.hip",
-             "linear_attention_rnn_finch_amd/csrc/wkv_serial.hip"),
+    "wkv_chunk_main": ("linear_attention_rnn_finch_amd/csrc/wkv_chunk.hip",
+                       "linear_attention_rnn_finch_amd/csrc/wkv_api.cpp"),
+    "wkv_decode": ("linear_attention_rnn_finch_amd/csrc/wkv_decode.hip",),
     "epilogue": ("linear_attention_rnn_finch_amd/csrc/wkv_epilogue.hip",),
 }
 
 
-def kernel_family(workload_name):
-    return "epilogue" if workload_name.startswith(("layernorm_heads", "gold_compress")) else "scan"
-
-
 def kernel_source_digest(family):
-    """SHA-256 over the family's kernel sources (any change voids its records)."""
+    """SHA-256 over the family's sources (any change voids its records)."""
     h = hashlib.sha256()
     for rel in KERNEL_SOURCES[family]:
         with open(os.path.join(ROOT, rel), "rb") as f:
@@ -101,7 +105,7 @@ def measured_traffic(workload_name, kernel_name):
             fields[key.strip()] = val.strip().strip("`")
     if fields.get("workload") != workload_name:
         return None
-    if fields.get("kernel_source_sha256") != kernel_source_digest(kernel_family(workload_name)):
+    if fields.get("kernel_source_sha256") != kernel_source_digest(traffic_family(workload_name, kernel_name)):
         return None
     try:
         return int(fields["traffic_bytes_per_launch"])

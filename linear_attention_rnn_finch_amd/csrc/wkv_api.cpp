@@ -241,7 +241,7 @@ wkv_status_t run(const Plan &p, const Tensors &t, const Variant &var, void *ws, 
     }
     const KernelTiming tm{g_ev_before, g_ev_after};
     if (p.max_len <= kDecodeMaxT && !p.split) {       // recurrent steps: state-streaming kernel
-        if ((e = launch_decode(g, t, p.bf16, var, st, tm)) != hipSuccess) return fail_hip(e, "step launch");
+        if ((e = launch_decode(g, t, p.bf16, var, (int)p.max_len, st, tm)) != hipSuccess) return fail_hip(e, "step launch");
         return WKV_OK;
     }
     if (!p.bf16) {

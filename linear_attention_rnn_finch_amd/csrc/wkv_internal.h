@@ -114,9 +114,9 @@ struct KernelTiming {
 
 hipError_t launch_serial(const Geometry &g, const Tensors &t, bool bf16, Variant v, hipStream_t st,
                          KernelTiming tm = {});
-// short sequences (at most kDecodeMaxT tokens each, never split): one wave per
-// (sequence, head), fp32 state in registers
-hipError_t launch_decode(const Geometry &g, const Tensors &t, bool bf16, Variant v, hipStream_t st,
+// short sequences (at most kDecodeMaxT tokens each, never split; max_len the
+// longest): one wave per (sequence, head), fp32 state in registers
+hipError_t launch_decode(const Geometry &g, const Tensors &t, bool bf16, Variant v, int max_len, hipStream_t st,
                          KernelTiming tm = {});
 // bf16 path: state pass + segment scan (only when some sequence is split), then
 // the main chunked scan.
