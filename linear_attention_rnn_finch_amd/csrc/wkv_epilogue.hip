@@ -15,10 +15,9 @@
 //   contraction over D on v_mfma_f32_16x16x32_bf16, computed as
 //   c^T = W x^T so that both operands are read as 16-byte row pieces (the
 //   weight is stored [D/16, D]) and every lane's four results are adjacent
-//   outputs of one token.  The contraction is split over the eight waves of
-//   a workgroup (see gold_compress_kernel): with only one workgroup per CU
-//   at this size, latency is hidden by having each wave's loads in flight at
-//   once rather than by occupancy.
+//   outputs of one token.  Operands are staged through LDS in slices of
+//   d_model, loaded as whole 128-byte lines two slices ahead (see
+//   gold_compress_kernel).
 #include <hip/hip_ext.h>
 
 #include "wkv_internal.h"
@@ -123,77 +122,124 @@ void (*layernorm_kernel_for(int nv))(const float *, const float *, const float *
 
 constexpr int kCmpRows = 32;      // tokens per workgroup (two 16-token tiles)
 constexpr int kCmpCols = 64;      // outputs per workgroup (four 16-output tiles)
-constexpr int kCmpWaves = 8;      // the contraction over d_model is split over the waves
-constexpr int kCmpBatch = 8;      // K steps of 32 whose loads a wave issues together
+constexpr int kCmpK = 256;        // d_model slice staged through LDS per step
+constexpr int kCmpPitch = kCmpK + 8;                     // LDS row pitch in bf16 (528 B)
+constexpr int kCmpThreads = 1024; // sixteen waves: two per 16 x 16 output tile
+constexpr int kCmpXLoads = kCmpRows * kCmpK / 8 / kCmpThreads;   // 16-byte pieces per thread and step: 1
+constexpr int kCmpWLoads = kCmpCols * kCmpK / 8 / kCmpThreads;   // 2
+
+struct alignas(16) CmpSmem {
+    uint16_t x[2][kCmpRows][kCmpPitch];   // token rows of the slice, double-buffered
+    uint16_t w[2][kCmpCols][kCmpPitch];   // weight rows of the slice
+};
+
+// One step's global loads, held in registers until they are written to LDS.
+struct CmpRegs {
+    u32x4 x[kCmpXLoads], w[kCmpWLoads];
+};
 
 __device__ __forceinline__ f32x4 mfma(bf16x8 a, bf16x8 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
-// Workgroup: 32 tokens x 64 outputs; wave w contracts over its own eighth of
-// d_model for all eight 16 x 16 tiles (every operand byte is read once per
-// workgroup), with all of its loads for up to 8 K steps in flight at once;
-// the eight partial tiles are summed through LDS.
+// Workgroup: 32 tokens x 64 outputs over the whole of d_model, in slices of
+// 256.  Each slice is loaded as whole 128-byte lines (the 32 lanes of a row
+// read its 512 contiguous bytes; a load that names a row as a 16-byte piece
+// per lane per MFMA operand would fetch 16 half lines per instruction), two
+// slices ahead of the arithmetic, and written to LDS rows of 528 bytes, whose
+// 16-byte shift per row keeps the operand reads free of bank conflicts.  Waves
+// v and v + 8 share the 16 x 16 tile of tokens m0 + 16 (v / 4 % 2) and
+// outputs n0 + 16 (v % 4), each taking half of every slice; their two partial
+// tiles are added through LDS at the end.  Four waves per SIMD hide the LDS
+// and barrier latency.
 template <bool OutBf16>
-__global__ __launch_bounds__(64 * kCmpWaves) void gold_compress_kernel(const uint16_t *x, const uint16_t *w,
-                                                                       void *c, int64_t M, int K, int N) {
-    __shared__ f32x4 part[kCmpWaves][2 * 4][64];          // [wave][tile][lane]: 64 KB
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+__global__ __launch_bounds__(kCmpThreads) void gold_compress_kernel(const uint16_t *x, const uint16_t *w, void *c,
+                                                                    int64_t M, int K, int N) {
+    __shared__ CmpSmem sm;
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
     const int i16 = lane & 15, grp = lane >> 4;
     const int64_t m0 = (int64_t)blockIdx.x * kCmpRows;
     const int n0 = blockIdx.y * kCmpCols;
-    const int kw = K / kCmpWaves;                           // this wave's share, a multiple of 128
-    const int kb = wave * kw;
-    // A = weight rows n0 + 16*nt + i16, B = token rows m0 + 16*mt + i16 (rows past
-    // M read row M - 1 and are not stored); lane takes K slots 8*grp .. +7
-    const uint16_t *wa[4], *xb[2];
+    const int steps = K / kCmpK;
+
+    // load piece q = tid + 256 j: row q / 32, 16-byte piece q % 32 of the row's slice
+    const uint16_t *xg[kCmpXLoads], *wg[kCmpWLoads];
+    int xl[kCmpXLoads], wl[kCmpWLoads];
     #pragma unroll
-    for (int nt = 0; nt < 4; ++nt) wa[nt] = w + (size_t)(n0 + 16 * nt + i16) * K + kb + 8 * grp;
-    #pragma unroll
-    for (int mt = 0; mt < 2; ++mt) {
-        int64_t m = m0 + 16 * mt + i16;
-        if (m >= M) m = M - 1;
-        xb[mt] = x + (size_t)m * K + kb + 8 * grp;
-    }
-    f32x4 acc[2][4];
-    #pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
-        #pragma unroll
-        for (int nt = 0; nt < 4; ++nt) acc[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    for (int k0 = 0; k0 < kw; k0 += 32 * kCmpBatch) {
-        u32x4 a[kCmpBatch][4], b[kCmpBatch][2];
-        #pragma unroll
-        for (int u = 0; u < kCmpBatch; ++u) {
-            if (k0 + 32 * u < kw) {
-                #pragma unroll
-                for (int nt = 0; nt < 4; ++nt) a[u][nt] = *reinterpret_cast<const u32x4 *>(wa[nt] + k0 + 32 * u);
-                #pragma unroll
-                for (int mt = 0; mt < 2; ++mt) b[u][mt] = *reinterpret_cast<const u32x4 *>(xb[mt] + k0 + 32 * u);
-            }
-        }
-        #pragma unroll
-        for (int u = 0; u < kCmpBatch; ++u) {
-            if (k0 + 32 * u < kw) {
-                #pragma unroll
-                for (int mt = 0; mt < 2; ++mt)
-                    #pragma unroll
-                    for (int nt = 0; nt < 4; ++nt)
-                        acc[mt][nt] = mfma(__builtin_bit_cast(bf16x8, a[u][nt]), __builtin_bit_cast(bf16x8, b[u][mt]),
-                                           acc[mt][nt]);
-            }
-        }
+    for (int j = 0; j < kCmpXLoads; ++j) {
+        const int q = tid + kCmpThreads * j, row = q >> 5, col = (q & 31) * 8;
+        int64_t m = m0 + row;
+        if (m >= M) m = M - 1;                              // rows past M: loaded, never stored
+        xg[j] = x + (size_t)m * K + col;
+        xl[j] = row * kCmpPitch + col;
     }
     #pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
+    for (int j = 0; j < kCmpWLoads; ++j) {
+        const int q = tid + kCmpThreads * j, row = q >> 5, col = (q & 31) * 8;
+        wg[j] = w + (size_t)(n0 + row) * K + col;
+        wl[j] = row * kCmpPitch + col;
+    }
+    // slice s (clamped to the last one: the look-ahead past the end reloads it)
+    auto load = [&](CmpRegs &P, int s) {
+        const int k0 = (s < steps ? s : steps - 1) * kCmpK;
         #pragma unroll
-        for (int nt = 0; nt < 4; ++nt) part[wave][4 * mt + nt][lane] = acc[mt][nt];
-    __syncthreads();
-    // thread = (tile, lane): acc layout value e is c[m0 + 16*mt + i16][n0 + 16*nt + 4*grp + e]
-    const int tile = threadIdx.x >> 6;                      // 8 tiles, one per wave's worth of threads
-    f32x4 sum = part[0][tile][lane];
-    #pragma unroll
-    for (int v = 1; v < kCmpWaves; ++v) sum += part[v][tile][lane];
+        for (int j = 0; j < kCmpXLoads; ++j) P.x[j] = *reinterpret_cast<const u32x4 *>(xg[j] + k0);
+        #pragma unroll
+        for (int j = 0; j < kCmpWLoads; ++j) P.w[j] = *reinterpret_cast<const u32x4 *>(wg[j] + k0);
+        __builtin_amdgcn_sched_barrier(0);                  // keep the loads where they are issued
+    };
+    auto stash = [&](const CmpRegs &P, int buf) {
+        #pragma unroll
+        for (int j = 0; j < kCmpXLoads; ++j) *reinterpret_cast<u32x4 *>(&sm.x[buf][0][0] + xl[j]) = P.x[j];
+        #pragma unroll
+        for (int j = 0; j < kCmpWLoads; ++j) *reinterpret_cast<u32x4 *>(&sm.w[buf][0][0] + wl[j]) = P.w[j];
+    };
+    // MFMA operands: lane (i16, grp) takes d_model slots 32u + 8grp .. +7 of
+    // weight row 16nt + i16 (A) and of token row 16mt + i16 (B), for the four
+    // substeps u of this wave's half of the slice
+    const int tile = wave & 7, half = wave >> 3;
     const int mt = tile >> 2, nt = tile & 3;
+    f32x4 acc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};   // even/odd substeps
+    auto compute = [&](int buf) {
+        bf16x8 a[4], b[4];
+        #pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int k = 32 * (4 * half + u) + 8 * grp;
+            a[u] = *reinterpret_cast<const bf16x8 *>(&sm.w[buf][16 * nt + i16][k]);
+            b[u] = *reinterpret_cast<const bf16x8 *>(&sm.x[buf][16 * mt + i16][k]);
+        }
+        #pragma unroll
+        for (int u = 0; u < 4; ++u) acc[u & 1] = mfma(a[u], b[u], acc[u & 1]);
+    };
+
+    // two register sets: while slice s is computed from LDS, slice s + 1 is
+    // written to the other LDS buffer and slice s + 2 is in flight (steps is
+    // even)
+    CmpRegs P0, P1;
+    load(P0, 0);
+    load(P1, 1);
+    stash(P0, 0);
+    __syncthreads();
+    for (int s = 0; s < steps; s += 2) {
+        load(P0, s + 2);
+        compute(0);
+        stash(P1, 1);
+        __syncthreads();
+        load(P1, s + 3);
+        compute(1);
+        stash(P0, 0);
+        __syncthreads();
+    }
+
+    // the second half's partial tiles, through LDS (the operand buffers are
+    // free after the last barrier)
+    f32x4 *part = reinterpret_cast<f32x4 *>(&sm.x[0][0][0]);   // [tile][lane]: 8 KB
+    if (half) part[tile * 64 + lane] = acc[0] + acc[1];
+    __syncthreads();
+    if (half) return;
+    // acc layout: value e of lane (i16, grp) is c[m0 + 16mt + i16][n0 + 16nt + 4grp + e]
+    const f32x4 sum = acc[0] + acc[1] + part[tile * 64 + lane];
     const int64_t m = m0 + 16 * mt + i16;
     if (m < M) {
         const size_t at = (size_t)m * N + n0 + 16 * nt + 4 * grp;
@@ -223,12 +269,13 @@ hipError_t launch_layernorm_rows(const float *x, const float *gamma, const float
 hipError_t launch_gold_compress(const uint16_t *x, const uint16_t *w, void *c, bool out_bf16, int64_t M, int K,
                                 int N, hipStream_t st, KernelTiming tm) {
     if (M <= 0) return hipSuccess;
+    if (K % (4 * kCmpK) != 0 || N % kCmpCols != 0) return hipErrorInvalidValue;
     const dim3 grid((unsigned)((M + kCmpRows - 1) / kCmpRows), (unsigned)(N / kCmpCols));
     if (out_bf16)
-        hipExtLaunchKernelGGL(gold_compress_kernel<true>, grid, dim3(64 * kCmpWaves), 0, st, tm.start, tm.stop, 0,
+        hipExtLaunchKernelGGL(gold_compress_kernel<true>, grid, dim3(kCmpThreads), 0, st, tm.start, tm.stop, 0,
                               x, w, c, M, K, N);
     else
-        hipExtLaunchKernelGGL(gold_compress_kernel<false>, grid, dim3(64 * kCmpWaves), 0, st, tm.start, tm.stop, 0,
+        hipExtLaunchKernelGGL(gold_compress_kernel<false>, grid, dim3(kCmpThreads), 0, st, tm.start, tm.stop, 0,
                               x, w, c, M, K, N);
     return hipGetLastError();
 }
