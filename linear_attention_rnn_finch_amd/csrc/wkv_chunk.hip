@@ -90,13 +90,22 @@ struct ChunkRegs<true> {
 
 // ---- LDS tile layouts ---------------------------------------------------------
 // Every tile is 64 rows x 64 bf16 (128 B per row, no padding).  Column units
-// are XOR-swizzled with a function of the low four row bits, which keeps the
-// MFMA operand reads free of bank conflicts (32 banks x 4 B) while every access
-// address stays "per-lane base + compile-time constant":
-//   rt, a : 8-byte unit u -> u ^ (r & 15)
-//   kt    : 8-byte unit u -> u ^ g(r & 15), g swaps the two bit pairs
+// are XOR-swizzled with a function of the row.  The LDS has 64 banks of 4 B;
+// 8-byte reads are served 32 lanes per pass and 8-byte writes 16 lanes per
+// pass, and the swizzles keep every pass on distinct banks:
+//   a     : 8-byte unit u -> u ^ (r & 15)
+//   rt    : 8-byte unit u -> u ^ (r & 15) ^ (r >> 4)
+//   kt    : 8-byte unit u -> u ^ L(r & 15) ^ phi(r >> 4), L(x) = (x0, x3, x2, x1)
+//           (bits from low to high), phi(y) = y0 + 8 y1
 //   v     : 16-byte unit u -> u ^ ((r & 3) << 1)
-__device__ __forceinline__ int g_kt(int x) { return (x >> 2) | ((x & 3) << 2); }
+// The pre-processing writes rows 4x + a (x = lane % 16), so the rt and kt
+// swizzles take row bits 4-5 as well; the operand reads name rows whose bits
+// 4-5 are a compile-time constant, so each read address is a per-lane base
+// XOR a constant (plus a constant).
+__device__ __forceinline__ int l_kt(int x) { return (x & 5) | (((x >> 3) & 1) << 1) | (((x >> 1) & 1) << 3); }
+__device__ __forceinline__ constexpr int phi_kt(int y) { return (y & 1) | (((y >> 1) & 1) << 3); }
+__device__ __forceinline__ int swz_rt(int r) { return (r & 15) ^ (r >> 4); }
+__device__ __forceinline__ int swz_kt(int r) { return l_kt(r & 15) ^ phi_kt(r >> 4); }
 __device__ __forceinline__ int off_v(int r, int c) {
     return r * 64 + ((((c >> 3) ^ ((r & 3) << 1)) << 3) | (c & 7));
 }
@@ -216,12 +225,14 @@ __device__ __forceinline__ u32x2 lds_read_tr(const uint16_t *tile, int elem) {
 
 // Per-lane LDS element offsets (lane i16 = x, group grp, wave w), computed once.
 struct LdsBases {
-    int ro_x[4];   // channel-contracted rows 16*b + x of rt / a: [2*kk + hh] (+ 1024*b)
-    int ro_k[4];   // same for kt
+    int ro_x[4];   // channel-contracted rows 16*b + x of a: [2*kk + hh] (+ 1024*b);
+                   // of rt: (ro_x ^ 4*b) + 1024*b
+    int ro_k[4];   // same for kt: (ro_k ^ 4*phi(b)) + 1024*b
     int pw_rt[4];  // pre-processing writes, rows 4*x + a: [a]
     int pw_kt[4];
     int aw[4];     // A tile writes, row 16*TB + x, columns 16*SB + 4*grp: [SB] (+ 1024*TB)
-    int tr_kt[4];  // token-contracted kt columns 16*ib + x: [ib] (+ 64*(32*kk + 16*hh))
+    int tr_kt[4];  // token-contracted kt columns 16*ib + x: [ib], used as
+                   // (tr_kt ^ 4*phi(2*kk + hh)) + 64*(32*kk + 16*hh)
     int tr_v;      // token-contracted v columns 16*w + x (+ 64*(32*kk + 16*hh))
     int vw;        // v writes, rows tid/8 (+ 64*32*m), 16-byte piece tid%8
 };
@@ -229,19 +240,18 @@ struct LdsBases {
 __device__ __forceinline__ LdsBases make_bases(int tid) {
     const int lane = tid & 63, x = lane & 15, grp = lane >> 4, w = tid >> 6;
     LdsBases b;
-    const int gx = x, gk = g_kt(x);
     #pragma unroll
-    for (int q = 0; q < 4; ++q) {                 // q = 2*kk + hh -> column unit bits 8*kk + 4*hh
-        const int hi = 4 * q;
-        b.ro_x[q] = x * 64 + (((grp ^ (gx & 3)) | (hi ^ (gx & 12))) << 2);
-        b.ro_k[q] = x * 64 + (((grp ^ (gk & 3)) | (hi ^ (gk & 12))) << 2);
+    for (int q = 0; q < 4; ++q) {                 // q = 2*kk + hh -> column unit 4*q + grp
+        b.ro_x[q] = x * 64 + (((4 * q + grp) ^ x) << 2);
+        b.ro_k[q] = x * 64 + (((4 * q + grp) ^ l_kt(x)) << 2);
     }
     #pragma unroll
     for (int a = 0; a < 4; ++a) {
-        b.pw_rt[a] = (4 * x + a) * 64 + (((4 * w + grp) ^ (4 * (x & 3) + a)) << 2);
-        b.pw_kt[a] = (4 * x + a) * 64 + (((4 * w + grp) ^ ((x & 3) | (a << 2))) << 2);
+        b.pw_rt[a] = (4 * x + a) * 64 + (((4 * w + grp) ^ swz_rt(4 * x + a)) << 2);
+        b.pw_kt[a] = (4 * x + a) * 64 + (((4 * w + grp) ^ swz_kt(4 * x + a)) << 2);
         b.aw[a] = x * 64 + ((((4 * a) ^ (x & 12)) | (grp ^ (x & 3))) << 2);
-        b.tr_kt[a] = (4 * grp + (x >> 2)) * 64 + ((((4 * a) ^ (4 * (x >> 2))) | ((x & 3) ^ grp)) << 2);
+        const int row0 = 4 * grp + (x >> 2);
+        b.tr_kt[a] = row0 * 64 + (((4 * a + (x & 3)) ^ l_kt(row0)) << 2);
     }
     b.tr_v = (4 * grp + (x >> 2)) * 64 + (((2 * w + ((x & 3) >> 1)) ^ (((x >> 2) & 3) << 1)) << 3) + 4 * (x & 1);
     const int ld_row = tid >> 3;
@@ -249,13 +259,26 @@ __device__ __forceinline__ LdsBases make_bases(int tid) {
     return b;
 }
 
-// channel-contracted operand of rt / a (row 16*b + x) or kt (with ro_k)
+// channel-contracted operand of a (row 16*b + x); of rt (rt_op) and kt (kt_op)
 __device__ __forceinline__ bf16x8 row_op(const uint16_t *tile, const int (&ro)[4], int b, int kk) {
     return as_bf16x8(lds_read_b64(tile, ro[2 * kk] + 1024 * b), lds_read_b64(tile, ro[2 * kk + 1] + 1024 * b));
+}
+__device__ __forceinline__ bf16x8 rt_op(const uint16_t *tile, const int (&ro)[4], int b, int kk) {
+    return as_bf16x8(lds_read_b64(tile, (ro[2 * kk] ^ (4 * b)) + 1024 * b),
+                     lds_read_b64(tile, (ro[2 * kk + 1] ^ (4 * b)) + 1024 * b));
+}
+__device__ __forceinline__ bf16x8 kt_op(const uint16_t *tile, const int (&ro)[4], int b, int kk) {
+    return as_bf16x8(lds_read_b64(tile, (ro[2 * kk] ^ (4 * phi_kt(b))) + 1024 * b),
+                     lds_read_b64(tile, (ro[2 * kk + 1] ^ (4 * phi_kt(b))) + 1024 * b));
 }
 // token-contracted operand: lane i16 gets column n0 + i16 (base chosen by the caller)
 __device__ __forceinline__ bf16x8 col_op(const uint16_t *tile, int base, int kk) {
     return as_bf16x8(lds_read_tr(tile, base + 64 * (32 * kk)), lds_read_tr(tile, base + 64 * (32 * kk + 16)));
+}
+// the same for kt, whose swizzle also takes row bits 4-5 (= 2*kk + hh)
+__device__ __forceinline__ bf16x8 kt_col_op(const uint16_t *tile, int base, int kk) {
+    return as_bf16x8(lds_read_tr(tile, (base ^ (4 * phi_kt(2 * kk))) + 64 * (32 * kk)),
+                     lds_read_tr(tile, (base ^ (4 * phi_kt(2 * kk + 1))) + 64 * (32 * kk + 16)));
 }
 
 // Inclusive prefix sum over the 16 lanes of each DPP row.
@@ -314,10 +337,10 @@ __device__ __forceinline__ void a_tiles(SM &sm, const LdsBases &lb, const int (&
         bf16x8 k_hi[NT], k_lo[NT], r_hi[NT], r_lo[NT];
         #pragma unroll
         for (int n = 0; n < NT; ++n) {
-            k_hi[n] = row_op(sm.kt_hi, lb.ro_k, SB[n], kk);
-            k_lo[n] = row_op(sm.kt_lo, lb.ro_k, SB[n], kk);
-            r_hi[n] = row_op(sm.rt_hi, lb.ro_x, TB[n], kk);
-            r_lo[n] = row_op(sm.rt_lo, lb.ro_x, TB[n], kk);
+            k_hi[n] = kt_op(sm.kt_hi, lb.ro_k, SB[n], kk);
+            k_lo[n] = kt_op(sm.kt_lo, lb.ro_k, SB[n], kk);
+            r_hi[n] = rt_op(sm.rt_hi, lb.ro_x, TB[n], kk);
+            r_lo[n] = rt_op(sm.rt_lo, lb.ro_x, TB[n], kk);
         }
         #pragma unroll
         for (int n = 0; n < NT; ++n) a[n] = mfma(k_hi[n], r_hi[n], a[n]);
@@ -665,8 +688,8 @@ __global__ __launch_bounds__(256, 2) void wkv_chunk_kernel(Geometry g, Tensors t
                 bf16x8 k_hi[4], k_lo[4];
                 #pragma unroll
                 for (int ib = 0; ib < 4; ++ib) {
-                    k_hi[ib] = col_op(sm.kt_hi, lb.tr_kt[ib], kk);
-                    k_lo[ib] = col_op(sm.kt_lo, lb.tr_kt[ib], kk);
+                    k_hi[ib] = kt_col_op(sm.kt_hi, lb.tr_kt[ib], kk);
+                    k_lo[ib] = kt_col_op(sm.kt_lo, lb.tr_kt[ib], kk);
                 }
                 #pragma unroll
                 for (int ib = 0; ib < 4; ++ib) p[ib] = mfma(k_hi[ib], vop[kk], p[ib]);
@@ -778,8 +801,8 @@ __global__ __launch_bounds__(256, 2) void wkv_chunk_kernel(Geometry g, Tensors t
                 bf16x8 r_hi[4], r_lo[4];
                 #pragma unroll
                 for (int tb = 0; tb < 4; ++tb) {
-                    r_hi[tb] = row_op(sm.rt_hi, lb.ro_x, tb, kk);
-                    r_lo[tb] = row_op(sm.rt_lo, lb.ro_x, tb, kk);
+                    r_hi[tb] = rt_op(sm.rt_hi, lb.ro_x, tb, kk);
+                    r_lo[tb] = rt_op(sm.rt_lo, lb.ro_x, tb, kk);
                 }
                 #pragma unroll
                 for (int tb = 0; tb < 4; ++tb) acc[tb] = mfma(s_hi[kk], r_hi[tb], acc[tb]);
@@ -800,8 +823,8 @@ __global__ __launch_bounds__(256, 2) void wkv_chunk_kernel(Geometry g, Tensors t
                 bf16x8 k_hi[4], k_lo[4];
                 #pragma unroll
                 for (int ib = 0; ib < 4; ++ib) {
-                    k_hi[ib] = col_op(sm.kt_hi, lb.tr_kt[ib], kk);
-                    k_lo[ib] = col_op(sm.kt_lo, lb.tr_kt[ib], kk);
+                    k_hi[ib] = kt_col_op(sm.kt_hi, lb.tr_kt[ib], kk);
+                    k_lo[ib] = kt_col_op(sm.kt_lo, lb.tr_kt[ib], kk);
                 }
                 #pragma unroll
                 for (int ib = 0; ib < 4; ++ib) p[ib] = mfma(k_hi[ib], vop[kk], p[ib]);
