@@ -57,6 +57,23 @@ def test_step_workloads_full_size(cfg, decay, variant):
     _check(make_workload(cfg, decay=decay, variant=variant))
 
 
+@pytest.mark.parametrize("decay,variant", FORMS, ids=IDS)
+def test_single_token_ragged_steps(decay, variant):
+    """At most one token per sequence (the instantiation without look-ahead),
+    some sequences empty: their state passes through unchanged."""
+    _check(make_workload(5, lengths=[1, 0, 1, 1, 0, 1, 0], H=4, decay=decay, variant=variant))
+
+
+@pytest.mark.parametrize("decay,variant", FORMS, ids=IDS)
+def test_all_sequences_empty(decay, variant):
+    """Packed call without tokens: every state passes through bit for bit."""
+    wl = make_workload(5, lengths=[0, 0, 0], H=4, decay=decay, variant=variant)
+    log("case all-empty packed decay=%s variant=%s" % (decay, variant))
+    o, s = run_gpu(wl)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(s.cpu().numpy(), wl.state0)
+
+
 def test_step_kernel_boundary_16_and_17_tokens():
     """16 tokens take the step kernel, 17 the chunked path: both match."""
     for T in (16, 17):
