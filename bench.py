@@ -54,11 +54,11 @@ def algorithmic_bytes(cfg, tokens, n_seq, has_state_in, variant="finch"):
 # HBM traffic of the main kernel, from rocprofv3 FETCH_SIZE / WRITE_SIZE passes
 # (scaled by a plain copy of known size); valid only for the workload and the
 # kernel source the counters were taken on.  Records are kept per kernel:
-# "wkv_chunk_main" (chunked scan), "wkv_decode" (step kernel), "epilogue".
+# "wkv_chunk_main" (chunked scan), "wkv_decode" (the step kernels), "epilogue".
 def traffic_family(workload_name, kernel_name):
     if workload_name.startswith(("layernorm_heads", "gold_compress")):
         return "epilogue"
-    return "wkv_decode" if kernel_name.startswith("wkv_decode") else "wkv_chunk_main"
+    return "wkv_decode" if kernel_name.startswith(("wkv_decode", "wkv_steps")) else "wkv_chunk_main"
 
 
 def traffic_file(workload_name, kernel_name):
@@ -326,7 +326,9 @@ def main():
         t1 = time.perf_counter()
     ms_per_step = (t1 - t0) * 1e3 / args.steps
     max_len = int(np.diff(wl.cu_seqlens).max()) if wl.packed else cfg.T
-    if max_len <= STEP_MAX_T:
+    if max_len <= STEP_MAX_T and cfg.dtype == "bf16" and max_len >= 2:
+        kernel_name = "wkv_steps_mfma_kernel"
+    elif max_len <= STEP_MAX_T:
         kernel_name = "wkv_decode_kernel"
     elif cfg.dtype != "bf16":
         kernel_name = "wkv_serial_kernel"

@@ -5,7 +5,7 @@ steps that continue it."""
 import numpy as np
 import pytest
 
-from synth import make_workload
+from synth import make_workload, f32_to_bf16_bits
 from gpu_util import log, to_gpu, run_gpu, run_oracle, errors, gpu_block_error
 
 pytestmark = pytest.mark.gpu
@@ -72,6 +72,25 @@ def test_all_sequences_empty(decay, variant):
     o, s = run_gpu(wl)
     torch.cuda.synchronize()
     np.testing.assert_array_equal(s.cpu().numpy(), wl.state0)
+
+
+@pytest.mark.parametrize("decay,variant", FORMS, ids=IDS)
+def test_stiff_steps(decay, variant):
+    """16-token calls in which some items' decay products fall below 2^-96
+    (they take the token-serial path inside the matrix-core step kernel),
+    next to items without decay and items with a vanishing w."""
+    wl = make_workload(5, T=16, B=3, H=4, decay=decay, variant=variant)
+    bits = lambda x: f32_to_bf16_bits(np.float32(x)).item()
+    w = wl.w
+    if decay == "log":
+        w[0, 2:10, 1, 5] = bits(4.0)        # w = exp(-e^4) ~ 2e-24 per token
+        w[1, 7, 2, 63] = 0x7F80             # d = +inf: w = 0
+        w[2, :, 3, 17:30] = 0xFF80          # d = -inf: w = 1
+    else:
+        w[0, 2:10, 1, 5] = bits(1e-30)
+        w[1, 7, 2, 63] = 0x0001             # smallest denormal
+        w[2, :, 3, 17:30] = bits(1.0)
+    _check(wl)
 
 
 def test_step_kernel_boundary_16_and_17_tokens():
