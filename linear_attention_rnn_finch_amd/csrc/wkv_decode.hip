@@ -360,28 +360,71 @@ __global__ __launch_bounds__(64 * kWavesPerBlock, 2) void wkv_steps_mfma_kernel(
     const int nt = a.nt;                                      // 0 .. 16
     const size_t head_off = (size_t)a.h * kHeadDim;
 
-    // ---- token rows -> staging tiles (rows past the item's tokens: r, k, v, u' = 0, w = 1)
+    // ---- token rows: requested first, then the state (below), then written to
+    // the staging tiles (rows past the item's tokens: r, k, v, u' = 0, w = 1);
+    // the writes then wait for the token rows only
     uint16_t *const tiles = &sm.tile[wave][0][0];
+    const float u_lane = C2 ? 0.f : t.u[head_off + lane];   // bonus, written to LDS below
+    // Every load is unconditional (a row past the item's tokens reads its last
+    // token, or row 0 of the tensor for an empty sequence: this kernel only
+    // runs for calls with tokens) and the padding is selected at the write, so
+    // that no branch joins make the compiler wait for the loads early.
+    u32x4 rows[kStageTiles][2];
     {
-        const void *src[kStageTiles] = {t.r, t.k, t.w, t.v, C2 ? t.u2 : nullptr};
+        const void *src[kStageTiles] = {t.r, t.k, t.w, t.v, t.u2 ? t.u2 : t.v};
+        #pragma unroll
+        for (int x = 0; x < kStageTiles; ++x) {
+            if (!C2 && x == 4) continue;
+            #pragma unroll
+            for (int m = 0; m < 2; ++m) {
+                const int row = (lane >> 3) + 8 * m, piece = lane & 7;
+                const int64_t grow = nt > 0 ? a.it.t0 + (row < nt ? row : nt - 1) : 0;
+                const size_t off = ((size_t)grow * g.H + a.h) * kHeadDim + 8 * piece;
+                rows[x][m] = *reinterpret_cast<const u32x4 *>(static_cast<const uint16_t *>(src[x]) + off);
+            }
+        }
+    }
+    // ---- state, 32 x 32 accumulator tiles: S[mc][nj][4q+e] = S[32mc+8q+4h+e][32nj+i32]
+    const size_t sbase = ((size_t)a.it.n * g.H + a.h) * (kHeadDim * kHeadDim);
+    // (rows 0-31 now, rows 32-63 after the staging writes, so that the wait
+    // before those writes names the token loads exactly). The loads go
+    // through a buffer resource over this head's state: with no input state
+    // its size is zero and every load reads zero, so no branch is needed
+    // (a branch around loads makes every later wait a full drain).
+    f32x16 S[2][2];
+    const __amdgpu_buffer_rsrc_t s_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<void *>(t.state_in ? static_cast<const void *>(t.state_in + sbase) : t.r), (short)0,
+        t.state_in ? kHeadDim * kHeadDim * (int)sizeof(float) : 0, 0x00020000);
+    const int s_lane = (4 * h * kHeadDim + i32) * (int)sizeof(float);
+    auto load_rows = [&](int mc) {
+        #pragma unroll
+        for (int nj = 0; nj < 2; ++nj)
+            #pragma unroll
+            for (int r = 0; r < 16; ++r)
+                S[mc][nj][r] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                    s_rsrc, s_lane + ((32 * mc + 8 * (r >> 2) + (r & 3)) * kHeadDim + 32 * nj) * (int)sizeof(float),
+                    0, 0));
+    };
+    __builtin_amdgcn_sched_barrier(0);   // keep every token load ahead of the state loads
+    load_rows(0);
+
+    {
         constexpr unsigned kPadW = LOGD ? 0xFF80FF80u : 0x3F803F80u;   // bf16 pairs: d = -inf, or w = 1
         #pragma unroll
         for (int x = 0; x < kStageTiles; ++x) {
             if (!C2 && x == 4) continue;
             const unsigned pad = x == 2 ? kPadW : 0u;
+            const bool present = x != 4 || t.u2 != nullptr;
             #pragma unroll
             for (int m = 0; m < 2; ++m) {
                 const int row = (lane >> 3) + 8 * m, piece = lane & 7;
-                u32x4 val = {pad, pad, pad, pad};
-                if (src[x] && row < nt) {
-                    const size_t off = ((size_t)(a.it.t0 + row) * g.H + a.h) * kHeadDim + 8 * piece;
-                    val = *reinterpret_cast<const u32x4 *>(static_cast<const uint16_t *>(src[x]) + off);
-                }
+                const u32x4 val = present && row < nt ? rows[x][m] : u32x4{pad, pad, pad, pad};
                 *reinterpret_cast<u32x4 *>(tiles + x * (kDecodeMaxT * kHeadDim) + stage_off(row, 2 * piece)) = val;
             }
         }
     }
-    if (!C2) sm.u[wave][lane] = t.u[head_off + lane];
+    load_rows(1);
+    if (!C2) sm.u[wave][lane] = u_lane;
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
@@ -469,22 +512,6 @@ __global__ __launch_bounds__(64 * kWavesPerBlock, 2) void wkv_steps_mfma_kernel(
         bonus = tpad ? 0.f : bonus;
         bonus += other_half(bonus);                          // over all 64 channels
     }
-
-    // ---- state (requested only now: a stiff call never needs it here), 32 x 32
-    // accumulator tiles: S[mc][nj][4q+e] = S[32mc+8q+4h+e][32nj+i32]
-    const size_t sbase = ((size_t)a.it.n * g.H + a.h) * (kHeadDim * kHeadDim);
-    f32x16 S[2][2] = {{f32x16{}, f32x16{}}, {f32x16{}, f32x16{}}};
-    if (t.state_in) {
-        const float *src = t.state_in + sbase + 4 * h * kHeadDim + i32;
-        #pragma unroll
-        for (int mc = 0; mc < 2; ++mc)
-            #pragma unroll
-            for (int nj = 0; nj < 2; ++nj)
-                #pragma unroll
-                for (int r = 0; r < 16; ++r)
-                    S[mc][nj][r] = src[(32 * mc + 8 * (r >> 2) + (r & 3)) * kHeadDim + 32 * nj];
-    }
-
 
     // ---- token-major operands, one K step (16 channels) at a time: lane (i32, h)
     // is token tt = i32 % 16 (lanes with i32 >= 16 are padding rows of the
