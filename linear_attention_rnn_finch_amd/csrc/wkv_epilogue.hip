@@ -124,7 +124,7 @@ constexpr int kCmpRows = 32;      // tokens per workgroup (two 16-token tiles)
 constexpr int kCmpCols = 64;      // outputs per workgroup (four 16-output tiles)
 constexpr int kCmpK = 256;        // d_model slice staged through LDS per step
 constexpr int kCmpPitch = kCmpK + 8;                     // LDS row pitch in bf16 (528 B)
-constexpr int kCmpThreads = 1024; // sixteen waves: two per 16 x 16 output tile
+constexpr int kCmpThreads = 512;  // eight waves: 32 tokens x 32 outputs each, a quarter of every slice
 constexpr int kCmpXLoads = kCmpRows * kCmpK / 8 / kCmpThreads;   // 16-byte pieces per thread and step: 1
 constexpr int kCmpWLoads = kCmpCols * kCmpK / 8 / kCmpThreads;   // 2
 
@@ -147,11 +147,11 @@ __device__ __forceinline__ f32x4 mfma(bf16x8 a, bf16x8 b, f32x4 c) {
 // read its 512 contiguous bytes; a load that names a row as a 16-byte piece
 // per lane per MFMA operand would fetch 16 half lines per instruction), two
 // slices ahead of the arithmetic, and written to LDS rows of 528 bytes, whose
-// 16-byte shift per row keeps the operand reads free of bank conflicts.  Waves
-// v and v + 8 share the 16 x 16 tile of tokens m0 + 16 (v / 4 % 2) and
-// outputs n0 + 16 (v % 4), each taking half of every slice; their two partial
-// tiles are added through LDS at the end.  Four waves per SIMD hide the LDS
-// and barrier latency.
+// 16-byte shift per row keeps the operand reads free of bank conflicts.  Wave
+// v computes all 32 tokens against outputs n0 + 32 (v % 2) .. + 31 (2 x 2
+// tiles of 16 x 16, each operand read once for two products) over the
+// quarter v / 2 of every slice; the four quarters' partial tiles are added
+// through LDS at the end.
 template <bool OutBf16>
 __global__ __launch_bounds__(kCmpThreads) void gold_compress_kernel(const uint16_t *x, const uint16_t *w, void *c,
                                                                     int64_t M, int K, int N) {
@@ -196,21 +196,26 @@ __global__ __launch_bounds__(kCmpThreads) void gold_compress_kernel(const uint16
         for (int j = 0; j < kCmpWLoads; ++j) *reinterpret_cast<u32x4 *>(&sm.w[buf][0][0] + wl[j]) = P.w[j];
     };
     // MFMA operands: lane (i16, grp) takes d_model slots 32u + 8grp .. +7 of
-    // weight row 16nt + i16 (A) and of token row 16mt + i16 (B), for the four
-    // substeps u of this wave's half of the slice
-    const int tile = wave & 7, half = wave >> 3;
-    const int mt = tile >> 2, nt = tile & 3;
-    f32x4 acc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};   // even/odd substeps
+    // weight rows 32nh + 16a + i16 (A) and of token rows 16b + i16 (B), for
+    // the two substeps u of this wave's quarter of the slice
+    const int nh = wave & 1, kq = wave >> 1;
+    f32x4 acc[2][2] = {{f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}},
+                       {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}}};
     auto compute = [&](int buf) {
-        bf16x8 a[4], b[4];
         #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const int k = 32 * (4 * half + u) + 8 * grp;
-            a[u] = *reinterpret_cast<const bf16x8 *>(&sm.w[buf][16 * nt + i16][k]);
-            b[u] = *reinterpret_cast<const bf16x8 *>(&sm.x[buf][16 * mt + i16][k]);
+        for (int u = 2 * kq; u < 2 * kq + 2; ++u) {
+            const int k = 32 * u + 8 * grp;
+            bf16x8 a[2], b[2];
+            #pragma unroll
+            for (int t = 0; t < 2; ++t) {
+                a[t] = *reinterpret_cast<const bf16x8 *>(&sm.w[buf][32 * nh + 16 * t + i16][k]);
+                b[t] = *reinterpret_cast<const bf16x8 *>(&sm.x[buf][16 * t + i16][k]);
+            }
+            #pragma unroll
+            for (int ta = 0; ta < 2; ++ta)
+                #pragma unroll
+                for (int tb = 0; tb < 2; ++tb) acc[ta][tb] = mfma(a[ta], b[tb], acc[ta][tb]);
         }
-        #pragma unroll
-        for (int u = 0; u < 4; ++u) acc[u & 1] = mfma(a[u], b[u], acc[u & 1]);
     };
 
     // two register sets: while slice s is computed from LDS, slice s + 1 is
@@ -232,17 +237,23 @@ __global__ __launch_bounds__(kCmpThreads) void gold_compress_kernel(const uint16
         __syncthreads();
     }
 
-    // the second half's partial tiles, through LDS (the operand buffers are
-    // free after the last barrier)
-    f32x4 *part = reinterpret_cast<f32x4 *>(&sm.x[0][0][0]);   // [tile][lane]: 8 KB
-    if (half) part[tile * 64 + lane] = acc[0] + acc[1];
+    // the four quarters' partial tiles, through LDS (the operand buffers are
+    // free after the last barrier): part[kq][nh][tile][lane], then wave v adds
+    // the quarters of tile v / 2 of output half v % 2 and stores it
+    f32x4 *part = reinterpret_cast<f32x4 *>(&sm.x[0][0][0]);   // 32 KB
+    #pragma unroll
+    for (int ta = 0; ta < 2; ++ta)
+        #pragma unroll
+        for (int tb = 0; tb < 2; ++tb) part[((kq * 2 + nh) * 4 + 2 * ta + tb) * 64 + lane] = acc[ta][tb];
     __syncthreads();
-    if (half) return;
-    // acc layout: value e of lane (i16, grp) is c[m0 + 16mt + i16][n0 + 16nt + 4grp + e]
-    const f32x4 sum = acc[0] + acc[1] + part[tile * 64 + lane];
-    const int64_t m = m0 + 16 * mt + i16;
+    const int tile = wave >> 1, ta = tile >> 1, tb = tile & 1;
+    f32x4 sum = part[((0 * 2 + nh) * 4 + tile) * 64 + lane];
+    #pragma unroll
+    for (int q = 1; q < 4; ++q) sum += part[((q * 2 + nh) * 4 + tile) * 64 + lane];
+    // acc layout: value e of lane (i16, grp) is c[m0 + 16tb + i16][n0 + 32nh + 16ta + 4grp + e]
+    const int64_t m = m0 + 16 * tb + i16;
     if (m < M) {
-        const size_t at = (size_t)m * N + n0 + 16 * nt + 4 * grp;
+        const size_t at = (size_t)m * N + n0 + 32 * nh + 16 * ta + 4 * grp;
         if (OutBf16)
             *reinterpret_cast<bf16x4 *>(static_cast<uint16_t *>(c) + at) = __builtin_convertvector(sum, bf16x4);
         else
