@@ -37,6 +37,16 @@ def test_short_steps_with_state(decay, variant, T):
 
 
 @pytest.mark.parametrize("decay,variant", FORMS, ids=IDS)
+@pytest.mark.parametrize("T", [2, 9, 16])
+def test_steps_without_initial_state(decay, variant, T):
+    """bf16 steps of 2-16 tokens with no initial state (state_in NULL: the
+    state starts at zero)."""
+    wl = make_workload(1, T=T, B=5, H=3, decay=decay, variant=variant)
+    assert wl.state0 is None
+    _check(wl)
+
+
+@pytest.mark.parametrize("decay,variant", FORMS, ids=IDS)
 @pytest.mark.parametrize("T", [1, 16])
 def test_f32_steps(decay, variant, T):
     wl = make_workload(0, T=T, B=2, H=3, decay=decay, variant=variant)
