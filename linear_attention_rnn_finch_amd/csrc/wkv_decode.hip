@@ -34,7 +34,7 @@
 namespace finch {
 namespace {
 
-constexpr int kWavesPerBlock = 4;
+constexpr int kWavesPerBlock = 1;   // token-serial kernel: one wave per workgroup (no barrier, no LDS)
 constexpr int kAhead = 4;   // tokens whose inputs are in flight ahead of the one computed
 
 __device__ inline float to_f32(float x) { return x; }
@@ -281,11 +281,14 @@ using lds_i16x4 = __attribute__((address_space(3))) i16x4;
 
 constexpr float kMinStepDecay = 0x1p-96f;   // smaller decay products take the token-serial path
 constexpr int kStageTiles = 5;               // r, k, w (or d), v, u'
+// One wave per workgroup: the kernel has no workgroup barrier, and a lone
+// wave's slot is released as soon as it ends (eight per CU, two per SIMD).
+constexpr int kStepWaves = 1;
 
 struct StepSmem {
-    uint16_t tile[kWavesPerBlock][kStageTiles][kDecodeMaxT * kHeadDim];   // per wave: 16 token rows per input
-    float dec[kWavesPerBlock][kHeadDim];                                  // P_15 per key channel
-    float u[kWavesPerBlock][kHeadDim];                                    // bonus u of the item's head
+    uint16_t tile[kStepWaves][kStageTiles][kDecodeMaxT * kHeadDim];   // per wave: 16 token rows per input
+    float dec[kStepWaves][kHeadDim];                                  // P_15 per key channel
+    float u[kStepWaves][kHeadDim];                                    // bonus u of the item's head
 };
 
 __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
@@ -348,12 +351,12 @@ __device__ __forceinline__ void decay_and_key(float x, float &w, float &k) {
 }
 
 template <bool LOGD, bool C2>
-__global__ __launch_bounds__(64 * kWavesPerBlock, 2) void wkv_steps_mfma_kernel(Geometry g, Tensors t) {
+__global__ __launch_bounds__(64 * kStepWaves, 2) void wkv_steps_mfma_kernel(Geometry g, Tensors t) {
     __shared__ StepSmem sm;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
     const int i32 = lane & 31, h = lane >> 5;
-    const int64_t item = (int64_t)blockIdx.x * kWavesPerBlock + wave;
+    const int64_t item = (int64_t)blockIdx.x * kStepWaves + wave;
     if (item >= (int64_t)g.n_seg * g.H) return;             // whole wave: no barrier below
     const Item a = item_at(g, item, lane >> 4, lane & 15);
     if (!a.ok) return;
@@ -663,7 +666,8 @@ hipError_t launch_decode(const Geometry &g, const Tensors &t, bool bf16, Variant
     const dim3 grid((unsigned)((items + kWavesPerBlock - 1) / kWavesPerBlock)), block(64 * kWavesPerBlock);
     if (bf16 && max_len >= 2) {
         auto kern = v.log_decay ? steps_kernel_for<true>(v.c2) : steps_kernel_for<false>(v.c2);
-        hipExtLaunchKernelGGL(kern, grid, block, 0, st, tm.start, tm.stop, 0, g, t);
+        const dim3 sgrid((unsigned)((items + kStepWaves - 1) / kStepWaves)), sblock(64 * kStepWaves);
+        hipExtLaunchKernelGGL(kern, sgrid, sblock, 0, st, tm.start, tm.stop, 0, g, t);
     } else if (bf16)
         hipExtLaunchKernelGGL(decode_kernel_for<uint16_t>(v, max_len), grid, block, 0, st, tm.start, tm.stop, 0, g,
                               t);
