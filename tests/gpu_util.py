@@ -8,7 +8,7 @@ import sys
 import numpy as np
 
 import oracle
-from synth import max_block_error, select_heads
+from synth import error_report, select_heads
 
 
 def log(msg):
@@ -76,14 +76,31 @@ def _host(x, heads, axis):
     return x
 
 
+class Errors(tuple):
+    """(normwise o error, normwise state error), the pass measures, with the
+    per-row errors (``row_o``, ``row_s``) and both full reports attached."""
+
+    def __new__(cls, rep_o, rep_s):
+        self = super().__new__(cls, (rep_o["block"], rep_s["block"]))
+        self.rep_o, self.rep_s = rep_o, rep_s
+        self.row_o, self.row_s = rep_o["row"], rep_s["row"]
+        return self
+
+
 def errors(wl, o_gpu, s_gpu, o_ref, s_ref, heads=None):
-    """Max normwise block errors (o, state); with ``heads``, the references
-    hold only those heads and the GPU results are reduced to them."""
-    eo = 0.0
+    """Error reports of (o, state) against the oracle (synth.compare): the
+    normwise block errors unpack as a pair; per-row and floored element-wise
+    errors are logged and attached.  With ``heads``, the references hold only
+    those heads and the GPU results are reduced to them."""
+    empty = {"block": 0.0, "row": 0.0, "elem_floored": 0.0, "worst_row": None}
+    rep_o = empty
     if o_ref is not None:
-        eo = max_block_error(_host(o_gpu, heads, -2), o_ref, wl.cu_seqlens)
-    es = max_block_error(_host(s_gpu, heads, 1), s_ref, kind="state")
-    return eo, es
+        rep_o = error_report(_host(o_gpu, heads, -2), o_ref, wl.cu_seqlens, heads=heads)
+    rep_s = error_report(_host(s_gpu, heads, 1), s_ref, kind="state", heads=heads)
+    log("  o: block %.3e row %.3e elem(floored) %.3e worst row %s | state: block %.3e row %.3e"
+        % (rep_o["block"], rep_o["row"], rep_o["elem_floored"], rep_o["worst_row"],
+           rep_s["block"], rep_s["row"]))
+    return Errors(rep_o, rep_s)
 
 
 def gpu_block_error(a, b, dims):

@@ -26,10 +26,14 @@ def _check(wl, heads=None, tol=None, g=None, **kw):
     o, s = run_gpu(wl, g, **kw)
     torch.cuda.synchronize()
     o_ref, s_ref = run_oracle(wl, heads)
-    eo, es = errors(wl, o, s, o_ref, s_ref, heads)
+    err = errors(wl, o, s, o_ref, s_ref, heads)
+    eo, es = err
     log("  err o=%.3e state=%.3e (tol %.0e)" % (eo, es, tol))
     assert np.isfinite(eo) and np.isfinite(es)
     assert eo <= tol and es <= tol, (eo, es)
+    # per-row errors (floored denominators) within the same bound: an error
+    # confined to a few rows of a long block cannot hide behind its maximum
+    assert err.row_o <= tol and err.row_s <= tol, (err.row_o, err.row_s)
     return o, s
 
 
@@ -190,16 +194,40 @@ def test_train_batch_full_size():
     _check(make_workload(2))
 
 
-@pytest.mark.timeout(900)
+def _check_head_batches(wl, results, batch=8):
+    """Every head of a large workload against the oracle, ``batch`` heads at a
+    time (the oracle's fp64 outputs of all heads together would not fit the
+    host comfortably).  ``results`` maps a label to GPU (o, state_out)."""
+    tol = wl.config.tolerance
+    H = wl.u.shape[0]
+    worst = {label: [0.0, 0.0, 0.0, 0.0] for label in results}
+    for h0 in range(0, H, batch):
+        heads = list(range(h0, min(H, h0 + batch)))
+        o_ref, s_ref = run_oracle(wl, heads)
+        for label, (o, s) in results.items():
+            log("  %s heads %d..%d" % (label, heads[0], heads[-1]))
+            err = errors(wl, o, s, o_ref, s_ref, heads)
+            eo, es = err
+            worst[label] = [max(a, b) for a, b in zip(worst[label], (eo, es, err.row_o, err.row_s))]
+            assert np.isfinite(eo) and np.isfinite(es)
+            assert eo <= tol and es <= tol, (label, heads, eo, es)
+            assert err.row_o <= tol and err.row_s <= tol, (label, heads, err.row_o, err.row_s)
+        del o_ref, s_ref
+    for label, (eo, es, ro, rs) in worst.items():
+        log("  %s, all %d heads: block o=%.3e state=%.3e row o=%.3e state=%.3e"
+            % (label, H, eo, es, ro, rs))
+
+
+@pytest.mark.timeout(1200)
 def test_long_context_full_size_and_8_segment_chain():
-    """T=262144, H=64 with random fp32 initial states: sampled heads against the
-    oracle, and the same sequence run as 8 consecutive carried-state calls
-    against both the oracle and the single call (every head)."""
+    """T=262144, H=64 with random fp32 initial states: every head against the
+    oracle (in batches of heads), and the same sequence run as 8 consecutive
+    carried-state calls against both the oracle and the single call."""
     import linear_attention_rnn_finch_amd as fw
     wl = make_workload(3)
-    heads = [0, 29, 63]
     g = to_gpu(wl)
-    o_full, s_full = _check(wl, heads=heads, g=g)
+    log("case %s single call" % wl.config.name)
+    o_full, s_full = run_gpu(wl, g)
     B, T, H, D = g["r"].shape
     o_chain = torch.empty_like(o_full)
     state = g["state0"].clone()
@@ -215,18 +243,19 @@ def test_long_context_full_size_and_8_segment_chain():
     e_s = gpu_block_error(state, s_full, (2, 3))
     log("  chain vs single call: o=%.3e state=%.3e" % (e_o, e_s))
     assert e_o <= tol and e_s <= tol
-    o_ref, s_ref = run_oracle(wl, heads)
-    eo, es = errors(wl, o_chain, state, o_ref, s_ref, heads)
-    log("  chain vs oracle: o=%.3e state=%.3e" % (eo, es))
-    assert eo <= tol and es <= tol
+    del g
+    _check_head_batches(wl, {"single call": (o_full, s_full), "8-call chain": (o_chain, state)})
 
 
-@pytest.mark.timeout(600)
+@pytest.mark.timeout(900)
 def test_ragged_full_size():
-    """16 packed sequences of U{1024..32768} tokens, own initial states: all
-    sequences, sampled heads."""
+    """16 packed sequences of U{1024..32768} tokens, own initial states: every
+    sequence and every head against the oracle (in batches of heads)."""
     wl = make_workload(4)
-    _check(wl, heads=[0, 13, 31])
+    log("case %s tokens=%d" % (wl.config.name, wl.tokens))
+    o, s = run_gpu(wl)
+    torch.cuda.synchronize()
+    _check_head_batches(wl, {"packed call": (o, s)})
 
 
 def _stiff_workload(T, H):

@@ -250,3 +250,110 @@ def test_generator_distributions():
     assert len(L) == 16 and L.min() >= 1024 and L.max() <= 32768
     wl4 = make_workload(4, lengths=[3, 5], H=2)
     assert wl4.state0.shape == (2, 2, 64, 64) and wl4.r.shape == (8, 2, 64)
+
+
+# ---- bf16 input decoding ----------------------------------------------------
+# Every bf16 value the oracle sees passes through its decoders (the C one in
+# wkv_oracle.c and oracle.bf16_bits_to_f64).  They are pinned here against
+# torch's own bfloat16 -> float64 conversion on all 65536 bit patterns.
+
+def _torch_bf16_table():
+    torch = pytest.importorskip("torch")
+    bits = torch.arange(65536, dtype=torch.int32).to(torch.int16)
+    return bits.view(torch.bfloat16).to(torch.float64).numpy()
+
+
+def _same_values(got, ref, signed_zero=True, rtol=0.0):
+    got = np.asarray(got, dtype=np.float64)
+    nan = np.isnan(ref)
+    np.testing.assert_array_equal(np.isnan(got), nan)
+    if rtol:
+        np.testing.assert_allclose(got[~nan], ref[~nan], rtol=rtol, atol=0)
+    else:
+        np.testing.assert_array_equal(got[~nan], ref[~nan])
+    if signed_zero:                     # the table holds +0 and -0
+        zero = ref == 0
+        np.testing.assert_array_equal(np.signbit(got[zero]), np.signbit(ref[zero]))
+
+
+def test_python_bf16_decoder_all_patterns():
+    ref = _torch_bf16_table()
+    _same_values(oracle.bf16_bits_to_f64(np.arange(65536, dtype=np.uint32).astype(np.uint16)), ref)
+
+
+@pytest.mark.parametrize("role", ["r", "k", "v", "w", "d", "u2"])
+def test_c_oracle_decodes_every_bf16_pattern(role):
+    """One token, D = 1, one head per bit pattern, so that o (or the state)
+    equals the decoded value of the pattern under test in the given role:
+      r, k, v: o = r (S_0 + u k v) with the other two = 1, u = 1, S_0 = 0;
+      w:       state = w S_0 + k v with S_0 = 1, k = 0;
+      d:       the same with w = exp(-exp(d)) (decay given as d);
+      u2:      Finch-C2 o = r S_0 + u' with r = 0."""
+    ref = _torch_bf16_table()
+    H = 65536
+    pat = np.arange(H, dtype=np.uint32).astype(np.uint16).reshape(1, 1, H, 1)
+    one = np.full_like(pat, 0x3F80)
+    zero = np.zeros_like(pat)
+    u = np.ones((H, 1), dtype=np.float32)
+    args = dict(r=one, k=one, v=one, w=one)
+    s0 = None
+    kw = {}
+    if role in ("r", "k", "v"):
+        args[role] = pat
+    elif role in ("w", "d"):
+        args["w"], args["k"] = pat, zero
+        s0 = np.ones((1, H, 1, 1))
+        if role == "d":
+            kw["decay"] = "log"
+    else:
+        args["r"] = zero
+        kw.update(variant="c2", second_value=pat)
+    o, s = oracle.wkv_scan(args["r"], args["k"], args["v"], args["w"], u, s0, **kw)
+    if role in ("w", "d"):
+        got = s.reshape(H)
+        if role == "d":
+            with np.errstate(over="ignore", invalid="ignore"):
+                ref = np.exp(-np.exp(ref))
+        # exp() of the C library and of numpy may differ in the last bit, and
+        # exp(-x) multiplies the relative error of x = exp(d) by x
+        _same_values(got, ref, signed_zero=False, rtol=1e-12 if role == "d" else 0.0)
+    else:
+        # the read-out sums onto +0, so the sign of a zero is not observable
+        _same_values(o.reshape(H), ref, signed_zero=False)
+
+
+def _bf16_fixture(name):
+    """A hand-worked fixture whose values are all exact in bf16, as bf16 bit
+    patterns (the encoding round-trips exactly, which is checked)."""
+    g = json.load(open(os.path.join(GOLDEN, name)))
+    enc = {}
+    for key in ("r", "k", "v", "w", "u2"):
+        if key in g:
+            x = np.array(g[key], dtype=np.float32)
+            bits = f32_to_bf16_bits(x)
+            np.testing.assert_array_equal(bf16_bits_to_f32(bits), x)
+            enc[key] = bits
+    return g, enc
+
+
+def test_hand_worked_fixture_in_bf16():
+    g, b = _bf16_fixture("hand_worked_d2_t3.json")
+    f = lambda key: np.array(g[key], dtype=np.float32)
+    o, s = scan1(b["r"], b["k"], b["v"], b["w"], f("u"), f("state0"))
+    np.testing.assert_array_equal(o, np.array(g["o"]))
+    np.testing.assert_array_equal(s, np.array(g["state_final"]))
+    o2, s2 = oracle.wkv_sum_form(b["r"], b["k"], b["v"], b["w"], f("u"), f("state0"))
+    np.testing.assert_array_equal(o2, np.array(g["o"]))
+    np.testing.assert_array_equal(s2, np.array(g["state_final"]))
+
+
+def test_c2_hand_worked_fixture_in_bf16():
+    g, b = _bf16_fixture("hand_worked_c2_d2_t3.json")
+    D = 2
+    T = len(g["r"])
+    add = lambda a: a.reshape(1, T, 1, D)
+    s0 = np.array(g["state0"], dtype=np.float64).reshape(1, 1, D, D)
+    o, s = oracle.wkv_scan(add(b["r"]), add(b["k"]), add(b["v"]), add(b["w"]), None, s0,
+                           variant="c2", second_value=add(b["u2"]))
+    np.testing.assert_array_equal(o.reshape(T, D), np.array(g["o"]))
+    np.testing.assert_array_equal(s.reshape(D, D), np.array(g["state_final"]))
