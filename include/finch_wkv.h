@@ -63,7 +63,7 @@
 extern "C" {
 #endif
 
-#define FINCH_WKV_ABI_VERSION 2
+#define FINCH_WKV_ABI_VERSION 3
 
 typedef enum {
     WKV_OK = 0,
@@ -95,7 +95,11 @@ typedef enum {
      * library applies; there is no static bonus (u is ignored and may be
      * NULL); u2 = second_value is the data-dependent second value u'_t, or
      * NULL for none (the pages' ablation without it). */
-    WKV_FLAG_FINCH_C2 = 2
+    WKV_FLAG_FINCH_C2 = 2,
+    /* o is written as bf16, each value rounded to nearest even from the fp32
+     * result (the layout is unchanged: [.., H, D], 2 bytes per element).
+     * state_out stays fp32.  Without the flag o is fp32. */
+    WKV_FLAG_OUT_BF16 = 4
 } wkv_flag_t;
 
 /* FINCH_WKV_ABI_VERSION of the loaded library. */
@@ -123,7 +127,9 @@ size_t wkv_prefill_workspace_bytes(int B, int T, int H, int D, wkv_dtype_t in_dt
  *   state_in    device, [B, H, D, D] fp32, or NULL (start from zeros)
  *   o           device, [B, T, H, D] fp32 (output; may be NULL only if T == 0)
  *   state_out   device, [B, H, D, D] fp32 (output), or NULL (not written)
- *   B >= 1, 1 <= H <= 65536, T >= 0, D == 64
+ *   B >= 1, 1 <= H <= 65536, T >= 0, D == 64; sizes whose launch would exceed
+ *   2^32 - 1 work-items in one grid dimension are rejected with
+ *   WKV_EUNSUPPORTED (e.g. more than 2^24 - 1 (segment, head) work items)
  *   workspace   device scratch of at least wkv_prefill_workspace_bytes(...)
  *               bytes (NULL allowed when that is 0), 256-byte aligned
  *   stream      hipStream_t to enqueue on
@@ -173,6 +179,8 @@ wkv_status_t wkv_prefill_varlen(const void *r, const void *k, const void *v,
  *                 ignored, may be NULL)
  *   second_value  with WKV_FLAG_FINCH_C2: u'_t, same layout and type as r, or
  *                 NULL (no second value); without the flag it must be NULL
+ *   o             fp32, or bf16 with WKV_FLAG_OUT_BF16 (then [.., H, D] of
+ *                 2-byte elements, 16-byte aligned)
  *   flags         unknown bits -> WKV_EUNSUPPORTED
  * Everything else (layouts, workspace size, aliasing, errors, T == 0, ragged
  * offsets) is exactly as for wkv_prefill / wkv_prefill_varlen, whose
@@ -181,7 +189,7 @@ wkv_status_t wkv_prefill_varlen(const void *r, const void *k, const void *v,
  */
 wkv_status_t wkv_prefill_ex(const void *r, const void *k, const void *v,
                             const void *decay, const float *u, const void *second_value,
-                            const float *state_in, float *o, float *state_out,
+                            const float *state_in, void *o, float *state_out,
                             int B, int T, int H, int D, wkv_dtype_t in_dtype,
                             unsigned flags, void *workspace, size_t workspace_bytes,
                             void *stream);
@@ -191,7 +199,7 @@ wkv_status_t wkv_prefill_varlen_ex(const void *r, const void *k, const void *v,
                                    const void *second_value,
                                    const int32_t *cu_seqlens_dev,
                                    const int32_t *cu_seqlens_host, int N,
-                                   const float *state_in, float *o, float *state_out,
+                                   const float *state_in, void *o, float *state_out,
                                    int H, int D, wkv_dtype_t in_dtype, unsigned flags,
                                    void *workspace, size_t workspace_bytes,
                                    void *stream);

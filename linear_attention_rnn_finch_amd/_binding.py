@@ -18,7 +18,7 @@ LIBRARY_PATH = os.path.join(_PKG, "libfinch_wkv.so")
 
 WKV_OK, WKV_EINVAL, WKV_EUNSUPPORTED, WKV_EWORKSPACE, WKV_EHIP = range(5)
 WKV_F32, WKV_BF16 = 0, 1
-WKV_FLAG_DECAY_LOG, WKV_FLAG_FINCH_C2 = 1, 2
+WKV_FLAG_DECAY_LOG, WKV_FLAG_FINCH_C2, WKV_FLAG_OUT_BF16 = 1, 2, 4
 HEAD_DIM = 64
 DECAYS = ("w", "log")            # decay argument holds w_t, or d_t with w_t = exp(-exp(d_t))
 VARIANTS = ("finch", "c2")       # base Finch (bonus u) or the Finch-C2 time mixer
@@ -115,13 +115,17 @@ def varlen_workspace_bytes(cu_seqlens_host, H: int, D: int = HEAD_DIM, dtype=tor
     return int(_lib.wkv_prefill_varlen_workspace_bytes(cu.data_ptr(), cu.numel() - 1, H, D, code))
 
 
-def _flags(decay, variant, u, second_value, r):
+def _flags(decay, variant, u, second_value, r, out_dtype=torch.float32):
     """Flags word of the extended entry points; checks u / second_value."""
+    if out_dtype not in (torch.float32, torch.bfloat16):
+        raise TypeError("out_dtype must be torch.float32 or torch.bfloat16")
     if decay not in DECAYS:
         raise ValueError("decay must be one of %s" % (DECAYS,))
     if variant not in VARIANTS:
         raise ValueError("variant must be one of %s" % (VARIANTS,))
     flags = (WKV_FLAG_DECAY_LOG if decay == "log" else 0) | (WKV_FLAG_FINCH_C2 if variant == "c2" else 0)
+    if out_dtype == torch.bfloat16:
+        flags |= WKV_FLAG_OUT_BF16
     if variant == "c2":
         if second_value is not None:
             _device_tensor("second_value", second_value, r.dtype)
@@ -134,21 +138,48 @@ def _flags(decay, variant, u, second_value, r):
     return flags
 
 
-def _workspace(nbytes, device, given):
+def _on_stream(stream):
+    """Context in which the binding allocates: the stream the kernels run on.
+    The caching allocator then ties every block it hands out here (outputs,
+    workspace) to that stream, so no other work can be given the block while
+    the kernels still use it."""
+    import contextlib
+    return contextlib.nullcontext() if stream is None else torch.cuda.stream(stream)
+
+
+def _workspace(nbytes, device, given, stream):
+    """The caller's workspace (checked), or a new one on the kernels' stream."""
     if nbytes == 0:
         return None, 0
     if given is not None:
+        _device_tensor("workspace", given)
+        if given.device != device:
+            raise ValueError("workspace must be on %s, got %s" % (device, given.device))
         return given, given.numel() * given.element_size()
-    return torch.empty(nbytes, dtype=torch.uint8, device=device), nbytes
+    with _on_stream(stream):
+        return torch.empty(nbytes, dtype=torch.uint8, device=device), nbytes
+
+
+def _check_outputs(o, state_out, o_shape, s_shape, out_dtype):
+    if o is not None:
+        _device_tensor("o", o, out_dtype)
+        if tuple(o.shape) != o_shape:
+            raise ValueError("o must be %s, got %s" % (o_shape, tuple(o.shape)))
+    if state_out is not None:
+        _device_tensor("state_out", state_out, torch.float32)
+        if tuple(state_out.shape) != s_shape:
+            raise ValueError("state_out must be %s, got %s" % (s_shape, tuple(state_out.shape)))
 
 
 def prefill(r, k, v, w, u, state_in=None, *, o=None, state_out=None, want_state=True,
-            workspace=None, stream=None, decay="w", variant="finch", second_value=None):
+            workspace=None, stream=None, decay="w", variant="finch", second_value=None,
+            out_dtype=torch.float32):
     """Finch WKV pre-fill of a fixed-length batch on the GPU.
 
     r, k, v, w: [B, T, H, 64] bfloat16 (or float32), contiguous, same device.
     u: [H, 64] float32.  state_in: [B, H, 64, 64] float32 or None (zeros).
-    Returns (o [B, T, H, 64] float32, state_out [B, H, 64, 64] float32 or None).
+    Returns (o [B, T, H, 64] in ``out_dtype`` (float32, or bfloat16 rounded
+    to nearest even), state_out [B, H, 64, 64] float32 or None).
     ``state_out`` may be ``state_in`` (carried state, updated in place).
     ``decay="log"``: w holds d with w = exp(-exp(d)).  ``variant="c2"``: the
     Finch-C2 mixer (k is taken before its (1 - w) factor, u is unused and may
@@ -162,7 +193,7 @@ def prefill(r, k, v, w, u, state_in=None, *, o=None, state_out=None, want_state=
     for name, t in (("k", k), ("v", v), ("w", w)):
         if t.shape != r.shape:
             raise ValueError("%s shape %s != r shape %s" % (name, tuple(t.shape), tuple(r.shape)))
-    flags = _flags(decay, variant, u, second_value, r)
+    flags = _flags(decay, variant, u, second_value, r, out_dtype)
     if variant == "finch" and tuple(u.shape) != (H, D):
         raise ValueError("u must be [H, D] = %s" % ((H, D),))
     if variant == "c2":
@@ -172,20 +203,14 @@ def prefill(r, k, v, w, u, state_in=None, *, o=None, state_out=None, want_state=
         if tuple(state_in.shape) != (B, H, D, D):
             raise ValueError("state_in must be [B, H, D, D]")
     code = _dtype_code(r)
-    if o is None:
-        o = torch.empty((B, T, H, D), dtype=torch.float32, device=r.device)
-    else:
-        _device_tensor("o", o, torch.float32)
-        if tuple(o.shape) != (B, T, H, D):
-            raise ValueError("o must be [B, T, H, D]")
-    if state_out is None and want_state:
-        state_out = torch.empty((B, H, D, D), dtype=torch.float32, device=r.device)
-    elif state_out is not None:
-        _device_tensor("state_out", state_out, torch.float32)
-        if tuple(state_out.shape) != (B, H, D, D):
-            raise ValueError("state_out must be [B, H, D, D]")
+    _check_outputs(o, state_out, (B, T, H, D), (B, H, D, D), out_dtype)
+    with _on_stream(stream):
+        if o is None:
+            o = torch.empty((B, T, H, D), dtype=out_dtype, device=r.device)
+        if state_out is None and want_state:
+            state_out = torch.empty((B, H, D, D), dtype=torch.float32, device=r.device)
     need = int(_lib.wkv_prefill_workspace_bytes(B, T, H, D, code))
-    ws, ws_bytes = _workspace(need, r.device, workspace)
+    ws, ws_bytes = _workspace(need, r.device, workspace, stream)
     with torch.cuda.device(r.device):
         status = _lib.wkv_prefill_ex(_ptr(r), _ptr(k), _ptr(v), _ptr(w), _ptr(u),
                                      _ptr(second_value), _ptr(state_in), _ptr(o),
@@ -197,13 +222,14 @@ def prefill(r, k, v, w, u, state_in=None, *, o=None, state_out=None, want_state=
 
 def prefill_varlen(r, k, v, w, u, cu_seqlens, state_in=None, *, cu_seqlens_host=None, o=None,
                    state_out=None, want_state=True, workspace=None, stream=None, decay="w",
-                   variant="finch", second_value=None):
+                   variant="finch", second_value=None, out_dtype=torch.float32):
     """Finch WKV pre-fill of N packed sequences.
 
     r, k, v, w: [total_tokens, H, 64]; cu_seqlens: [N + 1] int32 offsets on the
     GPU; cu_seqlens_host: the same offsets on the host (copied from the device,
     with a synchronisation, when omitted).  state_in/state_out: [N, H, 64, 64].
-    ``decay``, ``variant`` and ``second_value`` as for ``prefill``.
+    ``decay``, ``variant``, ``second_value`` and ``out_dtype`` as for
+    ``prefill``.
     """
     for name, t in (("r", r), ("k", k), ("v", v), ("w", w)):
         _device_tensor(name, t, r.dtype)
@@ -213,7 +239,9 @@ def prefill_varlen(r, k, v, w, u, cu_seqlens, state_in=None, *, cu_seqlens_host=
     for name, t in (("k", k), ("v", v), ("w", w)):
         if t.shape != r.shape:
             raise ValueError("%s shape differs from r" % name)
-    flags = _flags(decay, variant, u, second_value, r)
+    flags = _flags(decay, variant, u, second_value, r, out_dtype)
+    if variant == "finch" and tuple(u.shape) != (H, D):
+        raise ValueError("u must be [H, D] = %s" % ((H, D),))
     if variant == "c2":
         u = None
     _device_tensor("cu_seqlens", cu_seqlens, torch.int32)
@@ -230,12 +258,14 @@ def prefill_varlen(r, k, v, w, u, cu_seqlens, state_in=None, *, cu_seqlens_host=
         if tuple(state_in.shape) != (N, H, D, D):
             raise ValueError("state_in must be [N, H, D, D]")
     code = _dtype_code(r)
-    if o is None:
-        o = torch.empty((total, H, D), dtype=torch.float32, device=r.device)
-    if state_out is None and want_state:
-        state_out = torch.empty((N, H, D, D), dtype=torch.float32, device=r.device)
+    _check_outputs(o, state_out, (total, H, D), (N, H, D, D), out_dtype)
+    with _on_stream(stream):
+        if o is None:
+            o = torch.empty((total, H, D), dtype=out_dtype, device=r.device)
+        if state_out is None and want_state:
+            state_out = torch.empty((N, H, D, D), dtype=torch.float32, device=r.device)
     need = int(_lib.wkv_prefill_varlen_workspace_bytes(cu_host.data_ptr(), N, H, D, code))
-    ws, ws_bytes = _workspace(need, r.device, workspace)
+    ws, ws_bytes = _workspace(need, r.device, workspace, stream)
     with torch.cuda.device(r.device):
         status = _lib.wkv_prefill_varlen_ex(_ptr(r), _ptr(k), _ptr(v), _ptr(w), _ptr(u),
                                             _ptr(second_value), _ptr(cu_seqlens),

@@ -49,10 +49,6 @@ int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
 // has `max_len` tokens.  fp32 inputs are never split (their kernel is serial).
 int64_t choose_segment(int64_t work, int64_t max_len, bool bf16) {
     if (!bf16) return std::max<int64_t>(round_up(std::max<int64_t>(max_len, 1), kChunk), kChunk);
-    if (const char *env = std::getenv("FINCH_WKV_SEGMENT_TOKENS")) {
-        int64_t v = std::atoll(env);
-        if (v >= kChunk && v % kChunk == 0) return v;
-    }
     int64_t seg = round_up(std::max<int64_t>((work + kTargetItems - 1) / kTargetItems, 1), kChunk);
     seg = std::max(seg, kMinSegment);
     const int64_t whole = round_up(std::max<int64_t>(max_len, 1), kChunk);
@@ -154,6 +150,25 @@ wkv_status_t plan_varlen(const int32_t *cu_host, int N, int H, int D, wkv_dtype_
     return WKV_OK;
 }
 
+// A launch covers at most 2^32 - 1 work-items per grid dimension: every
+// kernel a plan would launch is checked here, before anything is enqueued.
+wkv_status_t check_grid(const Plan &p) {
+    constexpr int64_t kMaxWorkItems = 0xFFFFFFFFll;
+    const int64_t items = (int64_t)p.g.n_seg * p.g.H;           // one workgroup per (segment, head)
+    const int64_t slices = (int64_t)p.g.n_seq * p.g.H;
+    if (p.max_len <= kDecodeMaxT && !p.split) {                 // one wave per (sequence, head)
+        if (slices * 64 > kMaxWorkItems)
+            return fail(WKV_EUNSUPPORTED, "%lld (sequence, head) pairs exceed one launch", (long long)slices);
+        return WKV_OK;
+    }
+    if (items * 256 > kMaxWorkItems)
+        return fail(WKV_EUNSUPPORTED, "%lld work items exceed one launch", (long long)items);
+    if (p.split && slices * kScanGroupThreads > kMaxWorkItems)
+        return fail(WKV_EUNSUPPORTED, "%lld (sequence, head) pairs exceed the segment scan's launch",
+                    (long long)slices);
+    return WKV_OK;
+}
+
 // ---- pointer checks ---------------------------------------------------------
 
 struct Range {
@@ -174,12 +189,12 @@ bool overlaps(const Range &a, const Range &b) {
 
 wkv_status_t check_pointers(const Plan &p, const Variant &var, const void *r, const void *k,
                             const void *v, const void *w, const float *u, const void *u2,
-                            const float *state_in, const float *o, const float *state_out,
+                            const float *state_in, const void *o, const float *state_out,
                             const void *ws, size_t ws_bytes, const int32_t *cu_dev) {
     const int64_t tokens = p.g.total_tokens;
     const size_t elt = p.bf16 ? 2 : 4;
     const size_t in_bytes = (size_t)tokens * p.g.H * kHeadDim * elt;
-    const size_t o_bytes = (size_t)tokens * p.g.H * kHeadDim * sizeof(float);
+    const size_t o_bytes = (size_t)tokens * p.g.H * kHeadDim * (var.o_bf16 ? 2 : 4);
     const size_t st_bytes = (size_t)p.g.n_seq * p.g.H * kHeadDim * kHeadDim * sizeof(float);
     if (var.c2) u = nullptr;                           // the bonus is not part of Finch-C2
     else if (u2) return fail(WKV_EINVAL, "second_value is only defined for the Finch-C2 variant");
@@ -259,17 +274,18 @@ wkv_status_t run(const Plan &p, const Tensors &t, const Variant &var, void *ws, 
     return WKV_OK;
 }
 
-constexpr unsigned kKnownFlags = WKV_FLAG_DECAY_LOG | WKV_FLAG_FINCH_C2;
+constexpr unsigned kKnownFlags = WKV_FLAG_DECAY_LOG | WKV_FLAG_FINCH_C2 | WKV_FLAG_OUT_BF16;
 
 wkv_status_t variant_of(unsigned flags, Variant &v) {
     if (flags & ~kKnownFlags) return fail(WKV_EUNSUPPORTED, "unknown flags 0x%x", flags & ~kKnownFlags);
     v.log_decay = (flags & WKV_FLAG_DECAY_LOG) != 0;
     v.c2 = (flags & WKV_FLAG_FINCH_C2) != 0;
+    v.o_bf16 = (flags & WKV_FLAG_OUT_BF16) != 0;
     return WKV_OK;
 }
 
 wkv_status_t prefill_fixed(const void *r, const void *k, const void *v, const void *w,
-                           const float *u, const void *u2, const float *state_in, float *o,
+                           const float *u, const void *u2, const float *state_in, void *o,
                            float *state_out, int B, int T, int H, int D, wkv_dtype_t dt,
                            unsigned flags, void *ws, size_t ws_bytes, void *stream) {
     g_last_error.clear();
@@ -277,16 +293,17 @@ wkv_status_t prefill_fixed(const void *r, const void *k, const void *v, const vo
     if (wkv_status_t s = variant_of(flags, var)) return s;
     Plan p;
     if (wkv_status_t s = plan_fixed(B, T, H, D, dt, p)) return s;
+    if (wkv_status_t s = check_grid(p)) return s;
     if (wkv_status_t s = check_pointers(p, var, r, k, v, w, u, u2, state_in, o, state_out, ws,
                                         ws_bytes, nullptr))
         return s;
-    Tensors t{r, k, v, w, var.c2 ? nullptr : u, state_in, o, state_out, u2};
+    Tensors t{r, k, v, w, var.c2 ? nullptr : u, state_in, o, state_out, u2, var.o_bf16};
     return run(p, t, var, ws, static_cast<hipStream_t>(stream));
 }
 
 wkv_status_t prefill_varlen(const void *r, const void *k, const void *v, const void *w,
                             const float *u, const void *u2, const int32_t *cu_dev,
-                            const int32_t *cu_host, int N, const float *state_in, float *o,
+                            const int32_t *cu_host, int N, const float *state_in, void *o,
                             float *state_out, int H, int D, wkv_dtype_t dt, unsigned flags,
                             void *ws, size_t ws_bytes, void *stream) {
     g_last_error.clear();
@@ -294,12 +311,13 @@ wkv_status_t prefill_varlen(const void *r, const void *k, const void *v, const v
     if (wkv_status_t s = variant_of(flags, var)) return s;
     Plan p;
     if (wkv_status_t s = plan_varlen(cu_host, N, H, D, dt, p)) return s;
+    if (wkv_status_t s = check_grid(p)) return s;
     if (N > 0 && !cu_dev) return fail(WKV_EINVAL, "cu_seqlens_dev is NULL");
     if (wkv_status_t s = check_pointers(p, var, r, k, v, w, u, u2, state_in, o, state_out, ws,
                                         ws_bytes, cu_dev))
         return s;
     p.g.cu = cu_dev;
-    Tensors t{r, k, v, w, var.c2 ? nullptr : u, state_in, o, state_out, u2};
+    Tensors t{r, k, v, w, var.c2 ? nullptr : u, state_in, o, state_out, u2, var.o_bf16};
     return run(p, t, var, ws, static_cast<hipStream_t>(stream));
 }
 
@@ -357,7 +375,7 @@ wkv_status_t wkv_prefill(const void *r, const void *k, const void *v, const void
 }
 
 wkv_status_t wkv_prefill_ex(const void *r, const void *k, const void *v, const void *w,
-                            const float *u, const void *u2, const float *state_in, float *o,
+                            const float *u, const void *u2, const float *state_in, void *o,
                             float *state_out, int B, int T, int H, int D, wkv_dtype_t dt,
                             unsigned flags, void *ws, size_t ws_bytes, void *stream) {
     return prefill_fixed(r, k, v, w, u, u2, state_in, o, state_out, B, T, H, D, dt, flags, ws,
@@ -434,7 +452,7 @@ wkv_status_t wkv_gold_compress(const void *x, const void *w_kd, void *c, wkv_dty
 wkv_status_t wkv_prefill_varlen_ex(const void *r, const void *k, const void *v, const void *w,
                                    const float *u, const void *u2, const int32_t *cu_dev,
                                    const int32_t *cu_host, int N, const float *state_in,
-                                   float *o, float *state_out, int H, int D, wkv_dtype_t dt,
+                                   void *o, float *state_out, int H, int D, wkv_dtype_t dt,
                                    unsigned flags, void *ws, size_t ws_bytes, void *stream) {
     return prefill_varlen(r, k, v, w, u, u2, cu_dev, cu_host, N, state_in, o, state_out, H, D,
                           dt, flags, ws, ws_bytes, stream);

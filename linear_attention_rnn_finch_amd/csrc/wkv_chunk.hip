@@ -495,10 +495,21 @@ __global__ __launch_bounds__(256, 2) void wkv_chunk_kernel(Geometry g, Tensors t
     int64_t tc_pend = 0;
     int nt_pend = 0;
     auto store_o = [&]() {
-        const Rsrc ro = chunk_rsrc(t.o, tc_pend, nt_pend, H, h, kRowOut);
-        #pragma unroll
-        for (int tb = 0; tb < 4; ++tb)
-            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, o_pend[tb]), ro, off_out[tb], 0, 0);
+        if (t.o_bf16) {                                  // 4 bf16 (RNE) per lane and row
+            const Rsrc ro = chunk_rsrc(t.o, tc_pend, nt_pend, H, h, kRowIn);
+            #pragma unroll
+            for (int tb = 0; tb < 4; ++tb) {
+                const f32x2 a = {o_pend[tb][0], o_pend[tb][1]}, b = {o_pend[tb][2], o_pend[tb][3]};
+                const u32x2 pk = {__builtin_bit_cast(unsigned, __builtin_convertvector(a, bf16x2)),
+                                  __builtin_bit_cast(unsigned, __builtin_convertvector(b, bf16x2))};
+                __builtin_amdgcn_raw_buffer_store_b64(pk, ro, off_out[tb] / 2, 0, 0);
+            }
+        } else {
+            const Rsrc ro = chunk_rsrc(t.o, tc_pend, nt_pend, H, h, kRowOut);
+            #pragma unroll
+            for (int tb = 0; tb < 4; ++tb)
+                __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, o_pend[tb]), ro, off_out[tb], 0, 0);
+        }
     };
 
     ChunkRegs<kU2> P;
@@ -908,6 +919,7 @@ __global__ __launch_bounds__(256, 2) void wkv_chunk_kernel(Geometry g, Tensors t
 constexpr int kScanSlices = 16;
 constexpr int kScanThreads = 64;      // 16 workgroups x 64 threads x 4 entries = 4096
 constexpr int kScanBatch = 16;
+static_assert(kScanSlices * kScanThreads == kScanGroupThreads, "scan launch size known to the planner");
 
 __global__ __launch_bounds__(kScanThreads) void wkv_segment_scan_kernel(Geometry g, Tensors t, Workspace ws) {
     const int nh = blockIdx.x / kScanSlices;

@@ -208,7 +208,7 @@ __device__ __forceinline__ void step_token(const Tensors &t, const Tok<In> &cur,
     const float q1 = split32(p[1], p[3]);
     float o = split16(q0, q1);
     if (C2) o += u2_scale * to_f32(cur.u2);
-    t.o[row + jo] = o;
+    store_o1(t, row + jo, o);
     update_rows<0>(S, w, k, v);
 }
 
@@ -606,7 +606,7 @@ __global__ __launch_bounds__(64 * kStepWaves, 2) void wkv_steps_mfma_kernel(Geom
                     o4.z += u2_scale * bf_lo(pu.y);
                     o4.w += u2_scale * bf_hi(pu.y);
                 }
-                *reinterpret_cast<float4 *>(t.o + orow + j0) = o4;
+                store_o4(t, orow + j0, o4);
             }
     }
 

@@ -82,15 +82,39 @@ struct Tensors {
     const void *r, *k, *v, *w;   // w holds w_t, or d_t when the decay is given as d
     const float *u;          // [H, D] static bonus (base Finch; unused by Finch-C2)
     const float *state_in;   // [n_seq, H, D, D] or null
-    float *o;                // [tokens, H, D]
+    void *o;                 // [tokens, H, D], fp32 or (o_bf16) bf16
     float *state_out;        // [n_seq, H, D, D] or null
     const void *u2;          // Finch-C2 second value [tokens, H, D], or null
+    bool o_bf16;             // o is stored as bf16, rounded to nearest even
 };
+
+// Output stores shared by the scan kernels: fp32, or bf16 rounded to nearest
+// even (the conversion instruction's rounding), chosen per call.
+__device__ inline uint16_t bf16_rne_bits(float x) {
+    return __builtin_bit_cast(uint16_t, static_cast<__bf16>(x));
+}
+__device__ inline void store_o1(const Tensors &t, size_t idx, float x) {
+    if (t.o_bf16)
+        static_cast<uint16_t *>(t.o)[idx] = bf16_rne_bits(x);
+    else
+        static_cast<float *>(t.o)[idx] = x;
+}
+// four consecutive outputs starting at idx (a multiple of 4)
+__device__ inline void store_o4(const Tensors &t, size_t idx, float4 x) {
+    if (t.o_bf16) {
+        const uint2 b = make_uint2((uint32_t)bf16_rne_bits(x.x) | ((uint32_t)bf16_rne_bits(x.y) << 16),
+                                   (uint32_t)bf16_rne_bits(x.z) | ((uint32_t)bf16_rne_bits(x.w) << 16));
+        *reinterpret_cast<uint2 *>(static_cast<uint16_t *>(t.o) + idx) = b;
+    } else {
+        *reinterpret_cast<float4 *>(static_cast<float *>(t.o) + idx) = x;
+    }
+}
 
 // Form of the recurrence (compile-time switches of the kernels).
 struct Variant {
     bool log_decay = false;  // decay input d_t, w_t = exp(-exp(d_t))
     bool c2 = false;         // Finch-C2: keys times (1 - w_t), no bonus, + u2
+    bool o_bf16 = false;     // o stored as bf16 (round to nearest even)
 };
 
 // Workspace views (fp32).  seg_state[item]: the segment's zero-start end state
@@ -103,6 +127,8 @@ struct Workspace {
     int32_t *seg_seq;
 };
 constexpr int kSegStateFloats = kHeadDim * kHeadDim + kHeadDim;
+// threads the segment scan launches per (sequence, head)
+constexpr int kScanGroupThreads = 1024;
 constexpr int kSegStartFloats = kHeadDim * kHeadDim;
 
 // Launchers (defined in the .hip files).

@@ -97,7 +97,7 @@ __global__ __launch_bounds__(256) void wkv_serial_kernel(Geometry g, Tensors t) 
                 o = rs + (u2p ? load_in(u2p, idx) : 0.f);
             else
                 o = rs + bonus[row] * tv[row][j];
-            t.o[idx] = o;
+            store_o1(t, idx, o);
         }
     }
     if (t.state_out && it.p == it.P - 1) {

@@ -61,7 +61,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_abi_version_and_status_strings(lib):
-    assert lib.wkv_abi_version() == 2
+    assert lib.wkv_abi_version() == 3
     for s in range(5):
         assert lib.wkv_status_string(s)
     assert lib.wkv_status_string(99) == b"unknown status"
@@ -89,6 +89,8 @@ def call(lib, B=1, T=128, H=4, D=64, dt=BF16, r=R, k=K, v=V, w=W, u=U, s_in=S_IN
     (dict(B=0), EINVAL),
     (dict(T=-1), EINVAL),
     (dict(B=70000, T=70000), EINVAL),
+    (dict(B=300, T=17, H=65536), EUNSUP),     # 19.7M work items: more than one launch holds
+    (dict(B=2048, T=1, H=65536), EUNSUP),     # 134M step slices of one wave each
     (dict(r=None), EINVAL),
     (dict(w=None), EINVAL),
     (dict(u=None), EINVAL),
@@ -171,7 +173,7 @@ def test_varlen_workspace_grows_with_segments(lib):
 
 
 U2 = A * 30
-LOG, C2 = 1, 2
+LOG, C2, OBF16 = 1, 2, 4
 
 
 def call_ex(lib, flags, u=U, u2=None, B=1, T=128, H=4, dt=BF16, o=O, ws=WS):
@@ -182,13 +184,15 @@ def call_ex(lib, flags, u=U, u2=None, B=1, T=128, H=4, dt=BF16, o=O, ws=WS):
 
 
 @pytest.mark.parametrize("kw,expect", [
-    (dict(flags=4), EUNSUP),                          # unknown flag bit
+    (dict(flags=8), EUNSUP),                          # unknown flag bit
     (dict(flags=LOG | 8), EUNSUP),
     (dict(flags=0, u2=U2), EINVAL),                   # second value without C2
     (dict(flags=LOG, u=None), EINVAL),                # base Finch needs its bonus
     (dict(flags=C2, u2=U2 + 8), EINVAL),              # misaligned second value
     (dict(flags=C2, u2=U2, o=U2 + 64), EINVAL),       # o overlaps the second value
     (dict(flags=C2 | LOG, u2=U2, o=None), EINVAL),
+    (dict(flags=OBF16, o=O + 8), EINVAL),             # bf16 o: still 16-byte aligned
+    (dict(flags=OBF16, o=S_OUT - 128 * 4 * 64 * 2 + 256), EINVAL),   # bf16 o reaching state_out
 ])
 def test_extended_validation(lib, kw, expect):
     st, msg = call_ex(lib, **kw)
@@ -202,6 +206,11 @@ def test_extended_varlen_validation(lib):
     st = lib.wkv_prefill_varlen_ex(R, K, V, W, U, None, A * 20, cu.ctypes.data, 2, S_IN, O, S_OUT,
                                    4, 64, BF16, 16, WS, ws_bytes, None)
     assert st == EUNSUP
+    # a bf16 o of 300 tokens x 4 heads x 64 x 2 B ends 256 B into state_out
+    st = lib.wkv_prefill_varlen_ex(R, K, V, W, U, None, A * 20, cu.ctypes.data, 2, S_IN,
+                                   S_OUT - 300 * 4 * 64 * 2 + 256, S_OUT, 4, 64, BF16, OBF16, WS,
+                                   ws_bytes, None)
+    assert st == EINVAL and b"overlaps" in lib.wkv_last_error()
     st = lib.wkv_prefill_varlen_ex(R, K, V, W, U, U2, A * 20, cu.ctypes.data, 2, S_IN, O, S_OUT,
                                    4, 64, BF16, LOG, WS, ws_bytes, None)
     assert st == EINVAL and b"Finch-C2" in lib.wkv_last_error()
