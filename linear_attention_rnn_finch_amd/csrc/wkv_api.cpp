@@ -268,9 +268,7 @@ wkv_status_t run(const Plan &p, const Tensors &t, const Variant &var, void *ws, 
         w.seg_state = reinterpret_cast<float *>(base + p.off_seg_state);
         w.seg_start = reinterpret_cast<float *>(base + p.off_seg_start);
     }
-    if (p.split && (e = launch_segment_states(g, t, w, var, st)) != hipSuccess)
-        return fail_hip(e, "segment-state launch");
-    if ((e = launch_chunked_main(g, t, w, var, st, tm)) != hipSuccess) return fail_hip(e, "scan launch");
+    if ((e = launch_chunked(g, t, w, p.split, var, st, tm)) != hipSuccess) return fail_hip(e, "scan launch");
     return WKV_OK;
 }
 

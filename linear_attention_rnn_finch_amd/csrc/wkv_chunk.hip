@@ -126,7 +126,7 @@ constexpr int kRsrcWord3 = 0x00020000;         // raw dword access, no swizzle
 __device__ __forceinline__ Rsrc chunk_rsrc(const void *base, int64_t row0, int rows, int H, int h,
                                            int row_bytes) {
     const char *p = static_cast<const char *>(base) + ((size_t)row0 * H + h) * row_bytes;
-    const int bytes = ((rows - 1) * H + 1) * row_bytes;
+    const int bytes = rows > 0 ? ((rows - 1) * H + 1) * row_bytes : 0;   // no rows: every load reads 0
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<char *>(p), (short)0, bytes, kRsrcWord3);
 }
 
@@ -383,50 +383,27 @@ __device__ __forceinline__ float one_minus_w(float x, float e) {
     return e < 0.03125f ? series : direct;
 }
 
-template <Mode M, bool LOGD, bool C2>
-__global__ __launch_bounds__(256, 2) void wkv_chunk_kernel(Geometry g, Tensors t, Workspace ws) {
+// One segment of one head, chunk by chunk, from the state S in registers
+// (lane (i16, grp) of wave w holds S[16*ib + 4*grp + e][16*w + i16]).
+//  - Main: o of every token is stored; S ends as the state after the segment.
+//  - State: nothing is stored; S ends as the segment's zero-start aggregate
+//    when it starts at zero, and lam_seg (lanes with i16 == 15, channels
+//    c0 .. c0+3) accumulates the segment's total log2-decay.
+template <Mode M, bool LOGD, bool C2, typename SM>
+__device__ __forceinline__ void scan_chunks(SM &sm, const Tensors &t, int64_t seg_t0, int64_t seg_t1,
+                                            int h, int H, float (&S)[4][4], float (&lam_seg)[4]) {
     constexpr bool kU2 = M == Mode::Main && C2;            // second value staged and added
-    using SM = Smem<kU2 ? 4 : 3>;
-    __shared__ SM sm;
-
-    const int item = blockIdx.x;
-    const int h = item % g.H;
-    const ItemRange it = decode_segment(g, item / g.H);
-    if (!it.valid) return;
-    if (M == Mode::State && it.p == it.P - 1) return;      // last segment's aggregate is unused
-    // a split the host did not plan (device offsets differing from the host
-    // copy) has no workspace behind it: leave the item alone
-    if (it.P > 1 && (ws.seg_start == nullptr || ws.seg_state == nullptr)) return;
-
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lane = tid & 63;
     const int i16 = lane & 15;
     const int grp = lane >> 4;
-    const int H = g.H;
     const LdsBases lb = make_bases(tid);
-
-    // ---- carried state ------------------------------------------------------
-    // lane (i16, grp) of wave w holds S[16*ib + 4*grp + e][16*w + i16]
-    float S[4][4];
-    const float *s_src = nullptr;
-    if (M == Mode::Main) {
-        if (it.P > 1)
-            s_src = ws.seg_start + (size_t)item * kSegStartFloats;
-        else if (t.state_in)
-            s_src = t.state_in + ((size_t)it.n * H + h) * (kHeadDim * kHeadDim);
-    }
-    #pragma unroll
-    for (int ib = 0; ib < 4; ++ib)
-        #pragma unroll
-        for (int e = 0; e < 4; ++e)
-            S[ib][e] = s_src ? s_src[(16 * ib + 4 * grp + e) * kHeadDim + 16 * wave + i16] : 0.f;
 
     // pre-processing layout: channels c0..c0+3, tokens 4*i16 .. 4*i16+3
     const int c0 = 16 * wave + 4 * grp;
     f32x4 u4 = {0.f, 0.f, 0.f, 0.f};
     if (M == Mode::Main && !C2) u4 = *reinterpret_cast<const f32x4 *>(t.u + (size_t)h * kHeadDim + c0);
-    float lam_seg[4] = {0.f, 0.f, 0.f, 0.f};                // State: segment log2-decay per channel
 
 
     const uint16_t *gr = static_cast<const uint16_t *>(t.r);
@@ -461,7 +438,7 @@ __global__ __launch_bounds__(256, 2) void wkv_chunk_kernel(Geometry g, Tensors t
     #pragma unroll
     for (int tb = 0; tb < 4; ++tb) off_out[tb] = (16 * tb + i16) * H * kRowOut + 4 * (16 * wave + 4 * grp);
     auto issue_loads = [&](ChunkRegs<kU2> &P, int64_t tc) {
-        const int rows = (int)min<int64_t>(kChunk, it.t1 - tc);
+        const int rows = (int)min<int64_t>(kChunk, seg_t1 - tc);
         const Rsrc rk = chunk_rsrc(t.k, tc, rows, H, h, kRowIn);
         const Rsrc rw = chunk_rsrc(t.w, tc, rows, H, h, kRowIn);
         const Rsrc rv = chunk_rsrc(t.v, tc, rows, H, h, kRowIn);
@@ -485,7 +462,7 @@ __global__ __launch_bounds__(256, 2) void wkv_chunk_kernel(Geometry g, Tensors t
         }
     };
 
-    const int64_t n_tok = it.t1 - it.t0;
+    const int64_t n_tok = seg_t1 - seg_t0;
     const int n_chunks = (int)((n_tok + kChunk - 1) / kChunk);
     // o of chunk c (acc[tb][e] = o[16*tb + i16][16*wave + 4*grp + e]) is held
     // until chunk c + 1 has its inputs, and stored just before the loads of
@@ -513,11 +490,11 @@ __global__ __launch_bounds__(256, 2) void wkv_chunk_kernel(Geometry g, Tensors t
     };
 
     ChunkRegs<kU2> P;
-    if (n_chunks > 0) issue_loads(P, it.t0);
+    if (n_chunks > 0) issue_loads(P, seg_t0);
 
     for (int c = 0; c < n_chunks; ++c) {
-        const int64_t tc = it.t0 + (int64_t)c * kChunk;
-        const int nt = (int)min<int64_t>(kChunk, it.t1 - tc);
+        const int64_t tc = seg_t0 + (int64_t)c * kChunk;
+        const int nt = (int)min<int64_t>(kChunk, seg_t1 - tc);
 
         // Wave priority falls with progress through the segment: the two
         // workgroups sharing a CU then advance together (instead of the older
@@ -888,25 +865,52 @@ __global__ __launch_bounds__(256, 2) void wkv_chunk_kernel(Geometry g, Tensors t
     }
     if (M == Mode::Main && n_chunks > 0) store_o();
 
-    // ---- outputs of the work item ------------------------------------------------
-    if (M == Mode::State) {
-        float *dst = ws.seg_state + (size_t)item * kSegStateFloats;
+}
+
+__device__ __forceinline__ void load_public_state(const float *src, float (&S)[4][4]) {
+    const int tid = threadIdx.x, wave = tid >> 6, i16 = tid & 15, grp = (tid & 63) >> 4;
+    #pragma unroll
+    for (int ib = 0; ib < 4; ++ib)
         #pragma unroll
-        for (int ib = 0; ib < 4; ++ib)
-            #pragma unroll
-            for (int e = 0; e < 4; ++e)
-                dst[(16 * ib + 4 * grp + e) * kHeadDim + 16 * wave + i16] = S[ib][e];
-        if (i16 == 15) {
-            #pragma unroll
-            for (int q = 0; q < 4; ++q) dst[kHeadDim * kHeadDim + c0 + q] = lam_seg[q];
-        }
-    } else if (t.state_out && it.p == it.P - 1) {
-        float *dst = t.state_out + ((size_t)it.n * H + h) * (kHeadDim * kHeadDim);
+        for (int e = 0; e < 4; ++e)
+            S[ib][e] = src ? src[(16 * ib + 4 * grp + e) * kHeadDim + 16 * wave + i16] : 0.f;
+}
+__device__ __forceinline__ void store_public_state(float *dst, const float (&S)[4][4]) {
+    const int tid = threadIdx.x, wave = tid >> 6, i16 = tid & 15, grp = (tid & 63) >> 4;
+    #pragma unroll
+    for (int ib = 0; ib < 4; ++ib)
         #pragma unroll
-        for (int ib = 0; ib < 4; ++ib)
-            #pragma unroll
-            for (int e = 0; e < 4; ++e)
-                dst[(16 * ib + 4 * grp + e) * kHeadDim + 16 * wave + i16] = S[ib][e];
+        for (int e = 0; e < 4; ++e)
+            dst[(16 * ib + 4 * grp + e) * kHeadDim + 16 * wave + i16] = S[ib][e];
+}
+
+// State pass: the zero-start aggregate of every segment but the last of its
+// sequence, B_p (D*D, [key][value]) followed by the segment's total log2-decay
+// per key channel (D).  One chunk is prefetched ahead: keeping two or three
+// chunks of every item in flight was measured slower (HBM serves the strided
+// 128-byte row pieces of more chunks at once less efficiently).
+template <bool LOGD, bool C2>
+__global__ __launch_bounds__(256, 2) void wkv_state_kernel(Geometry g, Tensors t, Workspace ws) {
+    using SM = Smem<3>;
+    __shared__ SM sm;
+    const int item = blockIdx.x;
+    const int h = item % g.H;
+    const ItemRange it = decode_segment(g, item / g.H);
+    if (!it.valid || it.p == it.P - 1) return;           // the last segment's aggregate is unused
+    if (ws.seg_state == nullptr) return;                 // a split the host did not plan
+    float S[4][4], lam[4] = {0.f, 0.f, 0.f, 0.f};
+    #pragma unroll
+    for (int ib = 0; ib < 4; ++ib)
+        #pragma unroll
+        for (int e = 0; e < 4; ++e) S[ib][e] = 0.f;
+    scan_chunks<Mode::State, LOGD, C2>(sm, t, it.t0, it.t1, h, g.H, S, lam);
+    float *dst = ws.seg_state + (size_t)item * kSegStateFloats;
+    store_public_state(dst, S);
+    const int tid = threadIdx.x;
+    if ((tid & 15) == 15) {
+        const int c0 = 16 * (tid >> 6) + 4 * ((tid & 63) >> 4);
+        #pragma unroll
+        for (int q = 0; q < 4; ++q) dst[kHeadDim * kHeadDim + c0 + q] = lam[q];
     }
 }
 
@@ -967,39 +971,57 @@ __global__ __launch_bounds__(kScanThreads) void wkv_segment_scan_kernel(Geometry
     }
 }
 
-template <Mode M>
-using ChunkKernel = void (*)(Geometry, Tensors, Workspace);
-
-template <Mode M>
-ChunkKernel<M> chunk_kernel_for(Variant v) {
-    if (v.log_decay)
-        return v.c2 ? wkv_chunk_kernel<M, true, true> : wkv_chunk_kernel<M, true, false>;
-    return v.c2 ? wkv_chunk_kernel<M, false, true> : wkv_chunk_kernel<M, false, false>;
+// The chunked scan: one workgroup per (segment, head), from the state that
+// enters the segment (state_in for a sequence's first segment, else the
+// combined start state of the segment scan).
+template <bool LOGD, bool C2>
+__global__ __launch_bounds__(256, 2) void wkv_chunk_kernel(Geometry g, Tensors t, Workspace ws) {
+    using SM = Smem<C2 ? 4 : 3>;
+    __shared__ SM sm;
+    const int item = blockIdx.x;
+    const int h = item % g.H;
+    const ItemRange it = decode_segment(g, item / g.H);
+    if (!it.valid) return;
+    // a split the host did not plan (device offsets differing from the host
+    // copy) has no workspace behind it: leave the item alone
+    if (it.P > 1 && ws.seg_start == nullptr) return;
+    float S[4][4], lam[4] = {0.f, 0.f, 0.f, 0.f};
+    const float *s_src = nullptr;
+    if (it.P > 1)
+        s_src = ws.seg_start + (size_t)item * kSegStartFloats;
+    else if (t.state_in)
+        s_src = t.state_in + ((size_t)it.n * g.H + h) * (kHeadDim * kHeadDim);
+    load_public_state(s_src, S);
+    scan_chunks<Mode::Main, LOGD, C2>(sm, t, it.t0, it.t1, h, g.H, S, lam);
+    if (t.state_out && it.p == it.P - 1)
+        store_public_state(t.state_out + ((size_t)it.n * g.H + h) * (kHeadDim * kHeadDim), S);
 }
 
 }  // namespace
 
-hipError_t launch_segment_states(const Geometry &g, const Tensors &t, const Workspace &ws,
-                                 Variant v, hipStream_t st) {
+hipError_t launch_chunked(const Geometry &g, const Tensors &t, const Workspace &ws, bool split,
+                          Variant v, hipStream_t st, KernelTiming tm) {
     const int64_t items = (int64_t)g.n_seg * g.H;
     if (items <= 0) return hipSuccess;
-    hipLaunchKernelGGL(chunk_kernel_for<Mode::State>(v), dim3((unsigned)items), dim3(256), 0, st, g, t, ws);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(wkv_segment_scan_kernel, dim3((unsigned)(g.n_seq * g.H * kScanSlices)), dim3(kScanThreads), 0, st,
-                       g, t, ws);
-    return hipGetLastError();
-}
-
-hipError_t launch_chunked_main(const Geometry &g, const Tensors &t, const Workspace &ws,
-                               Variant v, hipStream_t st, KernelTiming tm) {
-    const int64_t items = (int64_t)g.n_seg * g.H;
-    if (items <= 0) return hipSuccess;
-    const ChunkKernel<Mode::Main> kern = chunk_kernel_for<Mode::Main>(v);
+    const dim3 grid((unsigned)items), block(256);
+    if (split) {
+        void (*ks)(Geometry, Tensors, Workspace) =
+            v.log_decay ? (v.c2 ? wkv_state_kernel<true, true> : wkv_state_kernel<true, false>)
+                        : (v.c2 ? wkv_state_kernel<false, true> : wkv_state_kernel<false, false>);
+        hipLaunchKernelGGL(ks, grid, block, 0, st, g, t, ws);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL(wkv_segment_scan_kernel, dim3((unsigned)(g.n_seq * g.H * kScanSlices)), dim3(kScanThreads),
+                           0, st, g, t, ws);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
+    void (*k)(Geometry, Tensors, Workspace) =
+        v.log_decay ? (v.c2 ? wkv_chunk_kernel<true, true> : wkv_chunk_kernel<true, false>)
+                    : (v.c2 ? wkv_chunk_kernel<false, true> : wkv_chunk_kernel<false, false>);
     if (tm.start || tm.stop)
-        hipExtLaunchKernelGGL(kern, dim3((unsigned)items), dim3(256), 0, st, tm.start, tm.stop, 0, g, t, ws);
+        hipExtLaunchKernelGGL(k, grid, block, 0, st, tm.start, tm.stop, 0, g, t, ws);
     else
-        hipLaunchKernelGGL(kern, dim3((unsigned)items), dim3(256), 0, st, g, t, ws);
+        hipLaunchKernelGGL(k, grid, block, 0, st, g, t, ws);
     return hipGetLastError();
 }
 

@@ -127,9 +127,9 @@ struct Workspace {
     int32_t *seg_seq;
 };
 constexpr int kSegStateFloats = kHeadDim * kHeadDim + kHeadDim;
+constexpr int kSegStartFloats = kHeadDim * kHeadDim;
 // threads the segment scan launches per (sequence, head)
 constexpr int kScanGroupThreads = 1024;
-constexpr int kSegStartFloats = kHeadDim * kHeadDim;
 
 // Launchers (defined in the .hip files).
 // Scan kernels take an optional event pair: when set, the launch records the
@@ -144,12 +144,10 @@ hipError_t launch_serial(const Geometry &g, const Tensors &t, bool bf16, Variant
 // longest): one wave per (sequence, head), fp32 state in registers
 hipError_t launch_decode(const Geometry &g, const Tensors &t, bool bf16, Variant v, int max_len, hipStream_t st,
                          KernelTiming tm = {});
-// bf16 path: state pass + segment scan (only when some sequence is split), then
-// the main chunked scan.
-hipError_t launch_segment_states(const Geometry &g, const Tensors &t, const Workspace &ws,
-                                 Variant v, hipStream_t st);
-hipError_t launch_chunked_main(const Geometry &g, const Tensors &t, const Workspace &ws,
-                               Variant v, hipStream_t st, KernelTiming tm = {});
+// bf16 path: when some sequence is split (split), the state pass and the
+// segment scan, then the chunked scan (the kernel the timing events attach to).
+hipError_t launch_chunked(const Geometry &g, const Tensors &t, const Workspace &ws, bool split,
+                          Variant v, hipStream_t st, KernelTiming tm = {});
 // epilogue of Finch-C2 pre-fill: LayerNorm over heads, GOLD key compression
 hipError_t launch_layernorm_rows(const float *x, const float *gamma, const float *beta, float eps, void *y,
                                  bool out_bf16, int64_t rows, int width, hipStream_t st, KernelTiming tm = {});

@@ -165,7 +165,7 @@ def test_graph_replays_match_eager():
     B, T, H, D = g["r"].shape
     o = torch.empty((B, T, H, D), dtype=torch.float32, device="cuda")
     st = torch.empty((B, H, D, D), dtype=torch.float32, device="cuda")
-    ws = torch.empty(max(fw.workspace_bytes(B, T, H, D), 1), dtype=torch.uint8, device="cuda")
+    ws = torch.zeros(max(fw.workspace_bytes(B, T, H, D), 1), dtype=torch.uint8, device="cuda")
     o_ref, s_ref = run_gpu(wl, g)
     torch.cuda.synchronize()
     graph = torch.cuda.CUDAGraph()
