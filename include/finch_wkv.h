@@ -205,6 +205,24 @@ wkv_status_t wkv_prefill_varlen_ex(const void *r, const void *k, const void *v,
                                    void *stream);
 
 /*
+ * wkv_prefill_ex without a workspace, for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc.  Same arguments, results and validation as
+ * wkv_prefill_ex; it allocates nothing.  Its scratch is a 36 MiB device array
+ * inside the library that each GPU holds from the first such call until the
+ * process ends (every fixed-length plan fits: at most about 34 MB are used).
+ * All calls on one GPU share that array: calls that overlap in time on one
+ * GPU (different streams, different threads without ordering) race and give
+ * wrong results.  Calls ordered on one stream are safe.  No part of the
+ * scratch has to start at zero.
+ */
+wkv_status_t wkv_prefill_noalloc(const void *r, const void *k, const void *v,
+                                 const void *decay, const float *u, const void *second_value,
+                                 const float *state_in, void *o, float *state_out,
+                                 int B, int T, int H, int D, wkv_dtype_t in_dtype,
+                                 unsigned flags, void *stream);
+
+/*
  * LayerNorm over the concatenated heads of each token: the normalisation of
  * the Finch-C2 output equation (section 3.4, output equation, applied to
  * r_t wkv_t + u'_t of all heads before W_O).  Per row of `width` values:

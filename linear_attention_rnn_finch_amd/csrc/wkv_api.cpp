@@ -320,6 +320,37 @@ wkv_status_t prefill_varlen(const void *r, const void *k, const void *v, const v
 }
 
 }  // namespace
+
+wkv_status_t record_error(wkv_status_t st, const char *what) { return fail(st, "%s", what); }
+
+wkv_status_t prefill_fixed_from(const void *r, const void *k, const void *v, const void *w,
+                                const float *u, const void *u2, const float *state_in, void *o,
+                                float *state_out, int B, int T, int H, int D, wkv_dtype_t dt,
+                                unsigned flags, ScratchSource scratch, void *stream) {
+    g_last_error.clear();
+    Variant var;
+    if (wkv_status_t s = variant_of(flags, var)) return s;
+    Plan p;
+    if (wkv_status_t s = plan_fixed(B, T, H, D, dt, p)) return s;
+    if (wkv_status_t s = check_grid(p)) return s;
+    void *ws = nullptr;
+    if (p.bytes > 0) {
+        // pointers are checked first with a stand-in scratch range that cannot
+        // overlap anything, so that no HIP call is made for an invalid call
+        if (wkv_status_t s = check_pointers(p, var, r, k, v, w, u, u2, state_in, o, state_out, nullptr,
+                                            0, nullptr);
+            s != WKV_OK && s != WKV_EWORKSPACE)
+            return s;
+        g_last_error.clear();
+        if (wkv_status_t s = scratch(p.bytes, &ws)) return s;
+    }
+    if (wkv_status_t s = check_pointers(p, var, r, k, v, w, u, u2, state_in, o, state_out, ws,
+                                        p.bytes, nullptr))
+        return s;
+    Tensors t{r, k, v, w, var.c2 ? nullptr : u, state_in, o, state_out, u2, var.o_bf16};
+    return run(p, t, var, ws, static_cast<hipStream_t>(stream));
+}
+
 }  // namespace finch
 
 using namespace finch;

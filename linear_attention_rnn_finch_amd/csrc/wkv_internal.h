@@ -157,3 +157,22 @@ hipError_t launch_plan_varlen(const Geometry &g, int32_t *seg_off, int32_t *seg_
                               hipStream_t st);
 
 }  // namespace finch
+
+#include "finch_wkv.h"
+
+namespace finch {
+
+// Host-side pieces of the C ABI (wkv_api.cpp) that other entry points share.
+// A scratch source sets *out to device memory of at least `bytes` for the
+// call and returns WKV_OK, or returns the error after recording why
+// (record_error).
+using ScratchSource = wkv_status_t (*)(size_t bytes, void **out);
+wkv_status_t record_error(wkv_status_t st, const char *what);
+// The fixed-length pre-fill of wkv_prefill_ex, with its scratch (if the plan
+// needs any) taken from `scratch` once the arguments have been validated.
+wkv_status_t prefill_fixed_from(const void *r, const void *k, const void *v, const void *w,
+                                const float *u, const void *u2, const float *state_in, void *o,
+                                float *state_out, int B, int T, int H, int D, wkv_dtype_t dt,
+                                unsigned flags, ScratchSource scratch, void *stream);
+
+}  // namespace finch

@@ -249,3 +249,18 @@ def test_compress_validation(lib, kw, expect):
     a.update(kw)
     st = lib.wkv_gold_compress(a["x"], a["w"], a["c"], a["out"], a["tokens"], a["d"], None)
     assert st == expect, lib.wkv_last_error()
+
+
+def test_noalloc_entry_point_validates_before_any_hip_call(lib):
+    """wkv_prefill_noalloc plans and checks its arguments like wkv_prefill_ex
+    before it looks up its static scratch (so these fail without a GPU)."""
+    vp, i = ctypes.c_void_p, ctypes.c_int
+    f = lib.wkv_prefill_noalloc
+    f.restype = i
+    f.argtypes = [vp] * 9 + [i] * 5 + [ctypes.c_uint, vp]
+    args = lambda **kw: [kw.get("r", R), K, V, W, U, None, S_IN, kw.get("o", O), S_OUT, 1, 4096, 32,
+                         kw.get("D", 64), BF16, kw.get("flags", 0), None]
+    assert f(*args(D=32)) == EUNSUP
+    assert f(*args(r=None)) == EINVAL and b"r is NULL" in lib.wkv_last_error()
+    assert f(*args(o=O + 4)) == EINVAL and b"aligned" in lib.wkv_last_error()
+    assert f(*args(flags=8)) == EUNSUP
