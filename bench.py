@@ -51,14 +51,15 @@ def algorithmic_bytes(cfg, tokens, n_seq, has_state_in, variant="finch"):
     return tokens * per_token + n_seq * cfg.H * per_state
 
 
-# HBM traffic of the main kernel, from rocprofv3 FETCH_SIZE / WRITE_SIZE passes
-# (scaled by a plain copy of known size); valid only for the workload and the
-# kernel source the counters were taken on.  Records are kept per kernel:
-# "wkv_chunk_main" (chunked scan), "wkv_decode" (the step kernels), "epilogue".
+# HBM traffic from rocprofv3 FETCH_SIZE / WRITE_SIZE passes (scaled by a plain
+# copy of known size); valid only for the workload and the kernel sources the
+# counters were taken on.  Records are kept per family: "wkv_call" (the whole
+# chunked pre-fill call: state pass, segment scan and chunked scan, summed),
+# "wkv_decode" (the step kernels), "epilogue".
 def traffic_family(workload_name, kernel_name):
     if workload_name.startswith(("layernorm_heads", "gold_compress")):
         return "epilogue"
-    return "wkv_decode" if kernel_name.startswith(("wkv_decode", "wkv_steps")) else "wkv_chunk_main"
+    return "wkv_decode" if kernel_name.startswith(("wkv_decode", "wkv_steps")) else "wkv_call"
 
 
 def traffic_file(workload_name, kernel_name):
@@ -75,8 +76,8 @@ def workload_name(cfg_name, decay, variant):
 # sources behind each family of traffic records: the kernel, and for the
 # chunked scan the host plan that sizes its segments
 KERNEL_SOURCES = {
-    "wkv_chunk_main": ("linear_attention_rnn_finch_amd/csrc/wkv_chunk.hip",
-                       "linear_attention_rnn_finch_amd/csrc/wkv_api.cpp"),
+    "wkv_call": ("linear_attention_rnn_finch_amd/csrc/wkv_chunk.hip",
+                 "linear_attention_rnn_finch_amd/csrc/wkv_api.cpp"),
     "wkv_decode": ("linear_attention_rnn_finch_amd/csrc/wkv_decode.hip",),
     "epilogue": ("linear_attention_rnn_finch_amd/csrc/wkv_epilogue.hip",),
 }
@@ -111,6 +112,60 @@ def measured_traffic(workload_name, kernel_name):
         return int(fields["traffic_bytes_per_launch"])
     except (KeyError, ValueError):
         return None
+
+
+# Matrix-core work issued by the chunked path, counted from the kernels'
+# instruction sequence: per workgroup and 64-token chunk the chunked scan
+# issues 268 v_mfma_f32_16x16x32_bf16 (A tiles 10 x 2 K-steps x 3 split
+# products = 60; read-out 4 waves x 4 x 2 x 3 = 96; state update 4 x 4 x 2 x 2
+# = 64; in-chunk pairs 4 x 6 x 2 = 48) and the state pass 64 (4 x 4 x 2 x 2).
+MFMA_FLOPS = 16 * 16 * 32 * 2
+MAIN_MFMA_PER_CHUNK = 268
+STATE_MFMA_PER_CHUNK = 64
+BF16_MFMA_PEAK = 2.5e15          # MI355X dense bf16, FLOP/s
+
+
+def chunk_counts(lengths, H):
+    """(chunked-scan chunks, state-pass chunks) of a bf16 call over sequences of
+    these lengths, with the library's segment plan: about 512 (segment, head)
+    items, segments a multiple of 64 tokens and at least 256, no longer than
+    the longest sequence rounded up to 64."""
+    up = lambda x, m: -(-x // m) * m
+    tokens, max_len = sum(lengths), max(lengths) if lengths else 0
+    seg = min(max(up(max(-(-tokens * H // 512), 1), 64), 256), up(max(max_len, 1), 64))
+    main = state = 0
+    for L in lengths:
+        P = 1 if L == 0 else -(-L // seg)
+        main += -(-L // 64)
+        if P > 1:
+            state += (P - 1) * seg // 64
+    return main * H, state * H
+
+
+def time_calls(call, n, torch):
+    """Average duration (ms) of whole calls from events recorded on the launch
+    stream before and after each call (queued back to back behind a device
+    sleep, so the events measure the GPU work, gaps between its kernels
+    included)."""
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+    torch.cuda.synchronize()
+    torch.cuda._sleep(50_000_000)
+    for a, b in evs:
+        a.record()
+        call()
+        b.record()
+    torch.cuda.synchronize()
+    return sum(a.elapsed_time(b) for a, b in evs) / n
+
+
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
 
 
 def copy_bandwidth(torch, mib=1024, reps=20):
@@ -172,14 +227,8 @@ def time_main_kernel(call, n, hip, lib, torch):
     return total / n, durations[len(durations) // 2]
 
 
-def cpu_baseline(wl, target_seconds):
-    """Time the fp64 oracle on the host over whole passes of the workload (all
-    slices), repeating until about target_seconds of work; returns the record
-    and the oracle outputs of the last pass."""
+def _time_oracle(wl, threads, target_seconds):
     import oracle
-    threads = len(os.sched_getaffinity(0))
-    if os.environ.get("OMP_NUM_THREADS", "").isdigit():
-        threads = min(threads, int(os.environ["OMP_NUM_THREADS"]))
     passes, t0, out = 0, time.perf_counter(), None
     while True:
         out = oracle.wkv_scan(wl.r, wl.k, wl.v, wl.w, wl.u, wl.state0, wl.cu_seqlens,
@@ -188,13 +237,28 @@ def cpu_baseline(wl, target_seconds):
         passes += 1
         el = time.perf_counter() - t0
         if el >= target_seconds or passes >= 100000:
-            break
+            return passes, el, out
+
+
+def cpu_baseline(wl, target_seconds):
+    """Time the fp64 oracle on the host over whole passes of the workload (all
+    slices), repeating until about target_seconds of work, on every thread of
+    the process affinity mask and on one thread; returns the record and the
+    oracle outputs of the last pass."""
+    threads = len(os.sched_getaffinity(0))
+    if os.environ.get("OMP_NUM_THREADS", "").isdigit():
+        threads = min(threads, int(os.environ["OMP_NUM_THREADS"]))
+    passes, el, out = _time_oracle(wl, threads, target_seconds)
+    passes1, el1, _ = _time_oracle(wl, 1, target_seconds)
     tokens = wl.tokens * passes
     rec = {"value": tokens / el, "unit": "tokens/s", "cores": threads, "kind": "oracle",
            "sample": "%d full pass(es) of the %s workload (%d tokens x %d heads), fp64 "
-                     "sequential recurrence, OpenMP over (sequence, head) slices, %.1f s"
+                     "sequential recurrence, OpenMP over (sequence, head) slices, %.1f s; "
+                     "one thread: %d pass(es) in %.1f s"
                      % (passes, workload_name(wl.config.name, wl.decay, wl.variant), wl.tokens,
-                        wl.u.shape[0], el)}
+                        wl.u.shape[0], el, passes1, el1),
+           "value_1thread": wl.tokens * passes1 / el1,
+           "cpu_model": cpu_model()}
     return rec, out
 
 
@@ -233,7 +297,7 @@ def main():
     import torch
     import linear_attention_rnn_finch_amd as fw
     from linear_attention_rnn_finch_amd import _binding
-    from synth import make_workload, get_config, max_block_error
+    from synth import make_workload, get_config, error_report
 
     cfg = get_config(int(args.config) if args.config.isdigit() else args.config)
     wl = make_workload(cfg, decay=args.decay, variant=args.variant)
@@ -333,19 +397,32 @@ def main():
     elif cfg.dtype != "bf16":
         kernel_name = "wkv_serial_kernel"
     else:
-        kernel_name = "wkv_chunk_kernel<Main>"
+        kernel_name = "wkv_chunk_kernel"
     tokens_per_step = wl.tokens
     value = tokens_per_step / (ms_per_step * 1e-3)
 
-    # main kernel duration, live HIP events
+    # durations measured live: the main kernel through the library's timing
+    # hook (events attached to its own dispatch), the whole call with events
+    # recorded on the launch stream around it
     hip = hip_runtime()
     lib = _binding._lib
     lib.wkv_set_kernel_timing_events.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
     k_avg_ms, k_med_ms = time_main_kernel(call, args.kernel_samples, hip, lib, torch)
+    c_avg_ms = time_calls(call, args.kernel_samples, torch)
     alg = algorithmic_bytes(cfg, wl.tokens, n_seq, wl.state0 is not None, args.variant)
-    achieved = alg / (k_avg_ms * 1e-3) / 1e9
     step_gbs = alg / (ms_per_step * 1e-3) / 1e9
+    kernel_gbs = alg / (k_avg_ms * 1e-3) / 1e9
     copy_gbs = copy_bandwidth(torch)
+    chunked = kernel_name == "wkv_chunk_kernel"
+    lengths = [int(x) for x in np.diff(wl.cu_seqlens)] if wl.packed else [cfg.T] * cfg.B
+    mfma = None
+    if chunked:
+        main_chunks, state_chunks = chunk_counts(lengths, cfg.H)
+        flops = MFMA_FLOPS * (MAIN_MFMA_PER_CHUNK * main_chunks + STATE_MFMA_PER_CHUNK * state_chunks)
+        mfma = {"issued_flops_per_call": flops,
+                "mfma_util": round(flops / (ms_per_step * 1e-3) / BF16_MFMA_PEAK, 4),
+                "main_kernel_mfma_util": round(MFMA_FLOPS * MAIN_MFMA_PER_CHUNK * main_chunks
+                                               / (k_avg_ms * 1e-3) / BF16_MFMA_PEAK, 4)}
 
     rec = {
         "metric": METRIC if cfg.name == "layer_1p5b_t4096" else OTHER_METRIC,
@@ -366,27 +443,38 @@ def main():
                    "timing": ("eager calls" if args.no_graph else
                               "HIP graph of %d captured calls, one replay" % args.steps),
                    "buffer_sets": n_sets},
-        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+        # the headline fraction is the whole pre-fill call's (every kernel of
+        # the step, in the step time above); the main kernel's own figure is
+        # kept beside it
+        "roofline": {"bound": "hbm", "scope": "pre-fill call" + (
+                         " (state pass, segment scan, chunked scan)" if chunked else " (one kernel)"),
+                     "achieved": round(step_gbs, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(step_gbs / HBM_PEAK_GBS, 4),
                      "traffic": measured_traffic(name, kernel_name),
-                     "kernel": kernel_name,
-                     "kernel_avg_us": round(k_avg_ms * 1e3, 2),
-                     "kernel_median_us": round(k_med_ms * 1e3, 2),
-                     "algorithmic_bytes_per_launch": alg,
-                     "whole_step_GBps": round(step_gbs, 1),
-                     "whole_step_frac": round(step_gbs / HBM_PEAK_GBS, 4),
+                     "algorithmic_bytes_per_call": alg,
+                     "call_event_avg_us": round(c_avg_ms * 1e3, 2),
                      "measured_copy_GBps": round(copy_gbs, 1),
-                     "kernel_frac_of_copy": round(achieved / copy_gbs, 4)},
+                     "frac_of_copy": round(step_gbs / copy_gbs, 4),
+                     "main_kernel": {"kernel": kernel_name,
+                                     "avg_us": round(k_avg_ms * 1e3, 2),
+                                     "median_us": round(k_med_ms * 1e3, 2),
+                                     "achieved": round(kernel_gbs, 1),
+                                     "frac": round(kernel_gbs / HBM_PEAK_GBS, 4)}},
     }
+    if mfma:
+        rec["roofline"].update(mfma)
 
     if not args.no_cpu_baseline:
         cpu_rec, (o_ref, s_ref) = cpu_baseline(wl, args.cpu_seconds)
         rec["cpu_baseline"] = cpu_rec
         t = call()
         torch.cuda.synchronize()
+        ro = error_report(t["o"].cpu().numpy(), o_ref, wl.cu_seqlens)
+        rs = error_report(t["st"].cpu().numpy(), s_ref, kind="state")
         rec["parity"] = {
-            "max_block_err_o": float(max_block_error(t["o"].cpu().numpy(), o_ref, wl.cu_seqlens)),
-            "max_block_err_state": float(max_block_error(t["st"].cpu().numpy(), s_ref, kind="state")),
+            "max_block_err_o": ro["block"], "max_block_err_state": rs["block"],
+            "max_row_err_o": ro["row"], "max_row_err_state": rs["row"],
+            "max_elem_err_floored_o": ro["elem_floored"],
             "tol": cfg.tolerance}
     print(json.dumps(rec), flush=True)
 
