@@ -122,36 +122,45 @@ void (*layernorm_kernel_for(int nv))(const float *, const float *, const float *
 
 constexpr int kCmpRows = 32;      // tokens per workgroup (two 16-token tiles)
 constexpr int kCmpCols = 64;      // outputs per workgroup (four 16-output tiles)
-constexpr int kCmpK = 256;        // d_model slice staged through LDS per step
-constexpr int kCmpPitch = kCmpK + 8;                     // LDS row pitch in bf16 (528 B)
+constexpr int kCmpK = 256;        // d_model slice per step (512-byte row pieces)
 constexpr int kCmpThreads = 512;  // eight waves: 32 tokens x 32 outputs each, a quarter of every slice
-constexpr int kCmpXLoads = kCmpRows * kCmpK / 8 / kCmpThreads;   // 16-byte pieces per thread and step: 1
-constexpr int kCmpWLoads = kCmpCols * kCmpK / 8 / kCmpThreads;   // 2
+constexpr int kCmpBufs = 3;       // slices in LDS: one being read, two loading
+constexpr int kCmpPieces = kCmpK / 8;                              // 16-byte pieces per row slice
+constexpr int kCmpSliceRows = kCmpRows + kCmpCols;                 // x rows, then weight rows
+constexpr int kCmpRowsPerLoad = 64 / kCmpPieces;                   // rows one wave instruction covers
+constexpr int kCmpLoadsPerWave = kCmpSliceRows / kCmpRowsPerLoad / (kCmpThreads / 64);
+static_assert(kCmpLoadsPerWave * kCmpRowsPerLoad * (kCmpThreads / 64) == kCmpSliceRows, "whole slice per step");
 
 struct alignas(16) CmpSmem {
-    uint16_t x[2][kCmpRows][kCmpPitch];   // token rows of the slice, double-buffered
-    uint16_t w[2][kCmpCols][kCmpPitch];   // weight rows of the slice
-};
-
-// One step's global loads, held in registers until they are written to LDS.
-struct CmpRegs {
-    u32x4 x[kCmpXLoads], w[kCmpWLoads];
+    uint16_t buf[kCmpBufs][kCmpSliceRows][kCmpK];   // 3 x 48 KB, rows unpadded, 16-byte pieces swizzled
 };
 
 __device__ __forceinline__ f32x4 mfma(bf16x8 a, bf16x8 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
+using lds_void = __attribute__((address_space(3))) void;
+
+// s_waitcnt immediates (gfx9 encoding: vmcnt bits 3:0, expcnt 6:4, lgkmcnt
+// 11:8): wait until at most N vector-memory operations of this wave are
+// outstanding, leaving the other counters unconstrained
+constexpr int kWaitVm0 = 0xF70;
+constexpr int kWaitVmAhead = 0xF70 | (kCmpLoadsPerWave * (kCmpBufs - 2));   // later slices may be in flight
+static_assert(kCmpLoadsPerWave * (kCmpBufs - 2) < 16, "vmcnt field");
+
 // Workgroup: 32 tokens x 64 outputs over the whole of d_model, in slices of
-// 256.  Each slice is loaded as whole 128-byte lines (the 32 lanes of a row
-// read its 512 contiguous bytes; a load that names a row as a 16-byte piece
-// per lane per MFMA operand would fetch 16 half lines per instruction), two
-// slices ahead of the arithmetic, and written to LDS rows of 528 bytes, whose
-// 16-byte shift per row keeps the operand reads free of bank conflicts.  Wave
-// v computes all 32 tokens against outputs n0 + 32 (v % 2) .. + 31 (2 x 2
-// tiles of 16 x 16, each operand read once for two products) over the
-// quarter v / 2 of every slice; the four quarters' partial tiles are added
-// through LDS at the end.
+// 256.  Each slice goes from global memory straight into LDS
+// (global_load_lds_dwordx4: a wave instruction writes 1 KB, two whole
+// 512-byte rows, contiguously): no registers and no LDS store instructions on
+// the way.  The 16-byte piece that lane L of a load writes (slot L % 32 of row
+// r) is the global piece (L % 32) ^ (r % 16) of that row, so each row is
+// stored XOR-swizzled and the operand reads -- 16 rows at one piece -- fall
+// on 16 different bank groups.  Three slices are in LDS at once (one read,
+// two loading), with one barrier per slice; five 128-wide slices in flight
+// instead were measured slower.  Wave v computes all 32 tokens against
+// outputs n0 + 32 (v % 2) .. + 31 (2 x 2 tiles of 16 x 16, each operand read
+// once for two products) over the quarter v / 2 of every slice; the four
+// quarters' partial tiles are added through LDS at the end.
 template <bool OutBf16>
 __global__ __launch_bounds__(kCmpThreads) void gold_compress_kernel(const uint16_t *x, const uint16_t *w, void *c,
                                                                     int64_t M, int K, int N) {
@@ -163,84 +172,79 @@ __global__ __launch_bounds__(kCmpThreads) void gold_compress_kernel(const uint16
     const int n0 = blockIdx.y * kCmpCols;
     const int steps = K / kCmpK;
 
-    // load piece q = tid + 256 j: row q / 32, 16-byte piece q % 32 of the row's slice
-    const uint16_t *xg[kCmpXLoads], *wg[kCmpWLoads];
-    int xl[kCmpXLoads], wl[kCmpWLoads];
+    // load j of this wave covers slice rows 2q, 2q + 1 (q = wave + 8 j); lane
+    // L takes row 2q + L / 32, global piece (L % 32) ^ (row % 16)
+    const uint16_t *src[kCmpLoadsPerWave];
+    int dst[kCmpLoadsPerWave];
     #pragma unroll
-    for (int j = 0; j < kCmpXLoads; ++j) {
-        const int q = tid + kCmpThreads * j, row = q >> 5, col = (q & 31) * 8;
-        int64_t m = m0 + row;
-        if (m >= M) m = M - 1;                              // rows past M: loaded, never stored
-        xg[j] = x + (size_t)m * K + col;
-        xl[j] = row * kCmpPitch + col;
+    for (int j = 0; j < kCmpLoadsPerWave; ++j) {
+        const int q = wave + (kCmpThreads / 64) * j, row = kCmpRowsPerLoad * q + lane / kCmpPieces;
+        const int piece = (lane % kCmpPieces) ^ (row & 15);
+        const uint16_t *base;
+        if (row < kCmpRows) {
+            int64_t m = m0 + row;
+            if (m >= M) m = M - 1;                          // rows past M: loaded, never stored
+            base = x + (size_t)m * K;
+        } else {
+            base = w + (size_t)(n0 + row - kCmpRows) * K;
+        }
+        src[j] = base + 8 * piece;
+        dst[j] = kCmpRowsPerLoad * q * kCmpK;               // element offset of the 1 KB block
     }
-    #pragma unroll
-    for (int j = 0; j < kCmpWLoads; ++j) {
-        const int q = tid + kCmpThreads * j, row = q >> 5, col = (q & 31) * 8;
-        wg[j] = w + (size_t)(n0 + row) * K + col;
-        wl[j] = row * kCmpPitch + col;
-    }
-    // slice s (clamped to the last one: the look-ahead past the end reloads it)
-    auto load = [&](CmpRegs &P, int s) {
-        const int k0 = (s < steps ? s : steps - 1) * kCmpK;
+    auto load = [&](int s) {                                // slice s into buffer s % 3 (no-op past the end)
+        if (s >= steps) return;
+        uint16_t *b = &sm.buf[s % kCmpBufs][0][0];
+        const int k0 = s * kCmpK;
         #pragma unroll
-        for (int j = 0; j < kCmpXLoads; ++j) P.x[j] = *reinterpret_cast<const u32x4 *>(xg[j] + k0);
-        #pragma unroll
-        for (int j = 0; j < kCmpWLoads; ++j) P.w[j] = *reinterpret_cast<const u32x4 *>(wg[j] + k0);
-        __builtin_amdgcn_sched_barrier(0);                  // keep the loads where they are issued
+        for (int j = 0; j < kCmpLoadsPerWave; ++j)
+            __builtin_amdgcn_global_load_lds(src[j] + k0, (lds_void *)(b + dst[j]), 16, 0, 0);
     };
-    auto stash = [&](const CmpRegs &P, int buf) {
-        #pragma unroll
-        for (int j = 0; j < kCmpXLoads; ++j) *reinterpret_cast<u32x4 *>(&sm.x[buf][0][0] + xl[j]) = P.x[j];
-        #pragma unroll
-        for (int j = 0; j < kCmpWLoads; ++j) *reinterpret_cast<u32x4 *>(&sm.w[buf][0][0] + wl[j]) = P.w[j];
+    // operand read: piece p of slice row r sits in slot p ^ (r % 16)
+    auto read = [&](const uint16_t *b, int row, int piece) {
+        return *reinterpret_cast<const bf16x8 *>(b + row * kCmpK + 8 * (piece ^ (row & 15)));
     };
-    // MFMA operands: lane (i16, grp) takes d_model slots 32u + 8grp .. +7 of
-    // weight rows 32nh + 16a + i16 (A) and of token rows 16b + i16 (B), for
-    // the two substeps u of this wave's quarter of the slice
     const int nh = wave & 1, kq = wave >> 1;
     f32x4 acc[2][2] = {{f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}},
                        {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}}};
-    auto compute = [&](int buf) {
+    auto compute = [&](int s) {
+        const uint16_t *b = &sm.buf[s % kCmpBufs][0][0];
         #pragma unroll
         for (int u = 2 * kq; u < 2 * kq + 2; ++u) {
-            const int k = 32 * u + 8 * grp;
-            bf16x8 a[2], b[2];
+            const int piece = 4 * u + grp;                  // d_model slots 32u + 8grp .. +7
+            bf16x8 a[2], bb[2];
             #pragma unroll
             for (int t = 0; t < 2; ++t) {
-                a[t] = *reinterpret_cast<const bf16x8 *>(&sm.w[buf][32 * nh + 16 * t + i16][k]);
-                b[t] = *reinterpret_cast<const bf16x8 *>(&sm.x[buf][16 * t + i16][k]);
+                a[t] = read(b, kCmpRows + 32 * nh + 16 * t + i16, piece);
+                bb[t] = read(b, 16 * t + i16, piece);
             }
             #pragma unroll
             for (int ta = 0; ta < 2; ++ta)
                 #pragma unroll
-                for (int tb = 0; tb < 2; ++tb) acc[ta][tb] = mfma(a[ta], b[tb], acc[ta][tb]);
+                for (int tb = 0; tb < 2; ++tb) acc[ta][tb] = mfma(a[ta], bb[tb], acc[ta][tb]);
         }
     };
 
-    // two register sets: while slice s is computed from LDS, slice s + 1 is
-    // written to the other LDS buffer and slice s + 2 is in flight (steps is
-    // even)
-    CmpRegs P0, P1;
-    load(P0, 0);
-    load(P1, 1);
-    stash(P0, 0);
-    __syncthreads();
-    for (int s = 0; s < steps; s += 2) {
-        load(P0, s + 2);
-        compute(0);
-        stash(P1, 1);
-        __syncthreads();
-        load(P1, s + 3);
-        compute(1);
-        stash(P0, 0);
-        __syncthreads();
+    #pragma unroll
+    for (int s = 0; s < kCmpBufs - 1; ++s) load(s);
+    for (int s = 0; s < steps; ++s) {
+        // this wave's loads of slice s are complete (later ones may not be),
+        // then everyone's are, and every wave has finished reading slice s - 1
+        // (a plain barrier: __syncthreads' fence would wait for the later
+        // slices too; every LDS read of slice s - 1 has returned, its products
+        // used them)
+        if (s + kCmpBufs - 2 < steps)
+            __builtin_amdgcn_s_waitcnt(kWaitVmAhead);
+        else
+            __builtin_amdgcn_s_waitcnt(kWaitVm0);
+        __builtin_amdgcn_s_barrier();
+        load(s + kCmpBufs - 1);                             // into the buffer slice s - 1 used
+        compute(s);
     }
+    __syncthreads();
 
-    // the four quarters' partial tiles, through LDS (the operand buffers are
-    // free after the last barrier): part[kq][nh][tile][lane], then wave v adds
-    // the quarters of tile v / 2 of output half v % 2 and stores it
-    f32x4 *part = reinterpret_cast<f32x4 *>(&sm.x[0][0][0]);   // 32 KB
+    // the four quarters' partial tiles, through LDS: part[kq][nh][tile][lane],
+    // then wave v adds the quarters of tile v / 2 of output half v % 2 and stores it
+    f32x4 *part = reinterpret_cast<f32x4 *>(&sm.buf[0][0][0]);   // 32 KB (buffers 0 and 1)
     #pragma unroll
     for (int ta = 0; ta < 2; ++ta)
         #pragma unroll
@@ -280,7 +284,7 @@ hipError_t launch_layernorm_rows(const float *x, const float *gamma, const float
 hipError_t launch_gold_compress(const uint16_t *x, const uint16_t *w, void *c, bool out_bf16, int64_t M, int K,
                                 int N, hipStream_t st, KernelTiming tm) {
     if (M <= 0) return hipSuccess;
-    if (K % (4 * kCmpK) != 0 || N % kCmpCols != 0) return hipErrorInvalidValue;
+    if (K % kCmpK != 0 || N % kCmpCols != 0) return hipErrorInvalidValue;
     const dim3 grid((unsigned)((M + kCmpRows - 1) / kCmpRows), (unsigned)(N / kCmpCols));
     if (out_bf16)
         hipExtLaunchKernelGGL(gold_compress_kernel<true>, grid, dim3(kCmpThreads), 0, st, tm.start, tm.stop, 0,
