@@ -71,7 +71,9 @@ void layout_workspace(Plan &p, bool varlen) {
     const size_t items = (size_t)p.g.n_seg * p.g.H;
     if (p.split) {
         p.off_seg_state = off;
-        off = align256(off + items * kSegStateFloats * sizeof(float));
+        // aggregates only for segments that are not the last of their sequence
+        const size_t aggs = (size_t)(p.g.n_seg - p.g.n_seq) * p.g.H;
+        off = align256(off + aggs * kSegStateFloats * sizeof(float));
         p.off_seg_start = off;
         off = align256(off + items * kSegStartFloats * sizeof(float));
     }

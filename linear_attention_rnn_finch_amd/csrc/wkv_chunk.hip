@@ -74,8 +74,6 @@ constexpr int kTileElems = kChunk * kHeadDim; // one 64 x 64 bf16 tile
 constexpr int kStageRow = 72;                  // staging row pitch in bf16 (144 B)
 constexpr int kStageElems = kChunk * kStageRow;
 
-enum class Mode { Main, State };
-
 // Registers holding one prefetched chunk: r, k, w, v (and the C2 second
 // value) as 16-byte pieces of whole token rows (rows tid/8 and tid/8 + 32,
 // piece tid%8), so that every load instruction covers complete 128-byte lines.
@@ -384,15 +382,12 @@ __device__ __forceinline__ float one_minus_w(float x, float e) {
 }
 
 // One segment of one head, chunk by chunk, from the state S in registers
-// (lane (i16, grp) of wave w holds S[16*ib + 4*grp + e][16*w + i16]).
-//  - Main: o of every token is stored; S ends as the state after the segment.
-//  - State: nothing is stored; S ends as the segment's zero-start aggregate
-//    when it starts at zero, and lam_seg (lanes with i16 == 15, channels
-//    c0 .. c0+3) accumulates the segment's total log2-decay.
-template <Mode M, bool LOGD, bool C2, typename SM>
+// (lane (i16, grp) of wave w holds S[16*ib + 4*grp + e][16*w + i16]): o of
+// every token is stored and S ends as the state after the segment.
+template <bool LOGD, bool C2, typename SM>
 __device__ __forceinline__ void scan_chunks(SM &sm, const Tensors &t, int64_t seg_t0, int64_t seg_t1,
-                                            int h, int H, float (&S)[4][4], float (&lam_seg)[4]) {
-    constexpr bool kU2 = M == Mode::Main && C2;            // second value staged and added
+                                            int h, int H, float (&S)[4][4]) {
+    constexpr bool kU2 = C2;                               // second value staged and added
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lane = tid & 63;
@@ -403,7 +398,7 @@ __device__ __forceinline__ void scan_chunks(SM &sm, const Tensors &t, int64_t se
     // pre-processing layout: channels c0..c0+3, tokens 4*i16 .. 4*i16+3
     const int c0 = 16 * wave + 4 * grp;
     f32x4 u4 = {0.f, 0.f, 0.f, 0.f};
-    if (M == Mode::Main && !C2) u4 = *reinterpret_cast<const f32x4 *>(t.u + (size_t)h * kHeadDim + c0);
+    if (!C2) u4 = *reinterpret_cast<const f32x4 *>(t.u + (size_t)h * kHeadDim + c0);
 
 
     const uint16_t *gr = static_cast<const uint16_t *>(t.r);
@@ -442,7 +437,7 @@ __device__ __forceinline__ void scan_chunks(SM &sm, const Tensors &t, int64_t se
         const Rsrc rk = chunk_rsrc(t.k, tc, rows, H, h, kRowIn);
         const Rsrc rw = chunk_rsrc(t.w, tc, rows, H, h, kRowIn);
         const Rsrc rv = chunk_rsrc(t.v, tc, rows, H, h, kRowIn);
-        if (M == Mode::Main) {
+        {
             const Rsrc rr = chunk_rsrc(t.r, tc, rows, H, h, kRowIn);
             #pragma unroll
             for (int m = 0; m < 2; ++m) P.r[m] = __builtin_amdgcn_raw_buffer_load_b128(rr, off_vin[m], 0, 0);
@@ -512,10 +507,10 @@ __device__ __forceinline__ void scan_chunks(SM &sm, const Tensors &t, int64_t se
             lds_write_b128(sm.v, lb.vw + 64 * 32 * m, P.v[m]);
             lds_write_b128(sm.stage[1], st_wr[m], P.k[m]);
             lds_write_b128(sm.stage[2], st_wr[m], P.w[m]);
-            if (M == Mode::Main) lds_write_b128(sm.stage[0], st_wr[m], P.r[m]);
+            lds_write_b128(sm.stage[0], st_wr[m], P.r[m]);
             if constexpr (kU2) lds_write_b128(sm.stage[3], st_wr[m], P.u2[m]);
         }
-        if (M == Mode::Main && c > 0) store_o();
+        if (c > 0) store_o();
         if (c + 1 < n_chunks) issue_loads(P, tc + kChunk);
         __syncthreads();
 
@@ -525,7 +520,7 @@ __device__ __forceinline__ void scan_chunks(SM &sm, const Tensors &t, int64_t se
         for (int a = 0; a < 4; ++a) {
             pk[a] = lds_read_b64(sm.stage[1], st_rd[a]);
             pw[a] = lds_read_b64(sm.stage[2], st_rd[a]);
-            if (M == Mode::Main) pr[a] = lds_read_b64(sm.stage[0], st_rd[a]);
+            pr[a] = lds_read_b64(sm.stage[0], st_rd[a]);
         }
         u32x2 pu2[4];
         if constexpr (kU2) {
@@ -545,14 +540,12 @@ __device__ __forceinline__ void scan_chunks(SM &sm, const Tensors &t, int64_t se
             lam[a][2] = bf16_lo(pw[a].y); lam[a][3] = bf16_hi(pw[a].y);
             kk_[a][0] = bf16_lo(pk[a].x); kk_[a][1] = bf16_hi(pk[a].x);
             kk_[a][2] = bf16_lo(pk[a].y); kk_[a][3] = bf16_hi(pk[a].y);
-            if (M == Mode::Main) {
-                rr[a][0] = bf16_lo(pr[a].x); rr[a][1] = bf16_hi(pr[a].x);
-                rr[a][2] = bf16_lo(pr[a].y); rr[a][3] = bf16_hi(pr[a].y);
-            }
+            rr[a][0] = bf16_lo(pr[a].x); rr[a][1] = bf16_hi(pr[a].x);
+            rr[a][2] = bf16_lo(pr[a].y); rr[a][3] = bf16_hi(pr[a].y);
         }
 
         // ---- pre-processing: decay prefix, rescaled operands, bonus ----------
-        if (M == Mode::Main) {
+        {
             // Products of the decays from the chunk start, P_t = w_0 ... w_t per key
             // channel: r~_t = r_t P_{t-1} and k~_s = k_s / P_s multiply to the decay
             // w_{s+1} ... w_{t-1} of the state equation.  lam holds the decay
@@ -613,51 +606,6 @@ __device__ __forceinline__ void scan_chunks(SM &sm, const Tensors &t, int64_t se
                 f32x4 b4 = {bp[0], bp[1], bp[2], bp[3]};
                 *reinterpret_cast<f32x4 *>(&sm.bonus_part[wave][4 * i16]) = b4;
             }
-        } else {
-            // State pass: log2 decays relative to the chunk end, k~_s = k_s
-            // 2^{Lam_63 - Lam_s} <= k_s (no factor exceeds 1, so it needs no
-            // token-serial fallback).  lam holds the decay inputs (w, or d).
-            #pragma unroll
-            for (int a = 0; a < 4; ++a)
-                #pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const float x = lam[a][q];
-                    const float e = LOGD ? __builtin_amdgcn_exp2f(x * kLog2e) : 0.f;   // exp(d)
-                    if (C2) kk_[a][q] *= one_minus_w<LOGD>(x, e);
-                    lam[a][q] = fmaxf(LOGD ? -e * kLog2e : __builtin_amdgcn_logf(x), kLog2Floor);
-                }
-            // inclusive prefix over the chunk: in-lane over 4 tokens, then across
-            // the 16 lanes; lam becomes Lam_t - Lam_63
-            float total[4];
-            #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                lam[1][q] += lam[0][q];
-                lam[2][q] += lam[1][q];
-                lam[3][q] += lam[2][q];
-                const float incl = row_scan16(lam[3][q]);
-                total[q] = row_bcast<15>(incl);                         // Lam_63
-                const float off = (incl - lam[3][q]) - total[q];
-                #pragma unroll
-                for (int a = 0; a < 4; ++a) lam[a][q] += off;
-            }
-            if (i16 == 15) {
-                #pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    sm.row_dec[c0 + q] = __builtin_amdgcn_exp2f(total[q]);
-                    lam_seg[q] += total[q];
-                }
-            }
-            #pragma unroll
-            for (int a = 0; a < 4; ++a) {
-                float ks[4];
-                #pragma unroll
-                for (int q = 0; q < 4; ++q)
-                    ks[q] = kk_[a][q] * __builtin_amdgcn_exp2f(-lam[a][q]);   // Lam_63 - Lam_t
-                u32x2 kh, kl;
-                split4(ks[0], ks[1], ks[2], ks[3], kh, kl);
-                lds_write_b64(sm.kt_hi, lb.pw_kt[a], kh);
-                lds_write_b64(sm.kt_lo, lb.pw_kt[a], kl);
-            }
         }
         __syncthreads();
 
@@ -667,32 +615,6 @@ __device__ __forceinline__ void scan_chunks(SM &sm, const Tensors &t, int64_t se
         vop[0] = col_op(sm.v, lb.tr_v, 0);
         vop[1] = col_op(sm.v, lb.tr_v, 1);
 
-        if (M == Mode::State) {
-            f32x4 p[4];
-            #pragma unroll
-            for (int ib = 0; ib < 4; ++ib) p[ib] = f32x4{0.f, 0.f, 0.f, 0.f};
-            #pragma unroll
-            for (int kk = 0; kk < 2; ++kk) {
-                bf16x8 k_hi[4], k_lo[4];
-                #pragma unroll
-                for (int ib = 0; ib < 4; ++ib) {
-                    k_hi[ib] = kt_col_op(sm.kt_hi, lb.tr_kt[ib], kk);
-                    k_lo[ib] = kt_col_op(sm.kt_lo, lb.tr_kt[ib], kk);
-                }
-                #pragma unroll
-                for (int ib = 0; ib < 4; ++ib) p[ib] = mfma(k_hi[ib], vop[kk], p[ib]);
-                #pragma unroll
-                for (int ib = 0; ib < 4; ++ib) p[ib] = mfma(k_lo[ib], vop[kk], p[ib]);
-            }
-            #pragma unroll
-            for (int ib = 0; ib < 4; ++ib) {
-                const f32x4 dec = *reinterpret_cast<const f32x4 *>(&sm.row_dec[16 * ib + 4 * grp]);
-                #pragma unroll
-                for (int e = 0; e < 4; ++e) S[ib][e] = dec[e] * S[ib][e] + p[ib][e];
-            }
-            __syncthreads();
-            continue;
-        }
 
         const bool stiff = (sm.stiff[0] | sm.stiff[1] | sm.stiff[2] | sm.stiff[3]) != 0;
         f32x4 acc[4];
@@ -863,8 +785,170 @@ __device__ __forceinline__ void scan_chunks(SM &sm, const Tensors &t, int64_t se
         nt_pend = nt;
         __syncthreads();
     }
-    if (M == Mode::Main && n_chunks > 0) store_o();
+    if (n_chunks > 0) store_o();
 
+}
+
+// LDS of the state pass: the staging tile of the raw k and w rows shares its
+// space with the k~ planes (the pre-processing reads every staged row into
+// registers, a barrier, then writes the planes), 26 KB in all, so that four
+// state workgroups fit on a compute unit.
+struct SmemState {
+    uint16_t v[kTileElems];                      // values of the chunk
+    union {
+        struct {
+            uint16_t kt_hi[kTileElems];          // k~ = k 2^{Lam_63 - Lam_s}, bf16 hi/lo planes
+            uint16_t kt_lo[kTileElems];
+        };
+        uint16_t stage[2][kStageElems];          // raw k, w rows of the chunk
+    };
+    alignas(16) float row_dec[kHeadDim];         // decay of the whole chunk per key channel
+};
+static_assert(sizeof(SmemState) <= 40 * 1024, "four state workgroups per CU");
+
+// The state pass over one run of tokens (zero start): S ends as the run's
+// aggregate B = sum_s diag(P_end / P_s) k_s^T v_s and lam_seg (lanes with
+// i16 == 15, channels c0 .. c0+3) as its total log2-decay.  One chunk is
+// prefetched ahead (keeping two or three chunks of each item in flight was
+// measured slower).
+template <bool LOGD, bool C2>
+__device__ __forceinline__ void state_run(SmemState &sm, const Tensors &t, int64_t t0, int64_t t1, int h, int H,
+                                          float (&S)[4][4], float (&lam_seg)[4]) {
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63;
+    const int i16 = lane & 15;
+    const int grp = lane >> 4;
+    const LdsBases lb = make_bases(tid);
+    const int c0 = 16 * wave + 4 * grp;
+    const int ld_row = tid >> 3;
+    const int ld_col = (tid & 7) * 8;
+    constexpr int kRowIn = kHeadDim * 2;
+    int off_vin[2], st_wr[2], st_rd[4];
+    #pragma unroll
+    for (int m = 0; m < 2; ++m) {
+        off_vin[m] = (ld_row + 32 * m) * H * kRowIn + 2 * ld_col;
+        st_wr[m] = off_stage(ld_row + 32 * m, tid & 7);
+    }
+    #pragma unroll
+    for (int a = 0; a < 4; ++a) st_rd[a] = off_stage(4 * i16 + a, 2 * wave + (grp >> 1)) + 4 * (grp & 1);
+
+    u32x4 Qk[2], Qw[2], Qv[2];
+    auto issue = [&](int64_t tc) {
+        const int rows = (int)max<int64_t>(min<int64_t>(kChunk, t1 - tc), 0);
+        const Rsrc rk = chunk_rsrc(t.k, tc, rows, H, h, kRowIn);
+        const Rsrc rw = chunk_rsrc(t.w, tc, rows, H, h, kRowIn);
+        const Rsrc rv = chunk_rsrc(t.v, tc, rows, H, h, kRowIn);
+        #pragma unroll
+        for (int m = 0; m < 2; ++m) {
+            Qk[m] = __builtin_amdgcn_raw_buffer_load_b128(rk, off_vin[m], 0, 0);
+            Qw[m] = __builtin_amdgcn_raw_buffer_load_b128(rw, off_vin[m], 0, 0);
+            Qv[m] = __builtin_amdgcn_raw_buffer_load_b128(rv, off_vin[m], 0, 0);
+        }
+    };
+
+    const int n_chunks = (int)((t1 - t0 + kChunk - 1) / kChunk);
+    if (n_chunks > 0) issue(t0);
+    for (int c = 0; c < n_chunks; ++c) {
+        const int64_t tc = t0 + (int64_t)c * kChunk;
+        const int nt = (int)min<int64_t>(kChunk, t1 - tc);
+        #pragma unroll
+        for (int m = 0; m < 2; ++m) {
+            lds_write_b128(sm.v, lb.vw + 64 * 32 * m, Qv[m]);
+            lds_write_b128(sm.stage[0], st_wr[m], Qk[m]);
+            lds_write_b128(sm.stage[1], st_wr[m], Qw[m]);
+        }
+        if (c + 1 < n_chunks) issue(tc + kChunk);
+        __syncthreads();
+        u32x2 pk[4], pw[4];
+        #pragma unroll
+        for (int a = 0; a < 4; ++a) {
+            pk[a] = lds_read_b64(sm.stage[0], st_rd[a]);
+            pw[a] = lds_read_b64(sm.stage[1], st_rd[a]);
+        }
+        if (nt < kChunk) {                      // partial chunk: w = 1 on padding rows
+            constexpr unsigned kPad = LOGD ? kNegInfPair : kOnePair;
+            #pragma unroll
+            for (int a = 0; a < 4; ++a)
+                if (4 * i16 + a >= nt) pw[a] = u32x2{kPad, kPad};
+        }
+        float lam[4][4], kk_[4][4];
+        #pragma unroll
+        for (int a = 0; a < 4; ++a) {
+            lam[a][0] = bf16_lo(pw[a].x); lam[a][1] = bf16_hi(pw[a].x);
+            lam[a][2] = bf16_lo(pw[a].y); lam[a][3] = bf16_hi(pw[a].y);
+            kk_[a][0] = bf16_lo(pk[a].x); kk_[a][1] = bf16_hi(pk[a].x);
+            kk_[a][2] = bf16_lo(pk[a].y); kk_[a][3] = bf16_hi(pk[a].y);
+        }
+        // log2 decays relative to the chunk end, k~_s = k_s 2^{Lam_63 - Lam_s}
+        // <= k_s (no factor exceeds 1, so no token-serial fallback is needed)
+        #pragma unroll
+        for (int a = 0; a < 4; ++a)
+            #pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const float x = lam[a][q];
+                const float e = LOGD ? __builtin_amdgcn_exp2f(x * kLog2e) : 0.f;   // exp(d)
+                if (C2) kk_[a][q] *= one_minus_w<LOGD>(x, e);
+                lam[a][q] = fmaxf(LOGD ? -e * kLog2e : __builtin_amdgcn_logf(x), kLog2Floor);
+            }
+        float total[4];
+        #pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            lam[1][q] += lam[0][q];
+            lam[2][q] += lam[1][q];
+            lam[3][q] += lam[2][q];
+            const float incl = row_scan16(lam[3][q]);
+            total[q] = row_bcast<15>(incl);                         // Lam_63
+            const float off = (incl - lam[3][q]) - total[q];
+            #pragma unroll
+            for (int a = 0; a < 4; ++a) lam[a][q] += off;
+        }
+        if (i16 == 15) {
+            #pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                sm.row_dec[c0 + q] = __builtin_amdgcn_exp2f(total[q]);
+                lam_seg[q] += total[q];
+            }
+        }
+        __syncthreads();                       // every staged row is read: the planes may overwrite them
+        #pragma unroll
+        for (int a = 0; a < 4; ++a) {
+            float ks[4];
+            #pragma unroll
+            for (int q = 0; q < 4; ++q) ks[q] = kk_[a][q] * __builtin_amdgcn_exp2f(-lam[a][q]);
+            u32x2 kh, kl;
+            split4(ks[0], ks[1], ks[2], ks[3], kh, kl);
+            lds_write_b64(sm.kt_hi, lb.pw_kt[a], kh);
+            lds_write_b64(sm.kt_lo, lb.pw_kt[a], kl);
+        }
+        __syncthreads();
+        bf16x8 vop[2];
+        vop[0] = col_op(sm.v, lb.tr_v, 0);
+        vop[1] = col_op(sm.v, lb.tr_v, 1);
+        f32x4 pp[4];
+        #pragma unroll
+        for (int ib = 0; ib < 4; ++ib) pp[ib] = f32x4{0.f, 0.f, 0.f, 0.f};
+        #pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+            bf16x8 k_hi[4], k_lo[4];
+            #pragma unroll
+            for (int ib = 0; ib < 4; ++ib) {
+                k_hi[ib] = kt_col_op(sm.kt_hi, lb.tr_kt[ib], kk);
+                k_lo[ib] = kt_col_op(sm.kt_lo, lb.tr_kt[ib], kk);
+            }
+            #pragma unroll
+            for (int ib = 0; ib < 4; ++ib) pp[ib] = mfma(k_hi[ib], vop[kk], pp[ib]);
+            #pragma unroll
+            for (int ib = 0; ib < 4; ++ib) pp[ib] = mfma(k_lo[ib], vop[kk], pp[ib]);
+        }
+        #pragma unroll
+        for (int ib = 0; ib < 4; ++ib) {
+            const f32x4 dec = *reinterpret_cast<const f32x4 *>(&sm.row_dec[16 * ib + 4 * grp]);
+            #pragma unroll
+            for (int e = 0; e < 4; ++e) S[ib][e] = dec[e] * S[ib][e] + pp[ib][e];
+        }
+        __syncthreads();                       // planes and values read before the next staging
+    }
 }
 
 __device__ __forceinline__ void load_public_state(const float *src, float (&S)[4][4]) {
@@ -885,17 +969,17 @@ __device__ __forceinline__ void store_public_state(float *dst, const float (&S)[
 }
 
 // State pass: the zero-start aggregate of every segment but the last of its
-// sequence, B_p (D*D, [key][value]) followed by the segment's total log2-decay
-// per key channel (D).  One chunk is prefetched ahead: keeping two or three
-// chunks of every item in flight was measured slower (HBM serves the strided
-// 128-byte row pieces of more chunks at once less efficiently).
+// sequence: B (D*D, [key][value]) followed by the segment's total log2-decay
+// per key channel (D), stored at index (s - n) * H + h for global segment s of
+// sequence n.  Shorter items (segments split into two or four runs, four
+// workgroups per compute unit) were measured slower.
 template <bool LOGD, bool C2>
-__global__ __launch_bounds__(256, 2) void wkv_state_kernel(Geometry g, Tensors t, Workspace ws) {
-    using SM = Smem<3>;
-    __shared__ SM sm;
+__global__ __launch_bounds__(256, C2 ? 3 : 4) void wkv_state_kernel(Geometry g, Tensors t, Workspace ws) {
+    __shared__ SmemState sm;
     const int item = blockIdx.x;
     const int h = item % g.H;
-    const ItemRange it = decode_segment(g, item / g.H);
+    const int seg = item / g.H;
+    const ItemRange it = decode_segment(g, seg);
     if (!it.valid || it.p == it.P - 1) return;           // the last segment's aggregate is unused
     if (ws.seg_state == nullptr) return;                 // a split the host did not plan
     float S[4][4], lam[4] = {0.f, 0.f, 0.f, 0.f};
@@ -903,8 +987,8 @@ __global__ __launch_bounds__(256, 2) void wkv_state_kernel(Geometry g, Tensors t
     for (int ib = 0; ib < 4; ++ib)
         #pragma unroll
         for (int e = 0; e < 4; ++e) S[ib][e] = 0.f;
-    scan_chunks<Mode::State, LOGD, C2>(sm, t, it.t0, it.t1, h, g.H, S, lam);
-    float *dst = ws.seg_state + (size_t)item * kSegStateFloats;
+    state_run<LOGD, C2>(sm, t, it.t0, it.t1, h, g.H, S, lam);
+    float *dst = ws.seg_state + ((size_t)(seg - it.n) * g.H + h) * kSegStateFloats;
     store_public_state(dst, S);
     const int tid = threadIdx.x;
     if ((tid & 15) == 15) {
@@ -952,7 +1036,7 @@ __global__ __launch_bounds__(kScanThreads) void wkv_segment_scan_kernel(Geometry
             b[q] = f32x4{0.f, 0.f, 0.f, 0.f};
             lam[q] = 0.f;
             if (p0 + q < P - 1) {
-                const float *agg = ws.seg_state + ((size_t)(first + p0 + q) * g.H + h) * kSegStateFloats;
+                const float *agg = ws.seg_state + ((size_t)(first - n + p0 + q) * g.H + h) * kSegStateFloats;
                 b[q] = *reinterpret_cast<const f32x4 *>(agg + idx);
                 lam[q] = agg[kHeadDim * kHeadDim + row];
             }
@@ -985,14 +1069,14 @@ __global__ __launch_bounds__(256, 2) void wkv_chunk_kernel(Geometry g, Tensors t
     // a split the host did not plan (device offsets differing from the host
     // copy) has no workspace behind it: leave the item alone
     if (it.P > 1 && ws.seg_start == nullptr) return;
-    float S[4][4], lam[4] = {0.f, 0.f, 0.f, 0.f};
+    float S[4][4];
     const float *s_src = nullptr;
     if (it.P > 1)
         s_src = ws.seg_start + (size_t)item * kSegStartFloats;
     else if (t.state_in)
         s_src = t.state_in + ((size_t)it.n * g.H + h) * (kHeadDim * kHeadDim);
     load_public_state(s_src, S);
-    scan_chunks<Mode::Main, LOGD, C2>(sm, t, it.t0, it.t1, h, g.H, S, lam);
+    scan_chunks<LOGD, C2>(sm, t, it.t0, it.t1, h, g.H, S);
     if (t.state_out && it.p == it.P - 1)
         store_public_state(t.state_out + ((size_t)it.n * g.H + h) * (kHeadDim * kHeadDim), S);
 }

@@ -117,9 +117,11 @@ struct Variant {
     bool o_bf16 = false;     // o stored as bf16 (round to nearest even)
 };
 
-// Workspace views (fp32).  seg_state[item]: the segment's zero-start end state
-// (D*D) followed by its total log2-decay per key channel (D).  seg_start[item]:
-// the state entering the segment (D*D).
+// Workspace views (fp32).  seg_state[(s - n) * H + h]: the zero-start end
+// state (D*D) of global segment s of sequence n, followed by its total
+// log2-decay per key channel (D); only segments that are not the last of their
+// sequence have one, and s - n numbers them.  seg_start[item]: the state
+// entering the segment (D*D).
 struct Workspace {
     float *seg_state;
     float *seg_start;
