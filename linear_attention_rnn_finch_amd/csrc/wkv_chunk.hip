@@ -381,12 +381,27 @@ __device__ __forceinline__ float one_minus_w(float x, float e) {
     return e < 0.03125f ? series : direct;
 }
 
-// One segment of one head, chunk by chunk, from the state S in registers
-// (lane (i16, grp) of wave w holds S[16*ib + 4*grp + e][16*w + i16]): o of
-// every token is stored and S ends as the state after the segment.
+// The 64 x 64 fp32 state in the accumulator layout (lane (i16, grp) of wave
+// w holds S[16*ib + 4*grp + e][16*w + i16]), from [key][value] memory (zeros
+// for a null source).
+__device__ __forceinline__ void load_public_state(const float *src, float (&S)[4][4]) {
+    const int tid = threadIdx.x, wave = tid >> 6, i16 = tid & 15, grp = (tid & 63) >> 4;
+    #pragma unroll
+    for (int ib = 0; ib < 4; ++ib)
+        #pragma unroll
+        for (int e = 0; e < 4; ++e)
+            S[ib][e] = src ? src[(16 * ib + 4 * grp + e) * kHeadDim + 16 * wave + i16] : 0.f;
+}
+
+// One segment of one head, chunk by chunk, from the state at s_src (zeros if
+// null) held in registers: o of every token is stored and S ends as the state
+// after the segment.  The state's loads are issued after the first chunk's,
+// so that the first wait for inputs does not also wait for the state (load
+// counters drain in issue order); the state is first read after the
+// pre-processing of that chunk.
 template <bool LOGD, bool C2, typename SM>
 __device__ __forceinline__ void scan_chunks(SM &sm, const Tensors &t, int64_t seg_t0, int64_t seg_t1,
-                                            int h, int H, float (&S)[4][4]) {
+                                            int h, int H, const float *s_src, float (&S)[4][4]) {
     constexpr bool kU2 = C2;                               // second value staged and added
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -486,6 +501,7 @@ __device__ __forceinline__ void scan_chunks(SM &sm, const Tensors &t, int64_t se
 
     ChunkRegs<kU2> P;
     if (n_chunks > 0) issue_loads(P, seg_t0);
+    load_public_state(s_src, S);
 
     for (int c = 0; c < n_chunks; ++c) {
         const int64_t tc = seg_t0 + (int64_t)c * kChunk;
@@ -951,14 +967,6 @@ __device__ __forceinline__ void state_run(SmemState &sm, const Tensors &t, int64
     }
 }
 
-__device__ __forceinline__ void load_public_state(const float *src, float (&S)[4][4]) {
-    const int tid = threadIdx.x, wave = tid >> 6, i16 = tid & 15, grp = (tid & 63) >> 4;
-    #pragma unroll
-    for (int ib = 0; ib < 4; ++ib)
-        #pragma unroll
-        for (int e = 0; e < 4; ++e)
-            S[ib][e] = src ? src[(16 * ib + 4 * grp + e) * kHeadDim + 16 * wave + i16] : 0.f;
-}
 __device__ __forceinline__ void store_public_state(float *dst, const float (&S)[4][4]) {
     const int tid = threadIdx.x, wave = tid >> 6, i16 = tid & 15, grp = (tid & 63) >> 4;
     #pragma unroll
@@ -1075,8 +1083,7 @@ __global__ __launch_bounds__(256, 2) void wkv_chunk_kernel(Geometry g, Tensors t
         s_src = ws.seg_start + (size_t)item * kSegStartFloats;
     else if (t.state_in)
         s_src = t.state_in + ((size_t)it.n * g.H + h) * (kHeadDim * kHeadDim);
-    load_public_state(s_src, S);
-    scan_chunks<LOGD, C2>(sm, t, it.t0, it.t1, h, g.H, S);
+    scan_chunks<LOGD, C2>(sm, t, it.t0, it.t1, h, g.H, s_src, S);
     if (t.state_out && it.p == it.P - 1)
         store_public_state(t.state_out + ((size_t)it.n * g.H + h) * (kHeadDim * kHeadDim), S);
 }
