@@ -289,14 +289,20 @@ __device__ __forceinline__ float row_scan16(float x) {
     return __int_as_float(v);
 }
 
-// Inclusive product over the 16 lanes of each DPP row (lanes without a
-// source keep the old value, 1).
+// Inclusive product over the 16 lanes of each DPP row, in four steps.  A
+// step multiplies x by the value SHIFT lanes earlier in the row, as one
+// v_mul_f32_dpp whose lanes without such a predecessor are masked off (bound
+// control clear) and so keep x.  (Written out because the compiler does not
+// fold a DPP move with fill value 1 into a float multiply, which costs two
+// more instructions per step.)  s_nop 1 gives the two wait states a DPP read
+// needs after a VALU write of its source.
+#define FINCH_ROW_MUL_SHR(x, SHIFT) \
+    asm("s_nop 1\n\tv_mul_f32_dpp %0, %0, %0 row_shr:" #SHIFT " row_mask:0xf bank_mask:0xf" : "+v"(x))
 __device__ __forceinline__ float row_prod16(float x) {
-    const int one = __float_as_int(1.f);
-    x *= __int_as_float(__builtin_amdgcn_update_dpp(one, __float_as_int(x), 0x111, 0xF, 0xF, false));
-    x *= __int_as_float(__builtin_amdgcn_update_dpp(one, __float_as_int(x), 0x112, 0xF, 0xF, false));
-    x *= __int_as_float(__builtin_amdgcn_update_dpp(one, __float_as_int(x), 0x114, 0xF, 0xF, false));
-    x *= __int_as_float(__builtin_amdgcn_update_dpp(one, __float_as_int(x), 0x118, 0xF, 0xF, false));
+    FINCH_ROW_MUL_SHR(x, 1);
+    FINCH_ROW_MUL_SHR(x, 2);
+    FINCH_ROW_MUL_SHR(x, 4);
+    FINCH_ROW_MUL_SHR(x, 8);
     return x;
 }
 
@@ -394,14 +400,17 @@ __device__ __forceinline__ void load_public_state(const float *src, float (&S)[4
 }
 
 // One segment of one head, chunk by chunk, from the state at s_src (zeros if
-// null) held in registers: o of every token is stored and S ends as the state
-// after the segment.  The state's loads are issued after the first chunk's,
+// null) held in registers: o of every token is stored and, with keep_state, S
+// ends as the state after the segment (without it the last chunk skips the
+// state update: a segment that does not end its sequence hands no state on,
+// its successor starts from the combined start state).  The state's loads are issued after the first chunk's,
 // so that the first wait for inputs does not also wait for the state (load
 // counters drain in issue order); the state is first read after the
 // pre-processing of that chunk.
 template <bool LOGD, bool C2, typename SM>
 __device__ __forceinline__ void scan_chunks(SM &sm, const Tensors &t, int64_t seg_t0, int64_t seg_t1,
-                                            int h, int H, const float *s_src, float (&S)[4][4]) {
+                                            int h, int H, const float *s_src, bool keep_state,
+                                            float (&S)[4][4]) {
     constexpr bool kU2 = C2;                               // second value staged and added
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -740,7 +749,7 @@ __device__ __forceinline__ void scan_chunks(SM &sm, const Tensors &t, int64_t se
         }
         // ---- state update: S = diag(2^Lam63) S + diag(2^{Lam63-R}) k~^T v --------
         // (the read-out above has taken the old S; k~ and v are ready since B1)
-        {
+        if (keep_state || c + 1 < n_chunks) {
             f32x4 p[4];
             #pragma unroll
             for (int ib = 0; ib < 4; ++ib) p[ib] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -1083,8 +1092,9 @@ __global__ __launch_bounds__(256, 2) void wkv_chunk_kernel(Geometry g, Tensors t
         s_src = ws.seg_start + (size_t)item * kSegStartFloats;
     else if (t.state_in)
         s_src = t.state_in + ((size_t)it.n * g.H + h) * (kHeadDim * kHeadDim);
-    scan_chunks<LOGD, C2>(sm, t, it.t0, it.t1, h, g.H, s_src, S);
-    if (t.state_out && it.p == it.P - 1)
+    const bool keep = t.state_out && it.p == it.P - 1;
+    scan_chunks<LOGD, C2>(sm, t, it.t0, it.t1, h, g.H, s_src, keep, S);
+    if (keep)
         store_public_state(t.state_out + ((size_t)it.n * g.H + h) * (kHeadDim * kHeadDim), S);
 }
 
