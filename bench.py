@@ -119,6 +119,8 @@ def measured_traffic(workload_name, kernel_name):
 # issues 268 v_mfma_f32_16x16x32_bf16 (A tiles 10 x 2 K-steps x 3 split
 # products = 60; read-out 4 waves x 4 x 2 x 3 = 96; state update 4 x 4 x 2 x 2
 # = 64; in-chunk pairs 4 x 6 x 2 = 48) and the state pass 64 (4 x 4 x 2 x 2).
+# The last chunk of a segment that does not end its sequence skips the state
+# update (its end state is not used).
 MFMA_FLOPS = 16 * 16 * 32 * 2
 MAIN_MFMA_PER_CHUNK = 268
 STATE_MFMA_PER_CHUNK = 64
@@ -126,20 +128,22 @@ BF16_MFMA_PEAK = 2.5e15          # MI355X dense bf16, FLOP/s
 
 
 def chunk_counts(lengths, H):
-    """(chunked-scan chunks, state-pass chunks) of a bf16 call over sequences of
-    these lengths, with the library's segment plan: about 512 (segment, head)
-    items, segments a multiple of 64 tokens and at least 256, no longer than
-    the longest sequence rounded up to 64."""
+    """(chunked-scan chunks, state-pass chunks, segments that do not end their
+    sequence) of a bf16 call over sequences of these lengths, with the
+    library's segment plan: about 512 (segment, head) items, segments a
+    multiple of 64 tokens and at least 256, no longer than the longest sequence
+    rounded up to 64."""
     up = lambda x, m: -(-x // m) * m
     tokens, max_len = sum(lengths), max(lengths) if lengths else 0
     seg = min(max(up(max(-(-tokens * H // 512), 1), 64), 256), up(max(max_len, 1), 64))
-    main = state = 0
+    main = state = inner = 0
     for L in lengths:
         P = 1 if L == 0 else -(-L // seg)
         main += -(-L // 64)
         if P > 1:
             state += (P - 1) * seg // 64
-    return main * H, state * H
+            inner += P - 1
+    return main * H, state * H, inner * H
 
 
 def time_calls(call, n, torch):
@@ -417,12 +421,12 @@ def main():
     lengths = [int(x) for x in np.diff(wl.cu_seqlens)] if wl.packed else [cfg.T] * cfg.B
     mfma = None
     if chunked:
-        main_chunks, state_chunks = chunk_counts(lengths, cfg.H)
-        flops = MFMA_FLOPS * (MAIN_MFMA_PER_CHUNK * main_chunks + STATE_MFMA_PER_CHUNK * state_chunks)
+        main_chunks, state_chunks, inner = chunk_counts(lengths, cfg.H)
+        main_flops = MFMA_FLOPS * (MAIN_MFMA_PER_CHUNK * main_chunks - STATE_MFMA_PER_CHUNK * inner)
+        flops = main_flops + MFMA_FLOPS * STATE_MFMA_PER_CHUNK * state_chunks
         mfma = {"issued_flops_per_call": flops,
                 "mfma_util": round(flops / (ms_per_step * 1e-3) / BF16_MFMA_PEAK, 4),
-                "main_kernel_mfma_util": round(MFMA_FLOPS * MAIN_MFMA_PER_CHUNK * main_chunks
-                                               / (k_avg_ms * 1e-3) / BF16_MFMA_PEAK, 4)}
+                "main_kernel_mfma_util": round(main_flops / (k_avg_ms * 1e-3) / BF16_MFMA_PEAK, 4)}
 
     rec = {
         "metric": METRIC if cfg.name == "layer_1p5b_t4096" else OTHER_METRIC,
