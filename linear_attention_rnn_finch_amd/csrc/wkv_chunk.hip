@@ -399,6 +399,19 @@ __device__ __forceinline__ void load_public_state(const float *src, float (&S)[4
             S[ib][e] = src ? src[(16 * ib + 4 * grp + e) * kHeadDim + 16 * wave + i16] : 0.f;
 }
 
+// Wave priority falls with progress through a run of n chunks: workgroups
+// sharing a CU then advance together, instead of the older one (which wins
+// arbitration at equal priority) finishing first and leaving the CU half idle
+// at the end.
+__device__ __forceinline__ void set_progress_priority(int c, int n) {
+    switch ((4 * c) / n) {
+    case 0: __builtin_amdgcn_s_setprio(3); break;
+    case 1: __builtin_amdgcn_s_setprio(2); break;
+    case 2: __builtin_amdgcn_s_setprio(1); break;
+    default: __builtin_amdgcn_s_setprio(0); break;
+    }
+}
+
 // One segment of one head, chunk by chunk, from the state at s_src (zeros if
 // null) held in registers: o of every token is stored and, with keep_state, S
 // ends as the state after the segment (without it the last chunk skips the
@@ -516,15 +529,7 @@ __device__ __forceinline__ void scan_chunks(SM &sm, const Tensors &t, int64_t se
         const int64_t tc = seg_t0 + (int64_t)c * kChunk;
         const int nt = (int)min<int64_t>(kChunk, seg_t1 - tc);
 
-        // Wave priority falls with progress through the segment: the two
-        // workgroups sharing a CU then advance together (instead of the older
-        // one finishing first and leaving the CU half idle at the end).
-        switch ((4 * c) / n_chunks) {
-        case 0: __builtin_amdgcn_s_setprio(3); break;
-        case 1: __builtin_amdgcn_s_setprio(2); break;
-        case 2: __builtin_amdgcn_s_setprio(1); break;
-        default: __builtin_amdgcn_s_setprio(0); break;
-        }
+        set_progress_priority(c, n_chunks);
 
         // ---- stage this chunk's rows; prefetch the next chunk --------------------
         #pragma unroll
@@ -814,22 +819,18 @@ __device__ __forceinline__ void scan_chunks(SM &sm, const Tensors &t, int64_t se
 
 }
 
-// LDS of the state pass: the staging tile of the raw k and w rows shares its
-// space with the k~ planes (the pre-processing reads every staged row into
-// registers, a barrier, then writes the planes), 26 KB in all, so that four
-// state workgroups fit on a compute unit.
+// LDS of the state pass, 42.7 KB (three workgroups per compute unit).  The
+// k~ planes have space of their own rather than sharing the staging tile's:
+// sharing saves 16 KB but needs one more barrier per chunk (every staged row
+// read before a plane is written), which measured slower on long segments.
 struct SmemState {
     uint16_t v[kTileElems];                      // values of the chunk
-    union {
-        struct {
-            uint16_t kt_hi[kTileElems];          // k~ = k 2^{Lam_63 - Lam_s}, bf16 hi/lo planes
-            uint16_t kt_lo[kTileElems];
-        };
-        uint16_t stage[2][kStageElems];          // raw k, w rows of the chunk
-    };
+    uint16_t kt_hi[kTileElems];                  // k~ = k 2^{Lam_63 - Lam_s}, bf16 hi/lo planes
+    uint16_t kt_lo[kTileElems];
+    uint16_t stage[2][kStageElems];              // raw k, w rows of the chunk
     alignas(16) float row_dec[kHeadDim];         // decay of the whole chunk per key channel
 };
-static_assert(sizeof(SmemState) <= 40 * 1024, "four state workgroups per CU");
+static_assert(sizeof(SmemState) <= 53 * 1024, "three state workgroups per CU");
 
 // The state pass over one run of tokens (zero start): S ends as the run's
 // aggregate B = sum_s diag(P_end / P_s) k_s^T v_s and lam_seg (lanes with
@@ -860,7 +861,12 @@ __device__ __forceinline__ void state_run(SmemState &sm, const Tensors &t, int64
 
     u32x4 Qk[2], Qw[2], Qv[2];
     auto issue = [&](int64_t tc) {
-        const int rows = (int)max<int64_t>(min<int64_t>(kChunk, t1 - tc), 0);
+        // integer clamps: the device max() overload for 64-bit integers goes
+        // through double arithmetic on the vector unit, which would leave the
+        // record count (and so the buffer resource) in vector registers and
+        // turn every load into a loop over distinct resources
+        const int64_t left = t1 - tc;
+        const int rows = left <= 0 ? 0 : (left >= kChunk ? kChunk : (int)left);
         const Rsrc rk = chunk_rsrc(t.k, tc, rows, H, h, kRowIn);
         const Rsrc rw = chunk_rsrc(t.w, tc, rows, H, h, kRowIn);
         const Rsrc rv = chunk_rsrc(t.v, tc, rows, H, h, kRowIn);
@@ -877,6 +883,7 @@ __device__ __forceinline__ void state_run(SmemState &sm, const Tensors &t, int64
     for (int c = 0; c < n_chunks; ++c) {
         const int64_t tc = t0 + (int64_t)c * kChunk;
         const int nt = (int)min<int64_t>(kChunk, t1 - tc);
+        set_progress_priority(c, n_chunks);
         #pragma unroll
         for (int m = 0; m < 2; ++m) {
             lds_write_b128(sm.v, lb.vw + 64 * 32 * m, Qv[m]);
@@ -935,7 +942,6 @@ __device__ __forceinline__ void state_run(SmemState &sm, const Tensors &t, int64
                 lam_seg[q] += total[q];
             }
         }
-        __syncthreads();                       // every staged row is read: the planes may overwrite them
         #pragma unroll
         for (int a = 0; a < 4; ++a) {
             float ks[4];
@@ -991,7 +997,7 @@ __device__ __forceinline__ void store_public_state(float *dst, const float (&S)[
 // sequence n.  Shorter items (segments split into two or four runs, four
 // workgroups per compute unit) were measured slower.
 template <bool LOGD, bool C2>
-__global__ __launch_bounds__(256, C2 ? 3 : 4) void wkv_state_kernel(Geometry g, Tensors t, Workspace ws) {
+__global__ __launch_bounds__(256, 3) void wkv_state_kernel(Geometry g, Tensors t, Workspace ws) {
     __shared__ SmemState sm;
     const int item = blockIdx.x;
     const int h = item % g.H;
