@@ -127,15 +127,32 @@ STATE_MFMA_PER_CHUNK = 64
 BF16_MFMA_PEAK = 2.5e15          # MI355X dense bf16, FLOP/s
 
 
-def chunk_counts(lengths, H):
+def _segment(lengths, H):
+    up = lambda x, m: -(-x // m) * m
+    tokens, max_len = sum(lengths), max(lengths) if lengths else 0
+    return min(max(up(max(-(-tokens * H // 512), 1), 64), 256), up(max(max_len, 1), 64))
+
+
+def whole_sequence_plan(lengths, H, packed):
+    """Whether the library runs this bf16 call as whole sequences on its
+    producer/consumer kernel: fixed length, longer than 16 tokens, split by
+    the segment plan, and at least 256 (sequence, head) pairs."""
+    if packed or not lengths or max(lengths) <= 16:
+        return False
+    return -(-max(lengths) // _segment(lengths, H)) > 1 and len(lengths) * H >= 256
+
+
+def chunk_counts(lengths, H, packed=False):
     """(chunked-scan chunks, state-pass chunks, segments that do not end their
     sequence) of a bf16 call over sequences of these lengths, with the
     library's segment plan: about 512 (segment, head) items, segments a
     multiple of 64 tokens and at least 256, no longer than the longest sequence
-    rounded up to 64."""
-    up = lambda x, m: -(-x // m) * m
-    tokens, max_len = sum(lengths), max(lengths) if lengths else 0
-    seg = min(max(up(max(-(-tokens * H // 512), 1), 64), 256), up(max(max_len, 1), 64))
+    rounded up to 64.  A fixed-length call that this plan would split but that
+    has at least 256 (sequence, head) pairs runs whole sequences instead (no
+    state pass)."""
+    if whole_sequence_plan(lengths, H, packed):
+        return sum(-(-L // 64) for L in lengths) * H, 0, 0
+    seg = _segment(lengths, H)
     main = state = inner = 0
     for L in lengths:
         P = 1 if L == 0 else -(-L // seg)
@@ -401,7 +418,9 @@ def main():
     elif cfg.dtype != "bf16":
         kernel_name = "wkv_serial_kernel"
     else:
-        kernel_name = "wkv_chunk_kernel"
+        lens = [int(x) for x in np.diff(wl.cu_seqlens)] if wl.packed else [cfg.T] * cfg.B
+        kernel_name = ("wkv_chunk_pc_kernel" if whole_sequence_plan(lens, cfg.H, wl.packed)
+                       else "wkv_chunk_kernel")
     tokens_per_step = wl.tokens
     value = tokens_per_step / (ms_per_step * 1e-3)
 
@@ -417,11 +436,11 @@ def main():
     step_gbs = alg / (ms_per_step * 1e-3) / 1e9
     kernel_gbs = alg / (k_avg_ms * 1e-3) / 1e9
     copy_gbs = copy_bandwidth(torch)
-    chunked = kernel_name == "wkv_chunk_kernel"
+    chunked = kernel_name in ("wkv_chunk_kernel", "wkv_chunk_pc_kernel")
     lengths = [int(x) for x in np.diff(wl.cu_seqlens)] if wl.packed else [cfg.T] * cfg.B
     mfma = None
     if chunked:
-        main_chunks, state_chunks, inner = chunk_counts(lengths, cfg.H)
+        main_chunks, state_chunks, inner = chunk_counts(lengths, cfg.H, packed=wl.packed)
         main_flops = MFMA_FLOPS * (MAIN_MFMA_PER_CHUNK * main_chunks - STATE_MFMA_PER_CHUNK * inner)
         flops = main_flops + MFMA_FLOPS * STATE_MFMA_PER_CHUNK * state_chunks
         mfma = {"issued_flops_per_call": flops,
@@ -451,7 +470,8 @@ def main():
         # the step, in the step time above); the main kernel's own figure is
         # kept beside it
         "roofline": {"bound": "hbm", "scope": "pre-fill call" + (
-                         " (state pass, segment scan, chunked scan)" if chunked else " (one kernel)"),
+                         " (state pass, segment scan, chunked scan)" if kernel_name == "wkv_chunk_kernel"
+                         and chunk_counts(lengths, cfg.H, packed=wl.packed)[1] > 0 else " (one kernel)"),
                      "achieved": round(step_gbs, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(step_gbs / HBM_PEAK_GBS, 4),
                      "traffic": measured_traffic(name, kernel_name),

@@ -38,6 +38,14 @@ wkv_status_t fail_hip(hipError_t e, const char *what) {
 // Work items the planner aims for: two resident 4-wave workgroups on each of
 // the 256 compute units of an MI355X.
 constexpr int64_t kTargetItems = 512;
+// A fixed-length bf16 call that the 4-wave kernel would split into segments
+// runs whole sequences on the producer/consumer kernel (one 512-thread
+// workgroup per compute unit) instead once it has this many (sequence, head)
+// pairs.  Measured at T = 4096, H = 32 per call: 262 -> 200 us at B = 8,
+// 481 -> 344 us at B = 12; at B = 4 to 7 (which would still need segments)
+// the 4-wave kernel with its state pass is as fast or faster, and from 512
+// pairs on it needs no segments.
+constexpr int64_t kWholeSeqItems = 256;
 // the kernels address one 64-token chunk with 32-bit byte offsets:
 // 64 rows x H heads x 256 B (fp32 o) must stay below 2^31
 constexpr int kMaxHeads = 65536;
@@ -110,8 +118,15 @@ wkv_status_t plan_fixed(int B, int T, int H, int D, wkv_dtype_t dt, Plan &p) {
     p.g.total_tokens = tokens;
     p.g.uniform_T = T;
     p.g.segs_per_seq = (int)per;
+    p.g.whole_seqs = 0;
     p.max_len = T;
     p.split = per > 1;
+    if (p.bf16 && T > kDecodeMaxT && per > 1 && (int64_t)B * H >= kWholeSeqItems) {
+        // enough (sequence, head) pairs for one producer/consumer workgroup per
+        // CU: each runs a whole sequence, with no state pass and no scan
+        p.g.whole_seqs = 1;
+        p.split = false;
+    }
     layout_workspace(p, false);
     return WKV_OK;
 }
@@ -146,6 +161,7 @@ wkv_status_t plan_varlen(const int32_t *cu_host, int N, int H, int D, wkv_dtype_
     p.g.total_tokens = tokens;
     p.g.uniform_T = -1;
     p.g.segs_per_seq = 0;
+    p.g.whole_seqs = 0;
     p.max_len = max_len;
     p.split = split;
     layout_workspace(p, true);
@@ -165,6 +181,8 @@ wkv_status_t check_grid(const Plan &p) {
     }
     if (items * 256 > kMaxWorkItems)
         return fail(WKV_EUNSUPPORTED, "%lld work items exceed one launch", (long long)items);
+    if (p.g.whole_seqs && slices * 512 > kMaxWorkItems)          // 512 threads per (sequence, head)
+        return fail(WKV_EUNSUPPORTED, "%lld (sequence, head) pairs exceed one launch", (long long)slices);
     if (p.split && slices * kScanGroupThreads > kMaxWorkItems)
         return fail(WKV_EUNSUPPORTED, "%lld (sequence, head) pairs exceed the segment scan's launch",
                     (long long)slices);

@@ -390,8 +390,8 @@ __device__ __forceinline__ float one_minus_w(float x, float e) {
 // The 64 x 64 fp32 state in the accumulator layout (lane (i16, grp) of wave
 // w holds S[16*ib + 4*grp + e][16*w + i16]), from [key][value] memory (zeros
 // for a null source).
-__device__ __forceinline__ void load_public_state(const float *src, float (&S)[4][4]) {
-    const int tid = threadIdx.x, wave = tid >> 6, i16 = tid & 15, grp = (tid & 63) >> 4;
+__device__ __forceinline__ void load_public_state(const float *src, float (&S)[4][4], int tid = threadIdx.x) {
+    const int wave = tid >> 6, i16 = tid & 15, grp = (tid & 63) >> 4;
     #pragma unroll
     for (int ib = 0; ib < 4; ++ib)
         #pragma unroll
@@ -982,8 +982,8 @@ __device__ __forceinline__ void state_run(SmemState &sm, const Tensors &t, int64
     }
 }
 
-__device__ __forceinline__ void store_public_state(float *dst, const float (&S)[4][4]) {
-    const int tid = threadIdx.x, wave = tid >> 6, i16 = tid & 15, grp = (tid & 63) >> 4;
+__device__ __forceinline__ void store_public_state(float *dst, const float (&S)[4][4], int tid = threadIdx.x) {
+    const int wave = tid >> 6, i16 = tid & 15, grp = (tid & 63) >> 4;
     #pragma unroll
     for (int ib = 0; ib < 4; ++ib)
         #pragma unroll
@@ -1104,6 +1104,446 @@ __global__ __launch_bounds__(256, 2) void wkv_chunk_kernel(Geometry g, Tensors t
         store_public_state(t.state_out + ((size_t)it.n * g.H + h) * (kHeadDim * kHeadDim), S);
 }
 
+
+// ---- producer/consumer form of the chunked scan (fixed-length batches) -------
+//
+// One workgroup of eight waves per compute unit and work item.  Waves 0-3
+// (producers) load chunk j, stage it and write its pre-processed planes
+// (r~, k~ hi/lo, v, bonus partial sums, chunk decay, stiff votes) into plane
+// set j % 2, while waves 4-7 (consumers) run the matrix phases of chunk j - 1
+// from the other set and store its o.  One workgroup barrier per step hands
+// the sets over; each group orders its own LDS traffic with a counter barrier
+// in LDS that the other group never waits on.  The consumers issue no loads
+// (only o stores), so their stores never delay the producers' waits for
+// inputs, and the producers' loads never delay the consumers.  The
+// arithmetic of every chunk is that of scan_chunks.
+
+struct PlaneSet {
+    uint16_t v[kTileElems];
+    uint16_t rt_hi[kTileElems];
+    uint16_t rt_lo[kTileElems];
+    uint16_t kt_hi[kTileElems];
+    uint16_t kt_lo[kTileElems];
+    alignas(16) float bonus_part[4][kChunk];
+    alignas(16) float row_dec[kHeadDim];
+    int stiff[4];
+};
+// the token-serial path stages 64 x 64 fp32 outputs across rt_hi and rt_lo
+static_assert(offsetof(PlaneSet, rt_lo) == offsetof(PlaneSet, rt_hi) + sizeof(uint16_t) * kTileElems,
+              "rt planes must be adjacent");
+
+template <bool C2>
+struct SmemPC {
+    PlaneSet set[2];
+    uint16_t a_hi[kTileElems];                     // in-chunk matrix A (consumers only)
+    uint16_t a_lo[kTileElems];
+    uint16_t stage[C2 ? 4 : 3][kStageElems];       // raw r, k, w (, u') rows (producers only)
+    u32x2 u2[C2 ? 2 : 1][4][C2 ? 256 : 1];         // u' in the accumulator layout, per set
+    int bar[2];                                    // counter barriers: producers, consumers
+};
+static_assert(sizeof(SmemPC<true>) <= 160 * 1024, "one producer/consumer workgroup per CU");
+
+// What the consumer phases read: one plane set plus the A planes (the names
+// a_tiles and the operand helpers expect).
+struct PCView {
+    uint16_t *v, *rt_hi, *rt_lo, *kt_hi, *kt_lo, *a_hi, *a_lo;
+    float (*bonus_part)[kChunk];
+    float *row_dec;
+    int *stiff;
+};
+
+// Barrier of the four waves of one group: each wave's LDS traffic is complete
+// (lgkmcnt 0) before it counts itself in, and a wave leaves once all four have
+// counted in this many times.  Memory operations of other kinds are not
+// waited for (the producers' prefetch loads stay in flight).
+__device__ __forceinline__ void group_barrier(int *ctr, int &gen) {
+    gen += 4;
+    __builtin_amdgcn_s_waitcnt(0xC07F);            // lgkmcnt(0), vmcnt and expcnt unconstrained
+    if ((threadIdx.x & 63) == 0) __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    while (__builtin_amdgcn_readfirstlane(__hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP)) < gen)
+        __builtin_amdgcn_s_sleep(1);
+    __asm__ __volatile__("" ::: "memory");
+}
+
+// One work item: tokens [t0, t1) of head h, from the state at s_src (zeros if
+// null); with keep_state S ends as the state after the item and is stored to
+// state_dst.
+template <bool LOGD, bool C2>
+__device__ __forceinline__ void pc_item(SmemPC<C2> &sm, const Tensors &t, int64_t t0, int64_t t1, int h, int H,
+                                        const float *s_src, float *state_dst) {
+    constexpr bool kU2 = C2;
+    const int tid = threadIdx.x;
+    const bool producer = tid < 256;                 // waves 0-3 (wave-uniform)
+    const int ltid = tid & 255;                      // index within the group
+    const int wave = __builtin_amdgcn_readfirstlane(ltid >> 6);
+    const int lane = tid & 63;
+    const int i16 = lane & 15;
+    const int grp = lane >> 4;
+    const LdsBases lb = make_bases(ltid);
+    const int c0 = 16 * wave + 4 * grp;              // pre-processing channels (producers)
+    constexpr int kRowIn = kHeadDim * 2;
+    constexpr int kRowOut = kHeadDim * 4;
+    const int n_chunks = (int)((t1 - t0 + kChunk - 1) / kChunk);
+
+    if (tid == 0) { sm.bar[0] = 0; sm.bar[1] = 0; }
+    __syncthreads();
+    int gen = 0;
+
+    // ---- producer state ----------------------------------------------------------
+    f32x4 u4 = {0.f, 0.f, 0.f, 0.f};
+    const int ld_row = ltid >> 3;
+    const int ld_col = (ltid & 7) * 8;
+    int off_vin[2], st_wr[2], st_rd[4], st_u2[4];
+    #pragma unroll
+    for (int m = 0; m < 2; ++m) {
+        off_vin[m] = (ld_row + 32 * m) * H * kRowIn + 2 * ld_col;
+        st_wr[m] = off_stage(ld_row + 32 * m, ltid & 7);
+    }
+    #pragma unroll
+    for (int a = 0; a < 4; ++a) st_rd[a] = off_stage(4 * i16 + a, 2 * wave + (grp >> 1)) + 4 * (grp & 1);
+    #pragma unroll
+    for (int tb = 0; tb < 4; ++tb) st_u2[tb] = off_stage(16 * tb + i16, 2 * wave + (grp >> 1)) + 4 * (grp & 1);
+    ChunkRegs<kU2> P;
+    auto issue_loads = [&](int64_t tc) {
+        const int64_t left = t1 - tc;
+        const int rows = left >= kChunk ? kChunk : (int)left;
+        const Rsrc rk = chunk_rsrc(t.k, tc, rows, H, h, kRowIn);
+        const Rsrc rw = chunk_rsrc(t.w, tc, rows, H, h, kRowIn);
+        const Rsrc rv = chunk_rsrc(t.v, tc, rows, H, h, kRowIn);
+        const Rsrc rr = chunk_rsrc(t.r, tc, rows, H, h, kRowIn);
+        #pragma unroll
+        for (int m = 0; m < 2; ++m) P.r[m] = __builtin_amdgcn_raw_buffer_load_b128(rr, off_vin[m], 0, 0);
+        if constexpr (kU2) {
+            const Rsrc ru = t.u2 ? chunk_rsrc(t.u2, tc, rows, H, h, kRowIn)
+                                 : __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(t.v), (short)0, 0, kRsrcWord3);
+            #pragma unroll
+            for (int m = 0; m < 2; ++m) P.u2[m] = __builtin_amdgcn_raw_buffer_load_b128(ru, off_vin[m], 0, 0);
+        }
+        #pragma unroll
+        for (int m = 0; m < 2; ++m) {
+            P.k[m] = __builtin_amdgcn_raw_buffer_load_b128(rk, off_vin[m], 0, 0);
+            P.w[m] = __builtin_amdgcn_raw_buffer_load_b128(rw, off_vin[m], 0, 0);
+            P.v[m] = __builtin_amdgcn_raw_buffer_load_b128(rv, off_vin[m], 0, 0);
+        }
+    };
+
+    // ---- consumer state ----------------------------------------------------------
+    float S[4][4];
+    int off_out[4];
+    #pragma unroll
+    for (int tb = 0; tb < 4; ++tb) off_out[tb] = (16 * tb + i16) * H * kRowOut + 4 * (16 * wave + 4 * grp);
+    const uint16_t *gr = static_cast<const uint16_t *>(t.r);
+    const uint16_t *gk = static_cast<const uint16_t *>(t.k);
+    const uint16_t *gw = static_cast<const uint16_t *>(t.w);
+
+    // Step j (one workgroup barrier each, n_chunks + 1 steps): the producers
+    // make chunk j in set j % 2, the consumers finish chunk j - 1 from set
+    // (j - 1) % 2.  Each role runs its own loop, so that the registers of one
+    // are free for the other.
+    if (producer) {
+        if (!C2) u4 = *reinterpret_cast<const f32x4 *>(t.u + (size_t)h * kHeadDim + c0);
+        if (n_chunks > 0) issue_loads(t0);
+        for (int j = 0; j < n_chunks; ++j) {
+            {
+                PlaneSet &ps = sm.set[j & 1];
+                const int64_t tc = t0 + (int64_t)j * kChunk;
+                const int64_t left = t1 - tc;
+                const int nt = left >= kChunk ? kChunk : (int)left;
+                #pragma unroll
+                for (int m = 0; m < 2; ++m) {
+                    lds_write_b128(sm.stage[0], st_wr[m], P.r[m]);
+                    lds_write_b128(sm.stage[1], st_wr[m], P.k[m]);
+                    lds_write_b128(sm.stage[2], st_wr[m], P.w[m]);
+                    if constexpr (kU2) lds_write_b128(sm.stage[3], st_wr[m], P.u2[m]);
+                    lds_write_b128(ps.v, lb.vw + 64 * 32 * m, P.v[m]);
+                }
+                if (j + 1 < n_chunks) issue_loads(tc + kChunk);
+                group_barrier(&sm.bar[0], gen);
+
+                u32x2 pr[4], pk[4], pw[4];
+                #pragma unroll
+                for (int a = 0; a < 4; ++a) {
+                    pk[a] = lds_read_b64(sm.stage[1], st_rd[a]);
+                    pw[a] = lds_read_b64(sm.stage[2], st_rd[a]);
+                    pr[a] = lds_read_b64(sm.stage[0], st_rd[a]);
+                }
+                if constexpr (kU2) {
+                    #pragma unroll
+                    for (int tb = 0; tb < 4; ++tb) sm.u2[j & 1][tb][ltid] = lds_read_b64(sm.stage[3], st_u2[tb]);
+                }
+                if (nt < kChunk) {                      // partial last chunk: w = 1 on padding rows
+                    constexpr unsigned kPad = LOGD ? kNegInfPair : kOnePair;
+                    #pragma unroll
+                    for (int a = 0; a < 4; ++a)
+                        if (4 * i16 + a >= nt) pw[a] = u32x2{kPad, kPad};
+                }
+                float lam[4][4], kk_[4][4], rr[4][4];
+                #pragma unroll
+                for (int a = 0; a < 4; ++a) {
+                    lam[a][0] = bf16_lo(pw[a].x); lam[a][1] = bf16_hi(pw[a].x);
+                    lam[a][2] = bf16_lo(pw[a].y); lam[a][3] = bf16_hi(pw[a].y);
+                    kk_[a][0] = bf16_lo(pk[a].x); kk_[a][1] = bf16_hi(pk[a].x);
+                    kk_[a][2] = bf16_lo(pk[a].y); kk_[a][3] = bf16_hi(pk[a].y);
+                    rr[a][0] = bf16_lo(pr[a].x); rr[a][1] = bf16_hi(pr[a].x);
+                    rr[a][2] = bf16_lo(pr[a].y); rr[a][3] = bf16_hi(pr[a].y);
+                }
+                float pwv[4][4];
+                #pragma unroll
+                for (int a = 0; a < 4; ++a)
+                    #pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const float x = lam[a][q];
+                        const float e = LOGD ? __builtin_amdgcn_exp2f(x * kLog2e) : 0.f;
+                        if (C2) kk_[a][q] *= one_minus_w<LOGD>(x, e);
+                        pwv[a][q] = LOGD ? __builtin_amdgcn_exp2f(-e * kLog2e) : x;
+                    }
+                float excl[4], total[4];
+                bool stiff = false;
+                #pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    pwv[1][q] *= pwv[0][q];
+                    pwv[2][q] *= pwv[1][q];
+                    pwv[3][q] *= pwv[2][q];
+                    const float incl = row_prod16(pwv[3][q]);
+                    excl[q] = row_prev(incl);
+                    total[q] = row_bcast<15>(incl);
+                    stiff |= !(total[q] >= kMinChunkDecay);
+                }
+                stiff = __any(stiff);
+                if (lane == 0) ps.stiff[wave] = stiff ? 1 : 0;
+                if (i16 == 15) {
+                    #pragma unroll
+                    for (int q = 0; q < 4; ++q) ps.row_dec[c0 + q] = total[q];
+                }
+                float bp[4];
+                #pragma unroll
+                for (int a = 0; a < 4; ++a) {
+                    float rs[4], ks[4];
+                    bp[a] = 0.f;
+                    #pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const float p_prev = a == 0 ? excl[q] : excl[q] * pwv[a - 1][q];
+                        const float p_cur = excl[q] * pwv[a][q];
+                        rs[q] = rr[a][q] * p_prev;
+                        ks[q] = kk_[a][q] * __builtin_amdgcn_rcpf(p_cur);
+                        if (!C2) bp[a] += rr[a][q] * u4[q] * kk_[a][q];
+                    }
+                    u32x2 rh, rl, kh, kl;
+                    split4(rs[0], rs[1], rs[2], rs[3], rh, rl);
+                    split4(ks[0], ks[1], ks[2], ks[3], kh, kl);
+                    lds_write_b64(ps.rt_hi, lb.pw_rt[a], rh);
+                    lds_write_b64(ps.rt_lo, lb.pw_rt[a], rl);
+                    lds_write_b64(ps.kt_hi, lb.pw_kt[a], kh);
+                    lds_write_b64(ps.kt_lo, lb.pw_kt[a], kl);
+                    if (!C2) bp[a] = sum_rows4(bp[a]);
+                }
+                if (!C2 && grp == 0) {
+                    f32x4 b4 = {bp[0], bp[1], bp[2], bp[3]};
+                    *reinterpret_cast<f32x4 *>(&ps.bonus_part[wave][4 * i16]) = b4;
+                }
+            }
+            __syncthreads();
+        }
+        __syncthreads();                                 // the consumers' last step
+    } else {
+        load_public_state(s_src, S, ltid);
+        __syncthreads();                                 // step 0: nothing to consume yet
+        for (int c = 0; c < n_chunks; ++c) {
+            PlaneSet &ps = sm.set[c & 1];
+            PCView sv{ps.v, ps.rt_hi, ps.rt_lo, ps.kt_hi, ps.kt_lo, sm.a_hi, sm.a_lo, ps.bonus_part, ps.row_dec,
+                      ps.stiff};
+            const int64_t tc = t0 + (int64_t)c * kChunk;
+            const int64_t left = t1 - tc;
+            const int nt = left >= kChunk ? kChunk : (int)left;
+            bf16x8 vop[2];
+            vop[0] = col_op(ps.v, lb.tr_v, 0);
+            vop[1] = col_op(ps.v, lb.tr_v, 1);
+            const bool stiff = (ps.stiff[0] | ps.stiff[1] | ps.stiff[2] | ps.stiff[3]) != 0;
+            f32x4 acc[4];
+            if (stiff) {
+                // exact token-by-token evaluation of this chunk (rare path),
+                // outputs staged as fp32 [t][j] in this set's r~ planes
+                float *o_stage = reinterpret_cast<float *>(ps.rt_hi);
+                for (int tt = 0; tt < nt; ++tt) {
+                    const size_t base = ((size_t)(tc + tt) * H + h) * kHeadDim;
+                    float part = 0.f;
+                    float kv[4][4], wv[4][4];
+                    #pragma unroll
+                    for (int ib = 0; ib < 4; ++ib) {
+                        const size_t off = base + 16 * ib + 4 * grp;
+                        const u32x2 a = *reinterpret_cast<const u32x2 *>(gr + off);
+                        const u32x2 b = *reinterpret_cast<const u32x2 *>(gk + off);
+                        const u32x2 d = *reinterpret_cast<const u32x2 *>(gw + off);
+                        const float rv[4] = {bf16_lo(a.x), bf16_hi(a.x), bf16_lo(a.y), bf16_hi(a.y)};
+                        kv[ib][0] = bf16_lo(b.x); kv[ib][1] = bf16_hi(b.x); kv[ib][2] = bf16_lo(b.y); kv[ib][3] = bf16_hi(b.y);
+                        wv[ib][0] = bf16_lo(d.x); wv[ib][1] = bf16_hi(d.x); wv[ib][2] = bf16_lo(d.y); wv[ib][3] = bf16_hi(d.y);
+                        #pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            part += rv[e] * S[ib][e];
+                            const float x = wv[ib][e];
+                            const float ex = LOGD ? __builtin_amdgcn_exp2f(x * kLog2e) : 0.f;
+                            if (C2) kv[ib][e] *= one_minus_w<LOGD>(x, ex);
+                            if (LOGD) wv[ib][e] = __builtin_amdgcn_exp2f(-ex * kLog2e);
+                        }
+                    }
+                    part = sum_rows4(part);
+                    const unsigned vbits = ps.v[off_v(tt, 16 * wave + i16)];
+                    const float vj = __uint_as_float(vbits << 16);
+                    const float b = C2 ? 0.f : ps.bonus_part[0][tt] + ps.bonus_part[1][tt] +
+                                               ps.bonus_part[2][tt] + ps.bonus_part[3][tt];
+                    if (grp == (tt & 3)) o_stage[tt * kHeadDim + 16 * wave + i16] = part + b * vj;
+                    #pragma unroll
+                    for (int ib = 0; ib < 4; ++ib)
+                        #pragma unroll
+                        for (int e = 0; e < 4; ++e) S[ib][e] = wv[ib][e] * S[ib][e] + kv[ib][e] * vj;
+                }
+                group_barrier(&sm.bar[1], gen);
+                #pragma unroll
+                for (int tb = 0; tb < 4; ++tb)
+                    acc[tb] = *reinterpret_cast<const f32x4 *>(&o_stage[(16 * tb + i16) * kHeadDim + 16 * wave + 4 * grp]);
+            } else {
+                if (wave == 2 || wave == 3) {
+                    const int TB = wave == 2 ? 0 : 2, SB = TB + 1;
+                    const u32x2 z = {0u, 0u};
+                    lds_write_b64(sm.a_hi, lb.aw[SB] + 1024 * TB, z);
+                    lds_write_b64(sm.a_lo, lb.aw[SB] + 1024 * TB, z);
+                }
+                if (wave == 0) {
+                    const int TB[3] = {0, 1, 2}, SB[3] = {0, 0, 0};
+                    a_tiles<!C2, 3>(sv, lb, TB, SB, i16, grp);
+                } else if (wave == 1) {
+                    const int TB[3] = {1, 2, 3}, SB[3] = {1, 1, 0};
+                    a_tiles<!C2, 3>(sv, lb, TB, SB, i16, grp);
+                } else if (wave == 2) {
+                    const int TB[2] = {2, 3}, SB[2] = {2, 1};
+                    a_tiles<!C2, 2>(sv, lb, TB, SB, i16, grp);
+                } else {
+                    const int TB[2] = {3, 3}, SB[2] = {3, 2};
+                    a_tiles<!C2, 2>(sv, lb, TB, SB, i16, grp);
+                }
+                {   // read-out of the carried state: o^T = S^T r~^T
+                    bf16x8 s_hi[2], s_lo[2];
+                    #pragma unroll
+                    for (int kk = 0; kk < 2; ++kk) {
+                        unsigned hi[4], lo[4];
+                        #pragma unroll
+                        for (int half = 0; half < 2; ++half) {
+                            const int ib = 2 * kk + half;
+                            const HiLo x = split2(S[ib][0], S[ib][1]);
+                            const HiLo y = split2(S[ib][2], S[ib][3]);
+                            hi[2 * half] = x.hi; lo[2 * half] = x.lo;
+                            hi[2 * half + 1] = y.hi; lo[2 * half + 1] = y.lo;
+                        }
+                        const u32x4 h4 = {hi[0], hi[1], hi[2], hi[3]}, l4 = {lo[0], lo[1], lo[2], lo[3]};
+                        s_hi[kk] = as_bf16x8(h4);
+                        s_lo[kk] = as_bf16x8(l4);
+                    }
+                    #pragma unroll
+                    for (int tb = 0; tb < 4; ++tb) acc[tb] = f32x4{0.f, 0.f, 0.f, 0.f};
+                    #pragma unroll
+                    for (int kk = 0; kk < 2; ++kk) {
+                        bf16x8 r_hi[4], r_lo[4];
+                        #pragma unroll
+                        for (int tb = 0; tb < 4; ++tb) {
+                            r_hi[tb] = rt_op(ps.rt_hi, lb.ro_x, tb, kk);
+                            r_lo[tb] = rt_op(ps.rt_lo, lb.ro_x, tb, kk);
+                        }
+                        #pragma unroll
+                        for (int tb = 0; tb < 4; ++tb) acc[tb] = mfma(s_hi[kk], r_hi[tb], acc[tb]);
+                        #pragma unroll
+                        for (int tb = 0; tb < 4; ++tb) acc[tb] = mfma(s_hi[kk], r_lo[tb], acc[tb]);
+                        #pragma unroll
+                        for (int tb = 0; tb < 4; ++tb) acc[tb] = mfma(s_lo[kk], r_hi[tb], acc[tb]);
+                    }
+                }
+                // state update, skipped in the last chunk when the end state is not wanted
+                if (state_dst || c + 1 < n_chunks) {
+                    f32x4 p[4];
+                    #pragma unroll
+                    for (int ib = 0; ib < 4; ++ib) p[ib] = f32x4{0.f, 0.f, 0.f, 0.f};
+                    #pragma unroll
+                    for (int kk = 0; kk < 2; ++kk) {
+                        bf16x8 k_hi[4], k_lo[4];
+                        #pragma unroll
+                        for (int ib = 0; ib < 4; ++ib) {
+                            k_hi[ib] = kt_col_op(ps.kt_hi, lb.tr_kt[ib], kk);
+                            k_lo[ib] = kt_col_op(ps.kt_lo, lb.tr_kt[ib], kk);
+                        }
+                        #pragma unroll
+                        for (int ib = 0; ib < 4; ++ib) p[ib] = mfma(k_hi[ib], vop[kk], p[ib]);
+                        #pragma unroll
+                        for (int ib = 0; ib < 4; ++ib) p[ib] = mfma(k_lo[ib], vop[kk], p[ib]);
+                    }
+                    #pragma unroll
+                    for (int ib = 0; ib < 4; ++ib) {
+                        const f32x4 dec = *reinterpret_cast<const f32x4 *>(&ps.row_dec[16 * ib + 4 * grp]);
+                        #pragma unroll
+                        for (int e = 0; e < 4; ++e) S[ib][e] = dec[e] * (S[ib][e] + p[ib][e]);
+                    }
+                }
+                group_barrier(&sm.bar[1], gen);          // every A tile is written
+                // in-chunk pairs: o^T += v^T A^T (A is zero for s >= 32 when t < 32)
+                #pragma unroll
+                for (int kk = 0; kk < 2; ++kk) {
+                    bf16x8 a_hi[4], a_lo[4];
+                    #pragma unroll
+                    for (int tb = 2 * kk; tb < 4; ++tb) {
+                        a_hi[tb] = row_op(sm.a_hi, lb.ro_x, tb, kk);
+                        a_lo[tb] = row_op(sm.a_lo, lb.ro_x, tb, kk);
+                    }
+                    #pragma unroll
+                    for (int tb = 2 * kk; tb < 4; ++tb) acc[tb] = mfma(vop[kk], a_hi[tb], acc[tb]);
+                    #pragma unroll
+                    for (int tb = 2 * kk; tb < 4; ++tb) acc[tb] = mfma(vop[kk], a_lo[tb], acc[tb]);
+                }
+            }
+            if constexpr (kU2) {                         // + u'_t (Finch-C2 output)
+                #pragma unroll
+                for (int tb = 0; tb < 4; ++tb) {
+                    const u32x2 u = sm.u2[c & 1][tb][ltid];
+                    acc[tb][0] += bf16_lo(u.x);
+                    acc[tb][1] += bf16_hi(u.x);
+                    acc[tb][2] += bf16_lo(u.y);
+                    acc[tb][3] += bf16_hi(u.y);
+                }
+            }
+            if (t.o_bf16) {
+                const Rsrc ro = chunk_rsrc(t.o, tc, nt, H, h, kRowIn);
+                #pragma unroll
+                for (int tb = 0; tb < 4; ++tb) {
+                    const f32x2 a = {acc[tb][0], acc[tb][1]}, b = {acc[tb][2], acc[tb][3]};
+                    const u32x2 pk = {__builtin_bit_cast(unsigned, __builtin_convertvector(a, bf16x2)),
+                                      __builtin_bit_cast(unsigned, __builtin_convertvector(b, bf16x2))};
+                    __builtin_amdgcn_raw_buffer_store_b64(pk, ro, off_out[tb] / 2, 0, 0);
+                }
+            } else {
+                const Rsrc ro = chunk_rsrc(t.o, tc, nt, H, h, kRowOut);
+                #pragma unroll
+                for (int tb = 0; tb < 4; ++tb)
+                    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, acc[tb]), ro, off_out[tb], 0, 0);
+            }
+            __syncthreads();
+        }
+        if (state_dst) store_public_state(state_dst, S, ltid);
+    }
+}
+
+// Fixed-length batches whose (sequence, head) pairs fill the GPU: work item
+// n * H + h is the whole sequence n of head h, from state_in (no segments, no
+// state pass).
+template <bool LOGD, bool C2>
+__global__ __launch_bounds__(512, 1) void wkv_chunk_pc_kernel(Geometry g, Tensors t, Workspace) {
+    __shared__ SmemPC<C2> sm;
+    const int item = blockIdx.x;
+    const int h = item % g.H;
+    const int n = item / g.H;
+    if (g.uniform_T < 0 || n >= g.n_seq) return;
+    const int64_t t0 = (int64_t)n * g.uniform_T;
+    const size_t slot = ((size_t)n * g.H + h) * (kHeadDim * kHeadDim);
+    pc_item<LOGD, C2>(sm, t, t0, t0 + g.uniform_T, h, g.H, t.state_in ? t.state_in + slot : nullptr,
+                      t.state_out ? t.state_out + slot : nullptr);
+}
+
 }  // namespace
 
 hipError_t launch_chunked(const Geometry &g, const Tensors &t, const Workspace &ws, bool split,
@@ -1121,6 +1561,17 @@ hipError_t launch_chunked(const Geometry &g, const Tensors &t, const Workspace &
         hipLaunchKernelGGL(wkv_segment_scan_kernel, dim3((unsigned)(g.n_seq * g.H * kScanSlices)), dim3(kScanThreads),
                            0, st, g, t, ws);
         if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
+    if (g.whole_seqs) {                                // producer/consumer kernel, whole sequences
+        const dim3 pc_grid((unsigned)((int64_t)g.n_seq * g.H)), pc_block(512);
+        void (*k)(Geometry, Tensors, Workspace) =
+            v.log_decay ? (v.c2 ? wkv_chunk_pc_kernel<true, true> : wkv_chunk_pc_kernel<true, false>)
+                        : (v.c2 ? wkv_chunk_pc_kernel<false, true> : wkv_chunk_pc_kernel<false, false>);
+        if (tm.start || tm.stop)
+            hipExtLaunchKernelGGL(k, pc_grid, pc_block, 0, st, tm.start, tm.stop, 0, g, t, ws);
+        else
+            hipLaunchKernelGGL(k, pc_grid, pc_block, 0, st, g, t, ws);
+        return hipGetLastError();
     }
     void (*k)(Geometry, Tensors, Workspace) =
         v.log_decay ? (v.c2 ? wkv_chunk_kernel<true, true> : wkv_chunk_kernel<true, false>)

@@ -27,6 +27,9 @@ struct Geometry {
     const int32_t *cu;      // packed only: device offsets [n_seq + 1]
     const int32_t *seg_off; // packed only: device, first global segment of sequence n [n_seq + 1]
     const int32_t *seg_seq; // packed only: device, sequence of global segment s (-1: none) [n_seg]
+    // fixed-length only: 1 when every (sequence, head) is one work item of
+    // the producer/consumer kernel (no segments, no state pass), else 0
+    int whole_seqs;
 };
 
 // One work item's token range and position inside its sequence.
