@@ -1240,7 +1240,11 @@ __device__ __forceinline__ void pc_item(SmemPC<C2> &sm, const Tensors &t, int64_
     // make chunk j in set j % 2, the consumers finish chunk j - 1 from set
     // (j - 1) % 2.  Each role runs its own loop, so that the registers of one
     // are free for the other.
+    // Each SIMD holds one producer and one consumer wave, and the consumers'
+    // matrix phases bound each step: the consumers win issue arbitration
+    // (8 % faster on 8 x 4096 x 32 than equal priority; the reverse is slower).
     if (producer) {
+        __builtin_amdgcn_s_setprio(0);
         if (!C2) u4 = *reinterpret_cast<const f32x4 *>(t.u + (size_t)h * kHeadDim + c0);
         if (n_chunks > 0) issue_loads(t0);
         for (int j = 0; j < n_chunks; ++j) {
@@ -1346,6 +1350,7 @@ __device__ __forceinline__ void pc_item(SmemPC<C2> &sm, const Tensors &t, int64_
         }
         __syncthreads();                                 // the consumers' last step
     } else {
+        __builtin_amdgcn_s_setprio(3);
         load_public_state(s_src, S, ltid);
         __syncthreads();                                 // step 0: nothing to consume yet
         for (int c = 0; c < n_chunks; ++c) {
