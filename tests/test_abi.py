@@ -128,6 +128,25 @@ def test_workspace_checks(lib):
     assert lib.wkv_last_error() == before
 
 
+def test_whole_sequence_plans_need_no_workspace(lib):
+    """The planner's choice, seen through the workspace query: a fixed-length
+    bf16 call that would be split runs whole sequences (no scratch) once it
+    has at least 256 (sequence, head) pairs; below that, or in fp32 (its own
+    kernel, never split), nothing changes; from 512 pairs on no split is
+    needed either."""
+    ws = lambda B, T, H, dt=BF16: lib.wkv_prefill_workspace_bytes(B, T, H, 64, dt)
+    assert ws(8, 4096, 32) == 0                       # 256 pairs: whole sequences
+    assert ws(2, 1000, 128) == 0 and ws(12, 4096, 32) == 0
+    assert ws(4, 4096, 32) > 0 and ws(7, 4096, 32) > 0    # 128, 224 pairs: split
+    assert ws(1, 4096, 32) > 0                        # the 1.5B layer: split
+    assert ws(16, 4096, 32) == 0                      # 512 pairs: no split needed
+    assert ws(8, 16, 32) == 0                         # recurrent steps
+    assert ws(8, 4096, 32, F32) == 0                  # fp32: token-serial kernel
+    # varlen calls keep the segmented kernel: a split ragged call needs scratch
+    cu = np.array([0] + [4096 * (i + 1) for i in range(8)], dtype=np.int32)
+    assert lib.wkv_prefill_varlen_workspace_bytes(cu.ctypes.data, 8, 32, 64, BF16) > 0
+
+
 def varlen(lib, cu, H=4, dt=BF16, ws_bytes=None, cu_dev=A * 20, **ptrs):
     cu = np.asarray(cu, dtype=np.int32)
     N = len(cu) - 1
