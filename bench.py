@@ -142,6 +142,20 @@ def whole_sequence_plan(lengths, H, packed):
     return -(-max(lengths) // _segment(lengths, H)) > 1 and len(lengths) * H >= 256
 
 
+def one_launch_plan(lengths, H, packed, capacity):
+    """Whether the library runs this split bf16 call as one launch of its
+    split kernel: segments of at most 1024 tokens, at most 4096 (sequence,
+    head) pairs, and every state workgroup resident at once (`capacity`
+    workgroups: compute units x 2)."""
+    if not lengths or max(lengths) <= 16 or whole_sequence_plan(lengths, H, packed):
+        return False
+    seg = _segment(lengths, H)
+    n_seg = sum(1 if L == 0 else -(-L // seg) for L in lengths)
+    if n_seg == len(lengths):
+        return False                                    # nothing is split
+    return seg <= 1024 and len(lengths) * H <= 4096 and (n_seg - len(lengths)) * H <= capacity
+
+
 def chunk_counts(lengths, H, packed=False):
     """(chunked-scan chunks, state-pass chunks, segments that do not end their
     sequence) of a bf16 call over sequences of these lengths, with the
@@ -302,6 +316,9 @@ def main():
                     help="base Finch (static bonus) or the Finch-C2 time mixer")
     ap.add_argument("--rotate", type=int, default=0,
                     help="buffer sets the calls cycle through (0: enough for 1 GiB, at most 16)")
+    ap.add_argument("--split-launches", type=int, choices=(1, 3), default=1,
+                    help="launch form of split calls: 1 (the library's default: one launch where it "
+                         "can) or 3 (state pass, segment scan, chunked scan), for comparison")
     ap.add_argument("--op", choices=("wkv", "layernorm", "compress"), default="wkv",
                     help="the pre-fill scan (default), or one epilogue step on the 1.5B layer "
                          "shape: LayerNorm over heads, GOLD key compression")
@@ -320,6 +337,7 @@ def main():
     from linear_attention_rnn_finch_amd import _binding
     from synth import make_workload, get_config, error_report
 
+    fw.set_split_launches(args.split_launches)
     cfg = get_config(int(args.config) if args.config.isdigit() else args.config)
     wl = make_workload(cfg, decay=args.decay, variant=args.variant)
     name = workload_name(cfg.name, args.decay, args.variant)
@@ -353,7 +371,7 @@ def main():
         t["s0"] = None if wl.state0 is None else torch.from_numpy(wl.state0).to(dev)
         t["o"] = torch.empty(o_shape, dtype=torch.float32, device=dev)
         t["st"] = torch.empty((n_seq, cfg.H, cfg.D, cfg.D), dtype=torch.float32, device=dev)
-        t["ws"] = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+        t["ws"] = fw.new_workspace(ws_bytes, dev)
         return t
 
     sets = [make_set() for _ in range(n_sets)]
@@ -419,7 +437,10 @@ def main():
         kernel_name = "wkv_serial_kernel"
     else:
         lens = [int(x) for x in np.diff(wl.cu_seqlens)] if wl.packed else [cfg.T] * cfg.B
+        capacity = 2 * torch.cuda.get_device_properties(0).multi_processor_count
         kernel_name = ("wkv_chunk_pc_kernel" if whole_sequence_plan(lens, cfg.H, wl.packed)
+                       else "wkv_split_kernel" if args.split_launches == 1
+                       and one_launch_plan(lens, cfg.H, wl.packed, capacity)
                        else "wkv_chunk_kernel")
     tokens_per_step = wl.tokens
     value = tokens_per_step / (ms_per_step * 1e-3)
@@ -436,7 +457,7 @@ def main():
     step_gbs = alg / (ms_per_step * 1e-3) / 1e9
     kernel_gbs = alg / (k_avg_ms * 1e-3) / 1e9
     copy_gbs = copy_bandwidth(torch)
-    chunked = kernel_name in ("wkv_chunk_kernel", "wkv_chunk_pc_kernel")
+    chunked = kernel_name in ("wkv_chunk_kernel", "wkv_chunk_pc_kernel", "wkv_split_kernel")
     lengths = [int(x) for x in np.diff(wl.cu_seqlens)] if wl.packed else [cfg.T] * cfg.B
     mfma = None
     if chunked:
@@ -465,16 +486,20 @@ def main():
                    "d_model": cfg.H * cfg.D, "tokens": wl.tokens,
                    "timing": ("eager calls" if args.no_graph else
                               "HIP graph of %d captured calls, one replay" % args.steps),
-                   "buffer_sets": n_sets},
+                   "buffer_sets": n_sets,
+                   "split_launches": args.split_launches},
         # the headline fraction is the whole pre-fill call's (every kernel of
         # the step, in the step time above); the main kernel's own figure is
         # kept beside it
         "roofline": {"bound": "hbm", "scope": "pre-fill call" + (
                          " (state pass, segment scan, chunked scan)" if kernel_name == "wkv_chunk_kernel"
-                         and chunk_counts(lengths, cfg.H, packed=wl.packed)[1] > 0 else " (one kernel)"),
+                         and chunk_counts(lengths, cfg.H, packed=wl.packed)[1] > 0
+                         else " (one kernel: state pass, segment scan and chunked scan as workgroup roles)"
+                         if kernel_name == "wkv_split_kernel" else " (one kernel)"),
                      "achieved": round(step_gbs, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(step_gbs / HBM_PEAK_GBS, 4),
-                     "traffic": measured_traffic(name, kernel_name),
+                     # the committed counter profiles cover the library's default launch form
+                     "traffic": measured_traffic(name, kernel_name) if args.split_launches == 1 else None,
                      "algorithmic_bytes_per_call": alg,
                      "call_event_avg_us": round(c_avg_ms * 1e3, 2),
                      "measured_copy_GBps": round(copy_gbs, 1),

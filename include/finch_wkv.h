@@ -63,7 +63,11 @@
 extern "C" {
 #endif
 
-#define FINCH_WKV_ABI_VERSION 3
+#define FINCH_WKV_ABI_VERSION 4
+
+/* Bytes of control records at the start of every nonzero workspace (see
+ * wkv_prefill_workspace_bytes). */
+#define WKV_WORKSPACE_CONTROL_BYTES 262144
 
 typedef enum {
     WKV_OK = 0,
@@ -117,6 +121,15 @@ const char *wkv_last_error(void);
  * answer: then workspace may be NULL).  Returns 0 as well for invalid sizes;
  * wkv_prefill reports those.  Deterministic: same arguments, same answer on the
  * same device.
+ *
+ * A nonzero workspace begins with WKV_WORKSPACE_CONTROL_BYTES of control
+ * records: counters and flags through which the workgroups of one launch hand
+ * segment states to each other.  Zero its first WKV_WORKSPACE_CONTROL_BYTES
+ * bytes once, before the first call that uses it (e.g. one hipMemset after
+ * allocating it); every call leaves them ready for the next one, so they must
+ * not be written between calls.  The rest of a workspace is scratch whose
+ * contents do not matter.  A workspace sized for one call serves any call
+ * whose query returns no more.
  */
 size_t wkv_prefill_workspace_bytes(int B, int T, int H, int D, wkv_dtype_t in_dtype);
 
@@ -213,8 +226,8 @@ wkv_status_t wkv_prefill_varlen_ex(const void *r, const void *k, const void *v,
  * process ends (every fixed-length plan fits: at most about 34 MB are used).
  * All calls on one GPU share that array: calls that overlap in time on one
  * GPU (different streams, different threads without ordering) race and give
- * wrong results.  Calls ordered on one stream are safe.  No part of the
- * scratch has to start at zero.
+ * wrong results.  Calls ordered on one stream are safe.  The array starts
+ * zeroed (static storage), which its control records need.
  */
 wkv_status_t wkv_prefill_noalloc(const void *r, const void *k, const void *v,
                                  const void *decay, const float *u, const void *second_value,
@@ -260,8 +273,8 @@ wkv_status_t wkv_gold_compress(const void *x, const void *w_kd, void *c, wkv_dty
  * Kernel timing hook for profiling tools (the benchmark uses it).  When
  * event_before/event_after (hipEvent_t, cast to void *) are non-NULL, every
  * later pre-fill call made from the calling thread attaches them to the launch
- * of its main scan kernel (the chunked kernel for bf16, the token-serial one
- * for fp32, the recurrent-step kernel when no sequence of the call has more
+ * of its main scan kernel (the chunked kernel for bf16 -- for a split call in
+ * one launch, that launch --, the token-serial one for fp32, the recurrent-step kernel when no sequence of the call has more
  * than 16 tokens; the one kernel of wkv_layernorm_heads and of
  * wkv_gold_compress): event_before takes that kernel's start timestamp and event_after
  * its end timestamp, so hipEventElapsedTime gives the kernel's own duration,
@@ -270,6 +283,19 @@ wkv_status_t wkv_gold_compress(const void *x, const void *w_kd, void *c, wkv_dty
  * calls that record them.  Per thread; always returns WKV_OK.
  */
 wkv_status_t wkv_set_kernel_timing_events(void *event_before, void *event_after);
+
+/*
+ * Launch form of split pre-fill calls, for comparisons and tests.  A bf16 call
+ * that cuts its sequences into segments runs by default (launches = 1) as one
+ * launch in which the segments' state pass, their combine and the chunked
+ * scan hand results to each other through the workspace's control records;
+ * it falls back to three launches (state pass, segment scan, chunked scan)
+ * when the call has more than WKV_WORKSPACE_CONTROL_BYTES / 64 (sequence,
+ * head) pairs or more state workgroups than the device holds at once.
+ * launches = 3 always takes the three launches.  Both give identical results.
+ * Per thread; WKV_EINVAL for other values.
+ */
+wkv_status_t wkv_set_split_launches(int launches);
 
 #ifdef __cplusplus
 }

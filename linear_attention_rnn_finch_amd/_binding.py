@@ -20,6 +20,9 @@ WKV_OK, WKV_EINVAL, WKV_EUNSUPPORTED, WKV_EWORKSPACE, WKV_EHIP = range(5)
 WKV_F32, WKV_BF16 = 0, 1
 WKV_FLAG_DECAY_LOG, WKV_FLAG_FINCH_C2, WKV_FLAG_OUT_BF16 = 1, 2, 4
 HEAD_DIM = 64
+# control records at the start of every nonzero workspace: zero before the
+# first call that uses the workspace, never written between calls
+WORKSPACE_CONTROL_BYTES = 262144
 DECAYS = ("w", "log")            # decay argument holds w_t, or d_t with w_t = exp(-exp(d_t))
 VARIANTS = ("finch", "c2")       # base Finch (bonus u) or the Finch-C2 time mixer
 
@@ -54,6 +57,8 @@ _lib.wkv_layernorm_heads.restype = _i
 _lib.wkv_layernorm_heads.argtypes = [_vp, _vp, _vp, ctypes.c_float, _vp, _i, ctypes.c_int64, _i, _vp]
 _lib.wkv_gold_compress.restype = _i
 _lib.wkv_gold_compress.argtypes = [_vp, _vp, _vp, _i, ctypes.c_int64, _i, _vp]
+_lib.wkv_set_split_launches.restype = _i
+_lib.wkv_set_split_launches.argtypes = [_i]
 _lib.wkv_prefill_varlen_ex.restype = _i
 _lib.wkv_prefill_varlen_ex.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i,
                                        _vp, _vp, _vp, _i, _i, _i, ctypes.c_uint, _vp, _sz, _vp]
@@ -68,6 +73,23 @@ class WkvError(RuntimeError):
 
 def abi_version() -> int:
     return int(_lib.wkv_abi_version())
+
+
+def set_split_launches(launches: int) -> None:
+    """Launch form of split bf16 calls made from this thread: 1 (default) runs
+    one launch where it can, 3 always the state pass, the segment scan and the
+    chunked scan.  Both give identical results."""
+    st = int(_lib.wkv_set_split_launches(int(launches)))
+    if st != WKV_OK:
+        raise WkvError(st, _lib.wkv_last_error().decode())
+
+
+def new_workspace(nbytes: int, device) -> torch.Tensor:
+    """A workspace of nbytes on `device`, its control records zeroed (the
+    state a workspace must be in before its first call)."""
+    ws = torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=device)
+    ws[:WORKSPACE_CONTROL_BYTES].zero_()
+    return ws
 
 
 def _check(status: int):
@@ -148,7 +170,8 @@ def _on_stream(stream):
 
 
 def _workspace(nbytes, device, given, stream):
-    """The caller's workspace (checked), or a new one on the kernels' stream."""
+    """The caller's workspace (checked; its control records are the caller's
+    to keep), or a new one on the kernels' stream with them zeroed."""
     if nbytes == 0:
         return None, 0
     if given is not None:
@@ -157,7 +180,7 @@ def _workspace(nbytes, device, given, stream):
             raise ValueError("workspace must be on %s, got %s" % (device, given.device))
         return given, given.numel() * given.element_size()
     with _on_stream(stream):
-        return torch.empty(nbytes, dtype=torch.uint8, device=device), nbytes
+        return new_workspace(nbytes, device), nbytes
 
 
 def _check_outputs(o, state_out, o_shape, s_shape, out_dtype):

@@ -18,6 +18,7 @@ namespace {
 thread_local std::string g_last_error;
 thread_local hipEvent_t g_ev_before = nullptr;   // optional timing of the main kernel
 thread_local hipEvent_t g_ev_after = nullptr;
+thread_local int g_split_launches = 1;           // 1: one launch where possible; 3: always three
 
 wkv_status_t fail(wkv_status_t st, const char *fmt, ...) {
     char buf[512];
@@ -77,6 +78,9 @@ size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 void layout_workspace(Plan &p, bool varlen) {
     size_t off = 0;
     const size_t items = (size_t)p.g.n_seg * p.g.H;
+    // every nonzero workspace starts with the control records, so that calls
+    // of any sizes can share one workspace without disturbing them
+    if (p.split || varlen) off = WKV_WORKSPACE_CONTROL_BYTES;
     if (p.split) {
         p.off_seg_state = off;
         // aggregates only for segments that are not the last of their sequence
@@ -260,10 +264,37 @@ wkv_status_t check_pointers(const Plan &p, const Variant &var, const void *r, co
 
 // ---- execution --------------------------------------------------------------
 
+// A split bf16 call with segments of at most kOneLaunchSegment tokens runs as
+// one launch (wkv_split_kernel) when its (sequence, head) pairs have control
+// records and all its state workgroups fit on the device at once (the
+// condition under which its waits are safe); otherwise as the state pass, the
+// segment scan and the chunked scan.  Measured per call, three launches -> one:
+// segments of 256 tokens (T = 4096, H = 32) 47.4 -> 46.2 us, 512 (B = 2)
+// 75.7 -> 73.8 us, 1024 (B = 4) 144.8 -> 138.0 us; 4096 (T = 65536) 543 -> 565
+// us and 32768 (T = 262144, H = 64) 3.96 -> 4.45 ms.  With long segments the
+// first segments' chunked scans, which start at once, take bandwidth from the
+// state pass, and the kernel boundaries they save are a small share.
+constexpr int64_t kOneLaunchSegment = 1024;
+
+wkv_status_t one_launch(const Plan &p, const Variant &var, bool *yes) {
+    *yes = false;
+    if (!p.split || !p.bf16 || g_split_launches != 1) return WKV_OK;
+    if (p.g.seg_len > kOneLaunchSegment) return WKV_OK;
+    if ((int64_t)p.g.n_seq * p.g.H > kCtlRecords) return WKV_OK;
+    const int64_t items = (int64_t)p.g.n_seg * p.g.H;
+    if (2 * items * 256 > 0xFFFFFFFFll) return WKV_OK;
+    int64_t capacity = 0;
+    if (hipError_t e = split_launch_capacity(var, &capacity)) return fail_hip(e, "occupancy query");
+    *yes = (int64_t)(p.g.n_seg - p.g.n_seq) * p.g.H <= capacity;
+    return WKV_OK;
+}
+
 wkv_status_t run(const Plan &p, const Tensors &t, const Variant &var, void *ws, hipStream_t st) {
     Geometry g = p.g;
     char *base = static_cast<char *>(ws);
     hipError_t e;
+    bool fused = false;
+    if (wkv_status_t s = one_launch(p, var, &fused)) return s;
     if (g.uniform_T < 0) {
         if (!g.cu) return fail(WKV_EINVAL, "packed launch without device offsets");
         int32_t *seg_off = reinterpret_cast<int32_t *>(base + p.off_seg_off);
@@ -287,6 +318,7 @@ wkv_status_t run(const Plan &p, const Tensors &t, const Variant &var, void *ws, 
     if (p.split) {
         w.seg_state = reinterpret_cast<float *>(base + p.off_seg_state);
         w.seg_start = reinterpret_cast<float *>(base + p.off_seg_start);
+        if (fused) w.ctl = reinterpret_cast<SplitCtl *>(base);
     }
     if ((e = launch_chunked(g, t, w, p.split, var, st, tm)) != hipSuccess) return fail_hip(e, "scan launch");
     return WKV_OK;
@@ -395,6 +427,12 @@ const char *wkv_last_error(void) { return g_last_error.c_str(); }
 wkv_status_t wkv_set_kernel_timing_events(void *before, void *after) {
     g_ev_before = static_cast<hipEvent_t>(before);
     g_ev_after = static_cast<hipEvent_t>(after);
+    return WKV_OK;
+}
+
+wkv_status_t wkv_set_split_launches(int launches) {
+    if (launches != 1 && launches != 3) return fail(WKV_EINVAL, "launches=%d must be 1 or 3", launches);
+    g_split_launches = launches;
     return WKV_OK;
 }
 

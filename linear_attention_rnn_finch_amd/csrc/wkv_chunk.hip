@@ -52,6 +52,8 @@
 
 #include <hip/hip_ext.h>
 
+#include <atomic>
+
 #include "wkv_internal.h"
 
 namespace finch {
@@ -412,17 +414,25 @@ __device__ __forceinline__ void set_progress_priority(int c, int n) {
     }
 }
 
-// One segment of one head, chunk by chunk, from the state at s_src (zeros if
-// null) held in registers: o of every token is stored and, with keep_state, S
-// ends as the state after the segment (without it the last chunk skips the
-// state update: a segment that does not end its sequence hands no state on,
-// its successor starts from the combined start state).  The state's loads are issued after the first chunk's,
-// so that the first wait for inputs does not also wait for the state (load
-// counters drain in issue order); the state is first read after the
-// pre-processing of that chunk.
-template <bool LOGD, bool C2, typename SM>
+// Where a segment's starting state comes from: begin() runs before the first
+// chunk's loads are issued, load(S) after them.
+struct PublicState {                      // state_in, a start state of the scan, or zeros (null)
+    const float *src;
+    __device__ void begin() {}
+    __device__ void load(float (&S)[4][4]) { load_public_state(src, S); }
+};
+
+// One segment of one head, chunk by chunk, from the state that src.load(S)
+// puts in registers: o of every token is stored and, with keep_state, S ends
+// as the state after the segment (without it the last chunk skips the state
+// update: a segment that does not end its sequence hands no state on, its
+// successor starts from the combined start state).  The state is loaded after
+// the first chunk's loads are issued, so that the first wait for inputs does
+// not also wait for the state (load counters drain in issue order); it is
+// first read after the pre-processing of that chunk.
+template <bool LOGD, bool C2, typename SM, typename Src>
 __device__ __forceinline__ void scan_chunks(SM &sm, const Tensors &t, int64_t seg_t0, int64_t seg_t1,
-                                            int h, int H, const float *s_src, bool keep_state,
+                                            int h, int H, Src &src, bool keep_state,
                                             float (&S)[4][4]) {
     constexpr bool kU2 = C2;                               // second value staged and added
     const int tid = threadIdx.x;
@@ -522,8 +532,9 @@ __device__ __forceinline__ void scan_chunks(SM &sm, const Tensors &t, int64_t se
     };
 
     ChunkRegs<kU2> P;
+    src.begin();
     if (n_chunks > 0) issue_loads(P, seg_t0);
-    load_public_state(s_src, S);
+    src.load(S);
 
     for (int c = 0; c < n_chunks; ++c) {
         const int64_t tc = seg_t0 + (int64_t)c * kChunk;
@@ -1099,11 +1110,216 @@ __global__ __launch_bounds__(256, 2) void wkv_chunk_kernel(Geometry g, Tensors t
     else if (t.state_in)
         s_src = t.state_in + ((size_t)it.n * g.H + h) * (kHeadDim * kHeadDim);
     const bool keep = t.state_out && it.p == it.P - 1;
-    scan_chunks<LOGD, C2>(sm, t, it.t0, it.t1, h, g.H, s_src, keep, S);
+    PublicState src{s_src};
+    scan_chunks<LOGD, C2>(sm, t, it.t0, it.t1, h, g.H, src, keep, S);
     if (keep)
         store_public_state(t.state_out + ((size_t)it.n * g.H + h) * (kHeadDim * kHeadDim), S);
 }
 
+
+// ---- one launch for split sequences ---------------------------------------------
+//
+// The state pass, the segment scan and the chunked scan of a split call as one
+// grid of 2 * items workgroups, so that no kernel boundary separates them and
+// the chunked scan of a segment starts as soon as a compute unit frees up.
+// Workgroups [0, items) take the state role for item = blockIdx: for every
+// segment but the last of its sequence, the zero-start aggregate B_p and its
+// log2-decay, published to the workspace; then, once every aggregate of the
+// (sequence, head) is there, each of its P - 1 state workgroups chains a
+// share of the 4096 state entries through all segments,
+//   S_{q+1} = diag(2^{Lam_q}) S_q + B_q,   S_0 = state_in (or zeros),
+// and writes its share of every start state.  Workgroups [items, 2 * items)
+// take the main role for item = blockIdx - items: the chunked scan of the
+// segment, from state_in (first segment) or from the start state, which it
+// waits for after issuing its first chunk's loads.
+//
+// Waits.  A state workgroup waits only for the other state workgroups of its
+// (sequence, head), and a main workgroup only for those.  Workgroups are
+// dispatched in index order, every state workgroup precedes every main
+// workgroup, and the host launches this form only when all state workgroups
+// fit on the device at once, so every workgroup waited for is resident or
+// finished.  Each wait is bounded (kWaitTicks) and marks the record's error
+// word if the bound expires, so no launch can hang.
+//
+// Memory.  Everything handed between workgroups (aggregates, start states,
+// counters, flags) is written and read with agent-scope atomic accesses,
+// which go through to the level that every XCD shares; a publisher waits for
+// its stores to complete before it counts itself.  No cache-wide release or
+// acquire is needed.  The per-(sequence, head) control records (SplitCtl)
+// carry an epoch that the last workgroup advances, so no record is cleared
+// between calls.
+constexpr uint64_t kWaitTicks = 1ull << 27;     // ~1.3 s of the 100 MHz clock: a safety bound only
+constexpr int kChainBatch = 16;                 // aggregates whose loads are issued together
+
+__device__ __forceinline__ int ctl_load(int *p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void ctl_store(int *p, int x) {
+    __hip_atomic_store(p, x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float x_load(const float *p) {
+    return __hip_atomic_load(const_cast<float *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void x_store(float *p, float x) {
+    __hip_atomic_store(p, x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// Every thread: wait until its stores have completed, then meet the others,
+// so that thread 0 may announce them.
+__device__ __forceinline__ void complete_stores() {
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+}
+// Thread 0: count the workgroup in *ctr; the last of n resets the counter and
+// sets *flag = val.
+__device__ __forceinline__ bool ctl_arrive(int *ctr, int n, int *flag, int val) {
+    if (__hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != n - 1) return false;
+    ctl_store(ctr, 0);
+    ctl_store(flag, val);
+    return true;
+}
+// Thread 0: wait until *flag == val (bounded; on expiry the record is marked).
+__device__ __forceinline__ void ctl_wait(int *flag, int val, int *err) {
+    const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+    while (ctl_load(flag) != val) {
+        __builtin_amdgcn_s_sleep(2);
+        if (__builtin_amdgcn_s_memrealtime() - t0 > kWaitTicks) {
+            ctl_store(err, 1);
+            return;
+        }
+    }
+}
+
+// Start state of a main-role workgroup: state_in (or zeros) for the first
+// segment of a sequence, else the published start state.  Then the flag is
+// read before the first chunk's loads are issued, so that checking it waits
+// for that one load only, and the state is read with agent-scope loads.
+struct SplitStartState {
+    SplitCtl *rec;                          // null: a first segment
+    const float *first;                     // state_in of the sequence, or null
+    const float *src;                       // published start state
+    int epoch;                              // thread 0 only
+    int seen = 0;
+    __device__ void begin() {
+        if (rec && threadIdx.x == 0) seen = ctl_load(&rec->started);
+    }
+    __device__ void load(float (&S)[4][4]) {
+        if (!rec) {
+            load_public_state(first, S);
+            return;
+        }
+        const int tid = threadIdx.x;
+        if (tid == 0 && seen != epoch + 1) ctl_wait(&rec->started, epoch + 1, &rec->error);
+        __syncthreads();
+        const int wave = tid >> 6, i16 = tid & 15, grp = (tid & 63) >> 4;
+        #pragma unroll
+        for (int ib = 0; ib < 4; ++ib)
+            #pragma unroll
+            for (int e = 0; e < 4; ++e) S[ib][e] = x_load(src + (16 * ib + 4 * grp + e) * kHeadDim + 16 * wave + i16);
+    }
+};
+
+template <bool C2>
+union SmemSplit {
+    Smem<C2 ? 4 : 3> main;
+    SmemState state;
+};
+
+template <bool LOGD, bool C2>
+__global__ __launch_bounds__(256, 2) void wkv_split_kernel(Geometry g, Tensors t, Workspace ws) {
+    __shared__ SmemSplit<C2> sm;
+    const int items = g.n_seg * g.H;
+    const bool state_role = (int)blockIdx.x < items;
+    const int item = state_role ? (int)blockIdx.x : (int)blockIdx.x - items;
+    const int h = item % g.H;
+    const int seg = item / g.H;
+    const ItemRange it = decode_segment(g, seg);
+    if (!it.valid) return;
+    const bool split = it.P > 1;
+    // a split the host did not plan (device offsets differing from the host
+    // copy) has no workspace behind it: leave the item alone
+    if (split && (ws.ctl == nullptr || ws.seg_state == nullptr || ws.seg_start == nullptr)) return;
+    if (state_role && (!split || it.p == it.P - 1)) return;   // the last segment's aggregate is unused
+    const int tid = threadIdx.x;
+    const int n_state = it.P - 1;
+    const size_t slot = ((size_t)it.n * g.H + h) * (kHeadDim * kHeadDim);
+    SplitCtl *rec = split ? ws.ctl + ((size_t)it.n * g.H + h) : nullptr;
+    int epoch = 0;                                         // thread 0 only
+    if (split && tid == 0) epoch = ctl_load(&rec->epoch);
+
+    if (state_role) {
+        float S[4][4], lam[4] = {0.f, 0.f, 0.f, 0.f};
+        #pragma unroll
+        for (int ib = 0; ib < 4; ++ib)
+            #pragma unroll
+            for (int e = 0; e < 4; ++e) S[ib][e] = 0.f;
+        state_run<LOGD, C2>(sm.state, t, it.t0, it.t1, h, g.H, S, lam);
+        // publish B_p ([key][value]) and its log2-decays
+        const size_t agg0 = (size_t)(seg - it.p - it.n) * g.H + h;   // aggregate of segment 0
+        float *dst = ws.seg_state + (agg0 + (size_t)it.p * g.H) * kSegStateFloats;
+        {
+            const int wave = tid >> 6, i16 = tid & 15, grp = (tid & 63) >> 4;
+            #pragma unroll
+            for (int ib = 0; ib < 4; ++ib)
+                #pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    x_store(dst + (16 * ib + 4 * grp + e) * kHeadDim + 16 * wave + i16, S[ib][e]);
+            if (i16 == 15) {
+                #pragma unroll
+                for (int q = 0; q < 4; ++q) x_store(dst + kHeadDim * kHeadDim + 16 * wave + 4 * grp + q, lam[q]);
+            }
+        }
+        complete_stores();
+        if (tid == 0 && !ctl_arrive(&rec->arrived, n_state, &rec->ready, epoch + 1))
+            ctl_wait(&rec->ready, epoch + 1, &rec->error);
+        __syncthreads();
+        // this workgroup's share of the chain: rows of 256 entries (one per
+        // thread) numbered p, p + P - 1, ...
+        const float *s_in = t.state_in ? t.state_in + slot : nullptr;
+        const size_t start0 = (size_t)(seg - it.p) * g.H + h;         // start state of segment 0
+        for (int sl = it.p; sl < (kHeadDim * kHeadDim) / 256; sl += n_state) {
+            const int e = 256 * sl + tid;
+            const int row = e / kHeadDim;
+            float x = s_in ? s_in[e] : 0.f;
+            for (int q0 = 0; q0 < n_state; q0 += kChainBatch) {
+                float b[kChainBatch], l[kChainBatch];
+                #pragma unroll
+                for (int q = 0; q < kChainBatch; ++q) {
+                    b[q] = 0.f;
+                    l[q] = 0.f;
+                    if (q0 + q < n_state) {
+                        const float *agg = ws.seg_state + (agg0 + (size_t)(q0 + q) * g.H) * kSegStateFloats;
+                        b[q] = x_load(agg + e);
+                        l[q] = x_load(agg + kHeadDim * kHeadDim + row);
+                    }
+                }
+                #pragma unroll
+                for (int q = 0; q < kChainBatch; ++q) {
+                    if (q0 + q < n_state) {
+                        const float d = __builtin_amdgcn_exp2f(l[q]);
+                        x = d * x + b[q];
+                        x_store(ws.seg_start + (start0 + (size_t)(q0 + q + 1) * g.H) * kSegStartFloats + e, x);
+                    }
+                }
+            }
+        }
+        complete_stores();
+        if (tid == 0) ctl_arrive(&rec->scanned, n_state, &rec->started, epoch + 1);
+        return;
+    }
+
+    // main role
+    const bool keep = t.state_out && it.p == it.P - 1;
+    float S[4][4];
+    const bool later = split && it.p > 0;
+    SplitStartState src{later ? rec : nullptr, t.state_in ? t.state_in + slot : nullptr,
+                        later ? ws.seg_start + (size_t)item * kSegStartFloats : nullptr, epoch};
+    scan_chunks<LOGD, C2>(sm.main, t, it.t0, it.t1, h, g.H, src, keep, S);
+    // the main workgroups of later segments count the call done: each has seen
+    // every start state published, so every other use of the record in this
+    // call is over once all of them have arrived
+    if (later && tid == 0) ctl_arrive(&rec->done, n_state, &rec->epoch, epoch + 1);
+    if (keep) store_public_state(t.state_out + slot, S);
+}
 
 // ---- producer/consumer form of the chunked scan (fixed-length batches) -------
 //
@@ -1551,11 +1767,51 @@ __global__ __launch_bounds__(512, 1) void wkv_chunk_pc_kernel(Geometry g, Tensor
 
 }  // namespace
 
+namespace {
+using KernelFn = void (*)(Geometry, Tensors, Workspace);
+KernelFn split_kernel_for(const Variant &v) {
+    return v.log_decay ? (v.c2 ? wkv_split_kernel<true, true> : wkv_split_kernel<true, false>)
+                       : (v.c2 ? wkv_split_kernel<false, true> : wkv_split_kernel<false, false>);
+}
+}  // namespace
+
+hipError_t split_launch_capacity(const Variant &v, int64_t *capacity) {
+    constexpr int kMaxDevices = 64;
+    static std::atomic<int64_t> cache[kMaxDevices][4];       // 0: not yet measured
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    const int form = (v.log_decay ? 1 : 0) + (v.c2 ? 2 : 0);
+    if (dev >= 0 && dev < kMaxDevices) {
+        const int64_t c = cache[dev][form].load(std::memory_order_relaxed);
+        if (c > 0) {
+            *capacity = c;
+            return hipSuccess;
+        }
+    }
+    int cus = 0, per_cu = 0;
+    if ((e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess) return e;
+    if ((e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, split_kernel_for(v), 256, 0)) != hipSuccess)
+        return e;
+    *capacity = (int64_t)cus * per_cu;
+    if (dev >= 0 && dev < kMaxDevices && *capacity > 0) cache[dev][form].store(*capacity, std::memory_order_relaxed);
+    return hipSuccess;
+}
+
 hipError_t launch_chunked(const Geometry &g, const Tensors &t, const Workspace &ws, bool split,
                           Variant v, hipStream_t st, KernelTiming tm) {
     const int64_t items = (int64_t)g.n_seg * g.H;
     if (items <= 0) return hipSuccess;
     const dim3 grid((unsigned)items), block(256);
+    if (split && ws.ctl) {                             // one launch: state, scan and chunked roles
+        const dim3 grid2((unsigned)(2 * items));
+        const KernelFn k = split_kernel_for(v);
+        if (tm.start || tm.stop)
+            hipExtLaunchKernelGGL(k, grid2, block, 0, st, tm.start, tm.stop, 0, g, t, ws);
+        else
+            hipLaunchKernelGGL(k, grid2, block, 0, st, g, t, ws);
+        return hipGetLastError();
+    }
     if (split) {
         void (*ks)(Geometry, Tensors, Workspace) =
             v.log_decay ? (v.c2 ? wkv_state_kernel<true, true> : wkv_state_kernel<true, false>)

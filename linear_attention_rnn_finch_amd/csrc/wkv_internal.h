@@ -4,6 +4,7 @@
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+#include "finch_wkv.h"
 
 namespace finch {
 
@@ -120,16 +121,39 @@ struct Variant {
     bool o_bf16 = false;     // o stored as bf16 (round to nearest even)
 };
 
+// Control record of one (sequence, head) for the one-launch split path: the
+// workgroups of a call meet through these counters and flags (agent-scope
+// atomics).  A flag is set to epoch + 1 and read against that value, and the
+// last main workgroup of the (sequence, head) to finish advances the epoch, so a
+// record is ready for the next call without any clearing; counters return to
+// zero at the end of each call.  A record must be zero before its first use.
+struct SplitCtl {
+    int epoch;      // calls that have completed on this record
+    int done;       // main workgroups of later segments that have finished
+    int arrived;    // state workgroups that have published their aggregate
+    int ready;      // epoch + 1: every aggregate of the call is published
+    int scanned;    // state workgroups that have written their start-state slices
+    int started;    // epoch + 1: every start state of the call is written
+    int error;      // sticky: a bounded wait expired (results of that call are void)
+    int pad[9];
+};
+static_assert(sizeof(SplitCtl) == 64, "one 64-byte record per (sequence, head)");
+// records at the head of every split plan's workspace: calls with more
+// (sequence, head) pairs take the three-launch path
+constexpr int kCtlRecords = WKV_WORKSPACE_CONTROL_BYTES / (int)sizeof(SplitCtl);
+
 // Workspace views (fp32).  seg_state[(s - n) * H + h]: the zero-start end
 // state (D*D) of global segment s of sequence n, followed by its total
 // log2-decay per key channel (D); only segments that are not the last of their
 // sequence have one, and s - n numbers them.  seg_start[item]: the state
-// entering the segment (D*D).
+// entering the segment (D*D).  ctl: the control records (one-launch path only,
+// else null), record n * H + h.
 struct Workspace {
     float *seg_state;
     float *seg_start;
     int32_t *seg_off;
     int32_t *seg_seq;
+    SplitCtl *ctl;
 };
 constexpr int kSegStateFloats = kHeadDim * kHeadDim + kHeadDim;
 constexpr int kSegStartFloats = kHeadDim * kHeadDim;
@@ -149,10 +173,14 @@ hipError_t launch_serial(const Geometry &g, const Tensors &t, bool bf16, Variant
 // longest): one wave per (sequence, head), fp32 state in registers
 hipError_t launch_decode(const Geometry &g, const Tensors &t, bool bf16, Variant v, int max_len, hipStream_t st,
                          KernelTiming tm = {});
-// bf16 path: when some sequence is split (split), the state pass and the
-// segment scan, then the chunked scan (the kernel the timing events attach to).
+// bf16 path: when some sequence is split (split), either one launch of the
+// split kernel (ws.ctl set) or the state pass and the segment scan, then the
+// chunked scan (the kernel the timing events attach to).
 hipError_t launch_chunked(const Geometry &g, const Tensors &t, const Workspace &ws, bool split,
                           Variant v, hipStream_t st, KernelTiming tm = {});
+// workgroups of the one-launch split kernel that the current device holds at
+// once (compute units x resident workgroups per unit)
+hipError_t split_launch_capacity(const Variant &v, int64_t *capacity);
 // epilogue of Finch-C2 pre-fill: LayerNorm over heads, GOLD key compression
 hipError_t launch_layernorm_rows(const float *x, const float *gamma, const float *beta, float eps, void *y,
                                  bool out_bf16, int64_t rows, int width, hipStream_t st, KernelTiming tm = {});

@@ -61,7 +61,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_abi_version_and_status_strings(lib):
-    assert lib.wkv_abi_version() == 3
+    assert lib.wkv_abi_version() == 4
     for s in range(5):
         assert lib.wkv_status_string(s)
     assert lib.wkv_status_string(99) == b"unknown status"
@@ -126,6 +126,31 @@ def test_workspace_checks(lib):
     before = lib.wkv_last_error()
     lib.wkv_prefill_workspace_bytes(1, 64, 1, 32, BF16)
     assert lib.wkv_last_error() == before
+
+
+def test_workspaces_start_with_the_control_records(lib):
+    """Every nonzero workspace holds the 256 KiB of control records first and
+    the split plan's scratch after them: the 1.5B-class layer (T = 4096,
+    H = 32, 16 segments) needs 15 x 32 aggregates of 16,640 bytes and 16 x 32
+    start states of 16,384 bytes behind them, each array 256-byte aligned; a
+    packed call that is not split still keeps the records ahead of its
+    segment tables."""
+    ctl = 262144
+    assert re.search(r"#define WKV_WORKSPACE_CONTROL_BYTES %d\b" % ctl, open(HEADER).read())
+    align = lambda x: -(-x // 256) * 256
+    assert lib.wkv_prefill_workspace_bytes(1, 4096, 32, 64, BF16) == (
+        ctl + align(15 * 32 * 16640) + align(16 * 32 * 16384))
+    cu = np.array([0, 100, 200], dtype=np.int32)       # two short sequences: no split
+    assert lib.wkv_prefill_varlen_workspace_bytes(cu.ctypes.data, 2, 4, 64, BF16) == ctl + 256 + 256
+
+
+def test_split_launch_switch(lib):
+    lib.wkv_set_split_launches.restype = ctypes.c_int
+    lib.wkv_set_split_launches.argtypes = [ctypes.c_int]
+    assert lib.wkv_set_split_launches(2) == EINVAL
+    assert b"launches" in lib.wkv_last_error()
+    assert lib.wkv_set_split_launches(3) == OK
+    assert lib.wkv_set_split_launches(1) == OK
 
 
 def test_whole_sequence_plans_need_no_workspace(lib):

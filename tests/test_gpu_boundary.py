@@ -29,7 +29,7 @@ def test_plain_wkv_prefill_through_ctypes():
     o = torch.empty((B, T, H, D), dtype=torch.float32, device="cuda")
     st = torch.empty((B, H, D, D), dtype=torch.float32, device="cuda")
     need = fw.workspace_bytes(B, T, H, D)
-    ws = torch.empty(max(need, 1), dtype=torch.uint8, device="cuda")
+    ws = fw.new_workspace(need, "cuda")
     lib = _binding._lib
     status = lib.wkv_prefill(_ptr(g["r"]), _ptr(g["k"]), _ptr(g["v"]), _ptr(g["w"]), _ptr(g["u"]),
                              _ptr(g["state0"]), _ptr(o), _ptr(st), B, T, H, D, _binding.WKV_BF16,
@@ -52,7 +52,7 @@ def test_plain_wkv_prefill_varlen_through_ctypes():
     st = torch.empty((N, H, D, D), dtype=torch.float32, device="cuda")
     cu_host = g["cu_host"].contiguous()
     need = fw.varlen_workspace_bytes(cu_host, H, D)
-    ws = torch.empty(max(need, 1), dtype=torch.uint8, device="cuda")
+    ws = fw.new_workspace(need, "cuda")
     lib = _binding._lib
     status = lib.wkv_prefill_varlen(_ptr(g["r"]), _ptr(g["k"]), _ptr(g["v"]), _ptr(g["w"]),
                                     _ptr(g["u"]), _ptr(g["cu"]), ctypes.c_void_p(cu_host.data_ptr()), N,

@@ -165,7 +165,7 @@ def test_graph_replays_match_eager():
     B, T, H, D = g["r"].shape
     o = torch.empty((B, T, H, D), dtype=torch.float32, device="cuda")
     st = torch.empty((B, H, D, D), dtype=torch.float32, device="cuda")
-    ws = torch.zeros(max(fw.workspace_bytes(B, T, H, D), 1), dtype=torch.uint8, device="cuda")
+    ws = fw.new_workspace(fw.workspace_bytes(B, T, H, D), "cuda")
     o_ref, s_ref = run_gpu(wl, g)
     torch.cuda.synchronize()
     graph = torch.cuda.CUDAGraph()
@@ -181,7 +181,7 @@ def test_graph_replays_match_eager():
     for rep in range(4):
         o.fill_(float("nan"))
         st.fill_(float("nan"))
-        ws.fill_(0xAB)
+        ws[fw.WORKSPACE_CONTROL_BYTES:].fill_(0xAB)      # scratch; the control records are kept
         torch.cuda.synchronize()
         graph.replay()
         torch.cuda.synchronize()

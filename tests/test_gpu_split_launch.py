@@ -1,0 +1,161 @@
+"""The one-launch form of split calls (wkv_split_kernel): state pass, segment
+combine and chunked scan as workgroup roles of one grid, handing segment
+states to each other through the workspace's control records.
+
+Every case runs both launch forms on the same inputs: one launch must equal
+the three launches (state pass, segment scan, chunked scan) bit for bit, both
+must match the fp64 oracle, and after each call the control records must be
+ready for the next one (counters back at zero, flags at the new epoch, no
+expired wait)."""
+import numpy as np
+import pytest
+
+from synth import make_workload
+from gpu_util import log, to_gpu, run_gpu, run_oracle, errors
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+FORMS = [("w", "finch"), ("log", "finch"), ("w", "c2"), ("log", "c2")]
+IDS = ["w", "logdecay", "c2", "c2_logdecay"]
+# SplitCtl fields (16 ints per (sequence, head) record)
+EPOCH, DONE, ARRIVED, READY, SCANNED, STARTED, ERROR = range(7)
+
+
+def _records(ws, n):
+    import linear_attention_rnn_finch_amd as fw
+    assert ws.numel() >= fw.WORKSPACE_CONTROL_BYTES
+    return ws[:fw.WORKSPACE_CONTROL_BYTES].view(torch.int32).view(-1, 16)[:n].cpu().numpy()
+
+
+def _check_records(rec, calls):
+    """Records of (sequence, head) pairs that ran `calls` one-launch calls."""
+    assert (rec[:, ERROR] == 0).all(), "a bounded wait expired"
+    assert (rec[:, [DONE, ARRIVED, SCANNED]] == 0).all(), rec[:4]
+    assert (rec[:, EPOCH] == calls).all(), rec[:4, EPOCH]
+    assert (rec[:, READY] == calls).all() and (rec[:, STARTED] == calls).all()
+
+
+def _both_forms(wl, g, ws):
+    import linear_attention_rnn_finch_amd as fw
+    out = {}
+    for launches in (3, 1):
+        fw.set_split_launches(launches)
+        try:
+            out[launches] = run_gpu(wl, g, workspace=ws)
+            torch.cuda.synchronize()
+        finally:
+            fw.set_split_launches(1)
+    return out
+
+
+def _workspace(wl):
+    import linear_attention_rnn_finch_amd as fw
+    B, T, H, D = (wl.r.shape if not wl.packed else (None, None) + wl.r.shape[1:])
+    if wl.packed:
+        need = fw.varlen_workspace_bytes(torch.from_numpy(wl.cu_seqlens.astype(np.int32)), H, D)
+    else:
+        need = fw.workspace_bytes(B, T, H, D)
+    return fw.new_workspace(need, "cuda")
+
+
+@pytest.mark.parametrize("decay,variant", FORMS, ids=IDS)
+def test_one_launch_equals_three_launches(decay, variant):
+    """2 x 2000 tokens x 8 heads with an initial state: segments of 256 tokens
+    (8 per sequence, the last one partial), every form."""
+    wl = make_workload(3, B=2, T=2000, H=8, decay=decay, variant=variant)
+    g = to_gpu(wl)
+    ws = _workspace(wl)
+    log("case one/three launches decay=%s variant=%s" % (decay, variant))
+    out = _both_forms(wl, g, ws)
+    assert torch.equal(out[1][0], out[3][0]) and torch.equal(out[1][1], out[3][1])
+    _check_records(_records(ws, 2 * 8), calls=1)
+    o_ref, s_ref = run_oracle(wl)
+    eo, es = errors(wl, out[1][0], out[1][1], o_ref, s_ref)
+    assert eo <= 2e-3 and es <= 2e-3, (eo, es)
+
+
+def test_layer_workload_records_and_repeats():
+    """The 1.5B-class layer (T = 4096, H = 32, 16 segments of 256 tokens):
+    five calls in a row on one workspace, each equal to the first and to three
+    launches; the records count the calls."""
+    import linear_attention_rnn_finch_amd as fw
+    wl = make_workload(1)
+    g = to_gpu(wl)
+    ws = _workspace(wl)
+    o1, s1 = run_gpu(wl, g, workspace=ws)
+    for _ in range(4):
+        o, s = run_gpu(wl, g, workspace=ws)
+        torch.cuda.synchronize()
+        assert torch.equal(o, o1) and torch.equal(s, s1)
+    _check_records(_records(ws, 32), calls=5)
+    fw.set_split_launches(3)
+    try:
+        o3, s3 = run_gpu(wl, g, workspace=ws)
+        torch.cuda.synchronize()
+    finally:
+        fw.set_split_launches(1)
+    assert torch.equal(o3, o1) and torch.equal(s3, s1)
+    _check_records(_records(ws, 32), calls=5)          # three launches leave the records alone
+
+
+@pytest.mark.parametrize("decay,variant", [("w", "finch"), ("log", "c2")], ids=["w", "c2_logdecay"])
+def test_ragged_one_launch(decay, variant):
+    """Packed sequences of mixed lengths (empty, shorter than a chunk, split
+    into many segments) with an initial state."""
+    lengths = [1700, 0, 64, 2500, 5, 900, 3]
+    wl = make_workload(4, lengths=lengths, H=6, decay=decay, variant=variant)
+    g = to_gpu(wl)
+    ws = _workspace(wl)
+    out = _both_forms(wl, g, ws)
+    assert torch.equal(out[1][0], out[3][0]) and torch.equal(out[1][1], out[3][1])
+    rec = _records(ws, len(lengths) * 6).reshape(len(lengths), 6, 16)
+    split = [n for n, L in enumerate(lengths) if L > 256]
+    _check_records(rec[split].reshape(-1, 16), calls=1)
+    assert (rec[[n for n in range(len(lengths)) if n not in split]] == 0).all()   # never split: untouched
+    o_ref, s_ref = run_oracle(wl)
+    eo, es = errors(wl, out[1][0], out[1][1], o_ref, s_ref)
+    assert eo <= 2e-3 and es <= 2e-3, (eo, es)
+
+
+def test_one_workspace_serves_calls_of_other_sizes():
+    """A workspace sized for the largest call, shared by calls of other
+    geometries in turn (their records overlap differently each time)."""
+    import linear_attention_rnn_finch_amd as fw
+    shapes = [(1, 4096, 32), (2, 1500, 8), (1, 2000, 16), (3, 700, 4), (1, 4096, 32)]
+    need = max(fw.workspace_bytes(B, T, H, 64) for B, T, H in shapes)
+    ws = fw.new_workspace(need, "cuda")
+    for i, (B, T, H) in enumerate(shapes):
+        wl = make_workload(3, B=B, T=T, H=H, decay="log" if i % 2 else "w")
+        log("case shared workspace B=%d T=%d H=%d" % (B, T, H))
+        g = to_gpu(wl)
+        o, s = run_gpu(wl, g, workspace=ws)
+        torch.cuda.synchronize()
+        assert int(_records(ws, 4096)[:, ERROR].max()) == 0
+        o_ref, s_ref = run_oracle(wl)
+        eo, es = errors(wl, o, s, o_ref, s_ref)
+        assert eo <= 2e-3 and es <= 2e-3, (B, T, H, eo, es)
+
+
+def test_more_pairs_than_records_take_three_launches():
+    """4128 (sequence, head) pairs (129 sequences x 32 heads), one of them
+    split: more pairs than the control records hold, so the call takes the
+    three launches and leaves the records untouched; 128 sequences (4096
+    pairs) take the one launch."""
+    import linear_attention_rnn_finch_amd as fw
+    for n_short, one in ((128, False), (127, True)):
+        lengths = [3000] + [20] * n_short
+        wl = make_workload(4, lengths=lengths, H=32)
+        g = to_gpu(wl)
+        ws = _workspace(wl)
+        o, s = run_gpu(wl, g, workspace=ws)
+        torch.cuda.synchronize()
+        rec = _records(ws, fw.WORKSPACE_CONTROL_BYTES // 64)
+        if one:
+            _check_records(rec[:32], calls=1)               # sequence 0, all heads
+        else:
+            assert (rec == 0).all()
+        o_ref, s_ref = run_oracle(wl)
+        eo, es = errors(wl, o, s, o_ref, s_ref)
+        assert eo <= 2e-3 and es <= 2e-3, (n_short, eo, es)
