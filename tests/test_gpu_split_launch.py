@@ -159,3 +159,34 @@ def test_more_pairs_than_records_take_three_launches():
         o_ref, s_ref = run_oracle(wl)
         eo, es = errors(wl, o, s, o_ref, s_ref)
         assert eo <= 2e-3 and es <= 2e-3, (n_short, eo, es)
+
+
+def test_random_shapes():
+    """Seeded random fixed and ragged calls in every form (segments of 256
+    tokens, 2 to 12 per sequence, 1 to 16 heads, with and without states):
+    one launch equals three launches bit for bit, matches the oracle, and
+    leaves every record of a split sequence ready for the next call."""
+    rng = np.random.default_rng(20261203)
+    for case in range(28):
+        decay, variant = FORMS[case % 4]
+        H = int(rng.integers(1, 17))
+        cfg = 3 if case % 3 else 1                          # with an initial state, or without
+        if case % 2:
+            lengths = [int(x) for x in rng.integers(0, 3000, size=int(rng.integers(2, 6)))]
+            wl = make_workload(4, lengths=lengths, H=H, decay=decay, variant=variant)
+        else:
+            B, T = int(rng.integers(1, 4)), int(rng.integers(300, 3000))
+            lengths = [T] * B
+            wl = make_workload(cfg, B=B, T=T, H=H, decay=decay, variant=variant)
+        log("case random %d lengths=%s H=%d decay=%s variant=%s" % (case, lengths, H, decay, variant))
+        g = to_gpu(wl)
+        ws = _workspace(wl)
+        out = _both_forms(wl, g, ws)
+        assert torch.equal(out[1][0], out[3][0]) and torch.equal(out[1][1], out[3][1]), case
+        rec = _records(ws, len(lengths) * H).reshape(len(lengths), H, 16)
+        split = [n for n, L in enumerate(lengths) if L > 256]
+        if split:
+            _check_records(rec[split].reshape(-1, 16), calls=1)
+        o_ref, s_ref = run_oracle(wl)
+        eo, es = errors(wl, out[1][0], out[1][1], o_ref, s_ref)
+        assert eo <= 2e-3 and es <= 2e-3, (case, eo, es)
