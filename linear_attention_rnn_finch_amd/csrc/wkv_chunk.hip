@@ -1208,7 +1208,8 @@ struct SplitStartState {
             return;
         }
         const int tid = threadIdx.x;
-        if (tid == 0 && seen != epoch + 1) ctl_wait(&rec->started, epoch + 1, &rec->error);
+        const int want = (int)((unsigned)epoch + 1u);
+        if (tid == 0 && seen != want) ctl_wait(&rec->started, want, &rec->error);
         __syncthreads();
         const int wave = tid >> 6, i16 = tid & 15, grp = (tid & 63) >> 4;
         #pragma unroll
@@ -1243,8 +1244,9 @@ __global__ __launch_bounds__(256, 2) void wkv_split_kernel(Geometry g, Tensors t
     const int n_state = it.P - 1;
     const size_t slot = ((size_t)it.n * g.H + h) * (kHeadDim * kHeadDim);
     SplitCtl *rec = split ? ws.ctl + ((size_t)it.n * g.H + h) : nullptr;
-    int epoch = 0;                                         // thread 0 only
+    int epoch = 0;                                         // thread 0 only; flags hold epoch + 1
     if (split && tid == 0) epoch = ctl_load(&rec->epoch);
+    const int next = (int)((unsigned)epoch + 1u);          // wraps after 2^32 calls
 
     if (state_role) {
         float S[4][4], lam[4] = {0.f, 0.f, 0.f, 0.f};
@@ -1269,41 +1271,54 @@ __global__ __launch_bounds__(256, 2) void wkv_split_kernel(Geometry g, Tensors t
             }
         }
         complete_stores();
-        if (tid == 0 && !ctl_arrive(&rec->arrived, n_state, &rec->ready, epoch + 1))
-            ctl_wait(&rec->ready, epoch + 1, &rec->error);
+        if (tid == 0 && !ctl_arrive(&rec->arrived, n_state, &rec->ready, next))
+            ctl_wait(&rec->ready, next, &rec->error);
         __syncthreads();
         // this workgroup's share of the chain: rows of 256 entries (one per
-        // thread) numbered p, p + P - 1, ...
+        // thread) numbered p, p + P - 1, ...; two rows at a time, their loads
+        // issued together (with 15 state workgroups the first has two rows,
+        // and the head's start states wait for the slowest share)
         const float *s_in = t.state_in ? t.state_in + slot : nullptr;
         const size_t start0 = (size_t)(seg - it.p) * g.H + h;         // start state of segment 0
-        for (int sl = it.p; sl < (kHeadDim * kHeadDim) / 256; sl += n_state) {
-            const int e = 256 * sl + tid;
-            const int row = e / kHeadDim;
-            float x = s_in ? s_in[e] : 0.f;
+        constexpr int kRows = (kHeadDim * kHeadDim) / 256;
+        for (int sl = it.p; sl < kRows; sl += 2 * n_state) {
+            const bool two = sl + n_state < kRows;
+            const int e0 = 256 * sl + tid, e1 = e0 + 256 * n_state;
+            float x0 = s_in ? s_in[e0] : 0.f;
+            float x1 = s_in && two ? s_in[e1] : 0.f;
             for (int q0 = 0; q0 < n_state; q0 += kChainBatch) {
-                float b[kChainBatch], l[kChainBatch];
+                float b0[kChainBatch], l0[kChainBatch], b1[kChainBatch], l1[kChainBatch];
                 #pragma unroll
                 for (int q = 0; q < kChainBatch; ++q) {
-                    b[q] = 0.f;
-                    l[q] = 0.f;
+                    b0[q] = l0[q] = b1[q] = l1[q] = 0.f;
                     if (q0 + q < n_state) {
                         const float *agg = ws.seg_state + (agg0 + (size_t)(q0 + q) * g.H) * kSegStateFloats;
-                        b[q] = x_load(agg + e);
-                        l[q] = x_load(agg + kHeadDim * kHeadDim + row);
+                        b0[q] = x_load(agg + e0);
+                        l0[q] = x_load(agg + kHeadDim * kHeadDim + e0 / kHeadDim);
+                        if (two) {
+                            b1[q] = x_load(agg + e1);
+                            l1[q] = x_load(agg + kHeadDim * kHeadDim + e1 / kHeadDim);
+                        }
                     }
                 }
                 #pragma unroll
                 for (int q = 0; q < kChainBatch; ++q) {
                     if (q0 + q < n_state) {
-                        const float d = __builtin_amdgcn_exp2f(l[q]);
-                        x = d * x + b[q];
-                        x_store(ws.seg_start + (start0 + (size_t)(q0 + q + 1) * g.H) * kSegStartFloats + e, x);
+                        float *dst = ws.seg_start + (start0 + (size_t)(q0 + q + 1) * g.H) * kSegStartFloats;
+                        const float d0 = __builtin_amdgcn_exp2f(l0[q]);
+                        x0 = d0 * x0 + b0[q];
+                        x_store(dst + e0, x0);
+                        if (two) {
+                            const float d1 = __builtin_amdgcn_exp2f(l1[q]);
+                            x1 = d1 * x1 + b1[q];
+                            x_store(dst + e1, x1);
+                        }
                     }
                 }
             }
         }
         complete_stores();
-        if (tid == 0) ctl_arrive(&rec->scanned, n_state, &rec->started, epoch + 1);
+        if (tid == 0) ctl_arrive(&rec->scanned, n_state, &rec->started, next);
         return;
     }
 
@@ -1317,7 +1332,7 @@ __global__ __launch_bounds__(256, 2) void wkv_split_kernel(Geometry g, Tensors t
     // the main workgroups of later segments count the call done: each has seen
     // every start state published, so every other use of the record in this
     // call is over once all of them have arrived
-    if (later && tid == 0) ctl_arrive(&rec->done, n_state, &rec->epoch, epoch + 1);
+    if (later && tid == 0) ctl_arrive(&rec->done, n_state, &rec->epoch, next);
     if (keep) store_public_state(t.state_out + slot, S);
 }
 
