@@ -69,7 +69,7 @@ struct Plan {
     int64_t max_len = 0;             // longest sequence of the call
     bool bf16 = false;
     bool split = false;              // some sequence has more than one segment
-    size_t off_seg_state = 0, off_seg_start = 0, off_seg_off = 0, off_seg_seq = 0;
+    size_t off_seg_state = 0, off_seg_start = 0, off_seg_off = 0, off_seg_seq = 0, off_seg_rank = 0;
     size_t bytes = 0;
 };
 
@@ -93,6 +93,8 @@ void layout_workspace(Plan &p, bool varlen) {
         p.off_seg_off = off;
         off = align256(off + (size_t)(p.g.n_seq + 1) * sizeof(int32_t));
         p.off_seg_seq = off;
+        off = align256(off + (size_t)p.g.n_seg * sizeof(int32_t));
+        p.off_seg_rank = off;
         off = align256(off + (size_t)p.g.n_seg * sizeof(int32_t));
     }
     p.bytes = off;
@@ -300,10 +302,17 @@ wkv_status_t run(const Plan &p, const Tensors &t, const Variant &var, void *ws, 
         int32_t *seg_off = reinterpret_cast<int32_t *>(base + p.off_seg_off);
         int32_t *seg_seq = reinterpret_cast<int32_t *>(base + p.off_seg_seq);
         if (g.n_seq == 0) return WKV_OK;
-        if ((e = launch_plan_varlen(g, seg_off, seg_seq, st)) != hipSuccess)
+        // longest first when the chunked scan has more work items than the
+        // device holds at once (the short ones then fill in at the end)
+        int32_t *seg_rank = nullptr;
+        if (p.bf16 && !fused && p.max_len > kDecodeMaxT && g.n_seq <= kRankMaxSeqs &&
+            (int64_t)g.n_seg * g.H > kTargetItems)
+            seg_rank = reinterpret_cast<int32_t *>(base + p.off_seg_rank);
+        if ((e = launch_plan_varlen(g, seg_off, seg_seq, seg_rank, st)) != hipSuccess)
             return fail_hip(e, "planner launch");
         g.seg_off = seg_off;
         g.seg_seq = seg_seq;
+        g.seg_rank = seg_rank;
     }
     const KernelTiming tm{g_ev_before, g_ev_after};
     if (p.max_len <= kDecodeMaxT && !p.split) {       // recurrent steps: state-streaming kernel

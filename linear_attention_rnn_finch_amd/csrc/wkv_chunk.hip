@@ -1096,9 +1096,10 @@ template <bool LOGD, bool C2>
 __global__ __launch_bounds__(256, 2) void wkv_chunk_kernel(Geometry g, Tensors t, Workspace ws) {
     using SM = Smem<C2 ? 4 : 3>;
     __shared__ SM sm;
-    const int item = blockIdx.x;
-    const int h = item % g.H;
-    const ItemRange it = decode_segment(g, item / g.H);
+    const int h = blockIdx.x % g.H;
+    const int rank = blockIdx.x / g.H;
+    const int seg = g.seg_rank ? g.seg_rank[rank] : rank;      // packed calls: longest first
+    const ItemRange it = decode_segment(g, seg);
     if (!it.valid) return;
     // a split the host did not plan (device offsets differing from the host
     // copy) has no workspace behind it: leave the item alone
@@ -1106,7 +1107,7 @@ __global__ __launch_bounds__(256, 2) void wkv_chunk_kernel(Geometry g, Tensors t
     float S[4][4];
     const float *s_src = nullptr;
     if (it.P > 1)
-        s_src = ws.seg_start + (size_t)item * kSegStartFloats;
+        s_src = ws.seg_start + ((size_t)seg * g.H + h) * kSegStartFloats;
     else if (t.state_in)
         s_src = t.state_in + ((size_t)it.n * g.H + h) * (kHeadDim * kHeadDim);
     const bool keep = t.state_out && it.p == it.P - 1;

@@ -28,6 +28,8 @@ struct Geometry {
     const int32_t *cu;      // packed only: device offsets [n_seq + 1]
     const int32_t *seg_off; // packed only: device, first global segment of sequence n [n_seq + 1]
     const int32_t *seg_seq; // packed only: device, sequence of global segment s (-1: none) [n_seg]
+    const int32_t *seg_rank;// packed only, or null: device, the global segment the chunked scan
+                            // takes as its r-th (segment, head) group, longest first [n_seg]
     // fixed-length only: 1 when every (sequence, head) is one work item of
     // the producer/consumer kernel (no segments, no state pass), else 0
     int whole_seqs;
@@ -186,7 +188,10 @@ hipError_t launch_layernorm_rows(const float *x, const float *gamma, const float
                                  bool out_bf16, int64_t rows, int width, hipStream_t st, KernelTiming tm = {});
 hipError_t launch_gold_compress(const uint16_t *x, const uint16_t *w, void *c, bool out_bf16, int64_t M, int K,
                                 int N, hipStream_t st, KernelTiming tm = {});
-hipError_t launch_plan_varlen(const Geometry &g, int32_t *seg_off, int32_t *seg_seq,
+// packed calls of at most this many sequences can have their segments ranked
+// longest first (seg_rank)
+constexpr int kRankMaxSeqs = 1024;
+hipError_t launch_plan_varlen(const Geometry &g, int32_t *seg_off, int32_t *seg_seq, int32_t *seg_rank,
                               hipStream_t st);
 
 }  // namespace finch

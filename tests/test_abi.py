@@ -134,14 +134,14 @@ def test_workspaces_start_with_the_control_records(lib):
     H = 32, 16 segments) needs 15 x 32 aggregates of 16,640 bytes and 16 x 32
     start states of 16,384 bytes behind them, each array 256-byte aligned; a
     packed call that is not split still keeps the records ahead of its
-    segment tables."""
+    segment tables (offsets, owners, longest-first ranks)."""
     ctl = 262144
     assert re.search(r"#define WKV_WORKSPACE_CONTROL_BYTES %d\b" % ctl, open(HEADER).read())
     align = lambda x: -(-x // 256) * 256
     assert lib.wkv_prefill_workspace_bytes(1, 4096, 32, 64, BF16) == (
         ctl + align(15 * 32 * 16640) + align(16 * 32 * 16384))
     cu = np.array([0, 100, 200], dtype=np.int32)       # two short sequences: no split
-    assert lib.wkv_prefill_varlen_workspace_bytes(cu.ctypes.data, 2, 4, 64, BF16) == ctl + 256 + 256
+    assert lib.wkv_prefill_varlen_workspace_bytes(cu.ctypes.data, 2, 4, 64, BF16) == ctl + 3 * 256
 
 
 def test_split_launch_switch(lib):
