@@ -77,7 +77,8 @@ def workload_name(cfg_name, decay, variant):
 # chunked scan the host plan that sizes its segments
 KERNEL_SOURCES = {
     "wkv_call": ("linear_attention_rnn_finch_amd/csrc/wkv_chunk.hip",
-                 "linear_attention_rnn_finch_amd/csrc/wkv_api.cpp"),
+                 "linear_attention_rnn_finch_amd/csrc/wkv_api.cpp",
+                 "linear_attention_rnn_finch_amd/csrc/wkv_plan.hip"),
     "wkv_decode": ("linear_attention_rnn_finch_amd/csrc/wkv_decode.hip",),
     "epilogue": ("linear_attention_rnn_finch_amd/csrc/wkv_epilogue.hip",),
 }

@@ -82,10 +82,13 @@ __global__ __launch_bounds__(kPlanThreads) void wkv_plan_varlen_kernel(Geometry 
     }
     if (!rank) return;
 
-    // bitonic sort of the keys, ascending (unused slots hold the largest key)
-    for (int k = 2; k <= kRankMaxSeqs; k <<= 1)
+    // bitonic sort of the keys, ascending, over the smallest power of two
+    // that holds them (unused slots hold the largest key)
+    int width = 2;
+    while (width < g.n_seq) width <<= 1;
+    for (int k = 2; k <= width; k <<= 1)
         for (int j = k >> 1; j > 0; j >>= 1) {
-            for (int i = tid; i < kRankMaxSeqs; i += kPlanThreads) {
+            for (int i = tid; i < width; i += kPlanThreads) {
                 const int l = i ^ j;
                 if (l > i) {
                     const uint64_t a = keys[i], b = keys[l];
