@@ -64,6 +64,25 @@ int64_t choose_segment(int64_t work, int64_t max_len, bool bf16) {
     return std::min(seg, whole);
 }
 
+// Runs per segment for the state pass of a three-launch split: as many as
+// bring its work items up to about three per compute unit (the state kernel's
+// occupancy), with runs of at least four chunks.  Packed calls with a few long
+// sequences otherwise leave most of the device idle in the state pass (16
+// ragged sequences, 192 items of 333 chunks: 690 us at 2.3 TB/s).
+constexpr int64_t kStateTargetItems = 768;
+constexpr int64_t kMinRun = 4 * kChunk;
+void choose_runs(Geometry &g) {
+    g.runs = 1;
+    g.run_len = g.seg_len;
+    const int64_t items = (int64_t)(g.n_seg - g.n_seq) * g.H;
+    if (items <= 0) return;
+    int64_t r = std::min<int64_t>(kStateTargetItems / items, g.seg_len / kMinRun);
+    if (r <= 1) return;
+    const int64_t len = round_up((g.seg_len + r - 1) / r, kChunk);
+    g.run_len = (int)len;
+    g.runs = (int)((g.seg_len + len - 1) / len);
+}
+
 struct Plan {
     Geometry g{};
     int64_t max_len = 0;             // longest sequence of the call
@@ -83,8 +102,9 @@ void layout_workspace(Plan &p, bool varlen) {
     if (p.split || varlen) off = WKV_WORKSPACE_CONTROL_BYTES;
     if (p.split) {
         p.off_seg_state = off;
-        // aggregates only for segments that are not the last of their sequence
-        const size_t aggs = (size_t)(p.g.n_seg - p.g.n_seq) * p.g.H;
+        // aggregates only for segments that are not the last of their
+        // sequence, one per state run
+        const size_t aggs = (size_t)(p.g.n_seg - p.g.n_seq) * p.g.runs * p.g.H;
         off = align256(off + aggs * kSegStateFloats * sizeof(float));
         p.off_seg_start = off;
         off = align256(off + items * kSegStartFloats * sizeof(float));
@@ -133,6 +153,7 @@ wkv_status_t plan_fixed(int B, int T, int H, int D, wkv_dtype_t dt, Plan &p) {
         p.g.whole_seqs = 1;
         p.split = false;
     }
+    choose_runs(p.g);
     layout_workspace(p, false);
     return WKV_OK;
 }
@@ -170,6 +191,7 @@ wkv_status_t plan_varlen(const int32_t *cu_host, int N, int H, int D, wkv_dtype_
     p.g.whole_seqs = 0;
     p.max_len = max_len;
     p.split = split;
+    choose_runs(p.g);
     layout_workspace(p, true);
     return WKV_OK;
 }
@@ -187,6 +209,8 @@ wkv_status_t check_grid(const Plan &p) {
     }
     if (items * 256 > kMaxWorkItems)
         return fail(WKV_EUNSUPPORTED, "%lld work items exceed one launch", (long long)items);
+    if (p.split && items * p.g.runs * 256 > kMaxWorkItems)                // state pass: one per run
+        return fail(WKV_EUNSUPPORTED, "%lld state runs exceed one launch", (long long)(items * p.g.runs));
     if (p.g.whole_seqs && slices * 512 > kMaxWorkItems)          // 512 threads per (sequence, head)
         return fail(WKV_EUNSUPPORTED, "%lld (sequence, head) pairs exceed one launch", (long long)slices);
     if (p.split && slices * kScanGroupThreads > kMaxWorkItems)
@@ -327,7 +351,11 @@ wkv_status_t run(const Plan &p, const Tensors &t, const Variant &var, void *ws, 
     if (p.split) {
         w.seg_state = reinterpret_cast<float *>(base + p.off_seg_state);
         w.seg_start = reinterpret_cast<float *>(base + p.off_seg_start);
-        if (fused) w.ctl = reinterpret_cast<SplitCtl *>(base);
+        if (fused) {
+            w.ctl = reinterpret_cast<SplitCtl *>(base);
+            g.runs = 1;                                // its state role covers whole segments
+            g.run_len = g.seg_len;
+        }
     }
     if ((e = launch_chunked(g, t, w, p.split, var, st, tm)) != hipSuccess) return fail_hip(e, "scan launch");
     return WKV_OK;

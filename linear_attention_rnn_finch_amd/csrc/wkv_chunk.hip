@@ -1002,27 +1002,34 @@ __device__ __forceinline__ void store_public_state(float *dst, const float (&S)[
             dst[(16 * ib + 4 * grp + e) * kHeadDim + 16 * wave + i16] = S[ib][e];
 }
 
-// State pass: the zero-start aggregate of every segment but the last of its
-// sequence: B (D*D, [key][value]) followed by the segment's total log2-decay
-// per key channel (D), stored at index (s - n) * H + h for global segment s of
-// sequence n.  Shorter items (segments split into two or four runs, four
-// workgroups per compute unit) were measured slower.
+// State pass: the zero-start aggregate of every run of every segment but the
+// last of its sequence: B (D*D, [key][value]) followed by the run's total
+// log2-decay per key channel (D), stored at index ((s - n) * runs + r) * H + h
+// for run r of global segment s of sequence n.  A segment is cut into several
+// runs only when its items alone would leave most of the device idle (the
+// planner's choice); where the items already fill it (four per compute unit
+// at the 1.5B-class layer) shorter runs were measured slower.
 template <bool LOGD, bool C2>
 __global__ __launch_bounds__(256, 3) void wkv_state_kernel(Geometry g, Tensors t, Workspace ws) {
     __shared__ SmemState sm;
     const int item = blockIdx.x;
     const int h = item % g.H;
-    const int seg = item / g.H;
+    const int q = item / g.H;
+    const int seg = q / g.runs, r = q - seg * g.runs;
     const ItemRange it = decode_segment(g, seg);
     if (!it.valid || it.p == it.P - 1) return;           // the last segment's aggregate is unused
     if (ws.seg_state == nullptr) return;                 // a split the host did not plan
+    // run r of the segment, clamped into it (integer clamps, see state_run)
+    const int64_t a = it.t0 + (int64_t)r * g.run_len;
+    const int64_t r0 = a < it.t1 ? a : it.t1;
+    const int64_t r1 = it.t1 - r0 > g.run_len ? r0 + g.run_len : it.t1;
     float S[4][4], lam[4] = {0.f, 0.f, 0.f, 0.f};
     #pragma unroll
     for (int ib = 0; ib < 4; ++ib)
         #pragma unroll
         for (int e = 0; e < 4; ++e) S[ib][e] = 0.f;
-    state_run<LOGD, C2>(sm, t, it.t0, it.t1, h, g.H, S, lam);
-    float *dst = ws.seg_state + ((size_t)(seg - it.n) * g.H + h) * kSegStateFloats;
+    state_run<LOGD, C2>(sm, t, r0, r1, h, g.H, S, lam);
+    float *dst = ws.seg_state + (((size_t)(seg - it.n) * g.runs + r) * g.H + h) * kSegStateFloats;
     store_public_state(dst, S);
     const int tid = threadIdx.x;
     if ((tid & 15) == 15) {
@@ -1032,12 +1039,13 @@ __global__ __launch_bounds__(256, 3) void wkv_state_kernel(Geometry g, Tensors t
     }
 }
 
-// Combine of segment aggregates: the state entering segment p of a sequence is
-//   S_{p+1} = diag(2^{Lam_p}) S_p + B_p,   S_0 = state_in (or zeros),
+// Combine of run aggregates: over the runs j of a sequence in order,
+//   S <- diag(2^{Lam_j}) S + B_j,   from S = state_in (or zeros),
+// and S before the first run of segment p is the state entering segment p;
 // a first-order recurrence per state entry.  Entries are independent: each
 // thread chains four neighbouring entries of one row (16-byte accesses), the
 // 4096 entries of a (sequence, head) spread over 16 one-wave workgroups,
-// and the loads of a batch of segments are issued before the chain.
+// and the loads of a batch of runs are issued before the chain.
 constexpr int kScanSlices = 16;
 constexpr int kScanThreads = 64;      // 16 workgroups x 64 threads x 4 entries = 4096
 constexpr int kScanBatch = 16;
@@ -1059,34 +1067,39 @@ __global__ __launch_bounds__(kScanThreads) void wkv_segment_scan_kernel(Geometry
     if (P <= 1) return;
     const int idx = ((blockIdx.x % kScanSlices) * kScanThreads + threadIdx.x) * 4;   // entries [i][j..j+3]
     const int row = idx >> 6;
+    const int R = g.runs;
+    const int steps = (P - 1) * R;                        // runs before the last segment
+    const size_t agg0 = (size_t)(first - n) * R;          // first run of the sequence
     f32x4 S = {0.f, 0.f, 0.f, 0.f};
     if (t.state_in)
         S = *reinterpret_cast<const f32x4 *>(t.state_in + ((size_t)n * g.H + h) * (kHeadDim * kHeadDim) + idx);
-    for (int p0 = 0; p0 < P; p0 += kScanBatch) {
+    for (int j0 = 0; j0 < steps; j0 += kScanBatch) {
         f32x4 b[kScanBatch];
         float lam[kScanBatch];
         #pragma unroll
         for (int q = 0; q < kScanBatch; ++q) {
             b[q] = f32x4{0.f, 0.f, 0.f, 0.f};
             lam[q] = 0.f;
-            if (p0 + q < P - 1) {
-                const float *agg = ws.seg_state + ((size_t)(first - n + p0 + q) * g.H + h) * kSegStateFloats;
+            if (j0 + q < steps) {
+                const float *agg = ws.seg_state + ((agg0 + j0 + q) * g.H + h) * kSegStateFloats;
                 b[q] = *reinterpret_cast<const f32x4 *>(agg + idx);
                 lam[q] = agg[kHeadDim * kHeadDim + row];
             }
         }
         #pragma unroll
         for (int q = 0; q < kScanBatch; ++q) {
-            if (p0 + q < P) {
-                *reinterpret_cast<f32x4 *>(ws.seg_start + ((size_t)(first + p0 + q) * g.H + h) * kSegStartFloats + idx) = S;
-                if (p0 + q < P - 1) {
-                    const float d = __builtin_amdgcn_exp2f(lam[q]);
-                    #pragma unroll
-                    for (int e = 0; e < 4; ++e) S[e] = d * S[e] + b[q][e];
-                }
+            const int j = j0 + q;
+            if (j < steps) {
+                if (j % R == 0)                          // the state entering segment j / R
+                    *reinterpret_cast<f32x4 *>(ws.seg_start + ((size_t)(first + j / R) * g.H + h) * kSegStartFloats +
+                                               idx) = S;
+                const float d = __builtin_amdgcn_exp2f(lam[q]);
+                #pragma unroll
+                for (int e = 0; e < 4; ++e) S[e] = d * S[e] + b[q][e];
             }
         }
     }
+    *reinterpret_cast<f32x4 *>(ws.seg_start + ((size_t)(first + P - 1) * g.H + h) * kSegStartFloats + idx) = S;
 }
 
 // The chunked scan: one workgroup per (segment, head), from the state that
@@ -1832,7 +1845,7 @@ hipError_t launch_chunked(const Geometry &g, const Tensors &t, const Workspace &
         void (*ks)(Geometry, Tensors, Workspace) =
             v.log_decay ? (v.c2 ? wkv_state_kernel<true, true> : wkv_state_kernel<true, false>)
                         : (v.c2 ? wkv_state_kernel<false, true> : wkv_state_kernel<false, false>);
-        hipLaunchKernelGGL(ks, grid, block, 0, st, g, t, ws);
+        hipLaunchKernelGGL(ks, dim3((unsigned)(items * g.runs)), block, 0, st, g, t, ws);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
         hipLaunchKernelGGL(wkv_segment_scan_kernel, dim3((unsigned)(g.n_seq * g.H * kScanSlices)), dim3(kScanThreads),

@@ -33,6 +33,12 @@ struct Geometry {
     // fixed-length only: 1 when every (sequence, head) is one work item of
     // the producer/consumer kernel (no segments, no state pass), else 0
     int whole_seqs;
+    // state pass of the three-launch split: each segment that is not the last
+    // of its sequence is covered by `runs` runs of run_len tokens (a multiple
+    // of 64; the last run of a segment may be shorter), each a work item with
+    // its own aggregate, which the segment scan chains in order
+    int runs;
+    int run_len;
 };
 
 // One work item's token range and position inside its sequence.
@@ -144,10 +150,11 @@ static_assert(sizeof(SplitCtl) == 64, "one 64-byte record per (sequence, head)")
 // (sequence, head) pairs take the three-launch path
 constexpr int kCtlRecords = WKV_WORKSPACE_CONTROL_BYTES / (int)sizeof(SplitCtl);
 
-// Workspace views (fp32).  seg_state[(s - n) * H + h]: the zero-start end
-// state (D*D) of global segment s of sequence n, followed by its total
-// log2-decay per key channel (D); only segments that are not the last of their
-// sequence have one, and s - n numbers them.  seg_start[item]: the state
+// Workspace views (fp32).  seg_state[((s - n) * runs + r) * H + h]: the
+// zero-start end state (D*D) of run r of global segment s of sequence n,
+// followed by its total log2-decay per key channel (D); only segments that are
+// not the last of their sequence have them, and s - n numbers those segments
+// (runs = 1 in the one-launch kernel).  seg_start[item]: the state
 // entering the segment (D*D).  ctl: the control records (one-launch path only,
 // else null), record n * H + h.
 struct Workspace {

@@ -144,6 +144,20 @@ def test_workspaces_start_with_the_control_records(lib):
     assert lib.wkv_prefill_varlen_workspace_bytes(cu.ctypes.data, 2, 4, 64, BF16) == ctl + 3 * 256
 
 
+def test_state_pass_runs(lib):
+    """A three-launch split whose state items alone would leave the device
+    idle cuts each segment into runs, each with its own aggregate: 4 x 16384
+    tokens x 32 heads has segments of 4096 tokens, 3 x 128 = 384 state items,
+    so two runs of 2048 tokens (768 aggregates); the 1.5B-class layer (480
+    items) and 262,144 tokens x 64 heads (448) keep one run per segment."""
+    ctl, agg, start = 262144, 16640, 16384
+    align = lambda x: -(-x // 256) * 256
+    assert lib.wkv_prefill_workspace_bytes(4, 16384, 32, 64, BF16) == (
+        ctl + align(3 * 2 * 128 * agg) + align(4 * 4 * 32 * start))
+    assert lib.wkv_prefill_workspace_bytes(1, 262144, 64, 64, BF16) == (
+        ctl + align(7 * 64 * agg) + align(8 * 64 * start))
+
+
 def test_split_launch_switch(lib):
     lib.wkv_set_split_launches.restype = ctypes.c_int
     lib.wkv_set_split_launches.argtypes = [ctypes.c_int]

@@ -23,14 +23,20 @@ def _up(x, m):
 def _plan(lengths, H):
     """Segment length, segments per sequence and the workspace offset of the
     rank table, as the library's host plan lays them out (split packed
-    call: control records, aggregates, start states, segment offsets,
+    call: control records, run aggregates, start states, segment offsets,
     owners, ranks; each array 256-byte aligned)."""
     tokens, max_len = sum(lengths), max(lengths)
     seg = min(max(_up(max(-(-tokens * H // 512), 1), 64), 256), _up(max(max_len, 1), 64))
     P = [1 if L == 0 else -(-L // seg) for L in lengths]
     n_seg, N = sum(P), len(lengths)
+    # state runs per segment: enough for about 768 state items, at least 4 chunks each
+    runs, items = 1, (n_seg - N) * H
+    r = min(768 // items, seg // 256) if items else 1
+    if r > 1:
+        run_len = _up(-(-seg // r), 64)
+        runs = -(-seg // run_len)
     off = 262144
-    off += _up((n_seg - N) * H * (64 * 64 + 64) * 4, 256)
+    off += _up((n_seg - N) * runs * H * (64 * 64 + 64) * 4, 256)
     off += _up(n_seg * H * 64 * 64 * 4, 256)
     off += _up((N + 1) * 4, 256)
     off += _up(n_seg * 4, 256)
