@@ -136,11 +136,15 @@ def _segment(lengths, H):
 
 def whole_sequence_plan(lengths, H, packed):
     """Whether the library runs this bf16 call as whole sequences on its
-    producer/consumer kernel: fixed length, longer than 16 tokens, split by
-    the segment plan, and at least 256 (sequence, head) pairs."""
-    if packed or not lengths or max(lengths) <= 16:
+    producer/consumer kernel: longer than 16 tokens, split by the segment
+    plan, and at least 256 (sequence, head) pairs; a packed call also needs
+    its longest sequence to be at most twice the mean work per CU (256)."""
+    if not lengths or max(lengths) <= 16:
         return False
-    return -(-max(lengths) // _segment(lengths, H)) > 1 and len(lengths) * H >= 256
+    split = -(-max(lengths) // _segment(lengths, H)) > 1
+    if not split or len(lengths) * H < 256:
+        return False
+    return not packed or max(lengths) * 256 <= 2 * sum(lengths) * H
 
 
 def one_launch_plan(lengths, H, packed, capacity):

@@ -47,6 +47,7 @@ constexpr int64_t kTargetItems = 512;
 // the 4-wave kernel with its state pass is as fast or faster, and from 512
 // pairs on it needs no segments.
 constexpr int64_t kWholeSeqItems = 256;
+constexpr int64_t kWholeSeqSlots = 256;     // producer/consumer workgroups resident at once
 // the kernels address one 64-token chunk with 32-bit byte offsets:
 // 64 rows x H heads x 256 B (fp32 o) must stay below 2^31
 constexpr int kMaxHeads = 65536;
@@ -152,6 +153,9 @@ wkv_status_t plan_fixed(int B, int T, int H, int D, wkv_dtype_t dt, Plan &p) {
         // CU: each runs a whole sequence, with no state pass and no scan
         p.g.whole_seqs = 1;
         p.split = false;
+        p.g.seg_len = (int)round_up(T, kChunk);
+        p.g.n_seg = B;
+        p.g.segs_per_seq = 1;
     }
     choose_runs(p.g);
     layout_workspace(p, false);
@@ -191,6 +195,16 @@ wkv_status_t plan_varlen(const int32_t *cu_host, int N, int H, int D, wkv_dtype_
     p.g.whole_seqs = 0;
     p.max_len = max_len;
     p.split = split;
+    if (p.bf16 && max_len > kDecodeMaxT && split && (int64_t)N * H >= kWholeSeqItems &&
+        max_len * kWholeSeqSlots <= 2 * tokens * H) {
+        // whole sequences on the producer/consumer kernel (one per CU, longest
+        // first), as for fixed-length batches, when no sequence is longer
+        // than twice the mean work per CU: no state pass and no scan
+        p.g.whole_seqs = 1;
+        p.split = false;
+        p.g.seg_len = (int)round_up(max_len, kChunk);
+        p.g.n_seg = N;
+    }
     choose_runs(p.g);
     layout_workspace(p, true);
     return WKV_OK;
@@ -329,8 +343,9 @@ wkv_status_t run(const Plan &p, const Tensors &t, const Variant &var, void *ws, 
         // longest first when the chunked scan has more work items than the
         // device holds at once (the short ones then fill in at the end)
         int32_t *seg_rank = nullptr;
+        const int64_t resident = g.whole_seqs ? kWholeSeqSlots : kTargetItems;
         if (p.bf16 && !fused && p.max_len > kDecodeMaxT && g.n_seq <= kRankMaxSeqs &&
-            (int64_t)g.n_seg * g.H > kTargetItems)
+            (int64_t)g.n_seg * g.H > resident)
             seg_rank = reinterpret_cast<int32_t *>(base + p.off_seg_rank);
         if ((e = launch_plan_varlen(g, seg_off, seg_seq, seg_rank, st)) != hipSuccess)
             return fail_hip(e, "planner launch");

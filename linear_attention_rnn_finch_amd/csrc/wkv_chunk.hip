@@ -1778,19 +1778,22 @@ __device__ __forceinline__ void pc_item(SmemPC<C2> &sm, const Tensors &t, int64_
     }
 }
 
-// Fixed-length batches whose (sequence, head) pairs fill the GPU: work item
-// n * H + h is the whole sequence n of head h, from state_in (no segments, no
-// state pass).
+// Batches whose (sequence, head) pairs fill the GPU: one workgroup per
+// (sequence, head), the whole sequence from state_in (no segments, no state
+// pass).  The plan has one segment per sequence; a packed call's sequences
+// are taken longest first when the rank table is there.  Any length works,
+// zero included (both roles then pass one barrier and the state is copied
+// through).
 template <bool LOGD, bool C2>
 __global__ __launch_bounds__(512, 1) void wkv_chunk_pc_kernel(Geometry g, Tensors t, Workspace) {
     __shared__ SmemPC<C2> sm;
-    const int item = blockIdx.x;
-    const int h = item % g.H;
-    const int n = item / g.H;
-    if (g.uniform_T < 0 || n >= g.n_seq) return;
-    const int64_t t0 = (int64_t)n * g.uniform_T;
-    const size_t slot = ((size_t)n * g.H + h) * (kHeadDim * kHeadDim);
-    pc_item<LOGD, C2>(sm, t, t0, t0 + g.uniform_T, h, g.H, t.state_in ? t.state_in + slot : nullptr,
+    const int h = blockIdx.x % g.H;
+    const int rank = blockIdx.x / g.H;
+    const int seg = g.seg_rank ? g.seg_rank[rank] : rank;
+    const ItemRange it = decode_segment(g, seg);
+    if (!it.valid || it.P != 1) return;                  // whole sequences only
+    const size_t slot = ((size_t)it.n * g.H + h) * (kHeadDim * kHeadDim);
+    pc_item<LOGD, C2>(sm, t, it.t0, it.t1, h, g.H, t.state_in ? t.state_in + slot : nullptr,
                       t.state_out ? t.state_out + slot : nullptr);
 }
 

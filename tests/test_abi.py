@@ -168,11 +168,11 @@ def test_split_launch_switch(lib):
 
 
 def test_whole_sequence_plans_need_no_workspace(lib):
-    """The planner's choice, seen through the workspace query: a fixed-length
-    bf16 call that would be split runs whole sequences (no scratch) once it
-    has at least 256 (sequence, head) pairs; below that, or in fp32 (its own
-    kernel, never split), nothing changes; from 512 pairs on no split is
-    needed either."""
+    """The planner's choice, seen through the workspace query: a bf16 call
+    that would be split runs whole sequences (no scratch beyond a packed
+    call's planner tables) once it has at least 256 (sequence, head) pairs;
+    below that, or in fp32 (its own kernel, never split), nothing changes;
+    from 512 pairs on a fixed-length call needs no split either."""
     ws = lambda B, T, H, dt=BF16: lib.wkv_prefill_workspace_bytes(B, T, H, 64, dt)
     assert ws(8, 4096, 32) == 0                       # 256 pairs: whole sequences
     assert ws(2, 1000, 128) == 0 and ws(12, 4096, 32) == 0
@@ -181,9 +181,14 @@ def test_whole_sequence_plans_need_no_workspace(lib):
     assert ws(16, 4096, 32) == 0                      # 512 pairs: no split needed
     assert ws(8, 16, 32) == 0                         # recurrent steps
     assert ws(8, 4096, 32, F32) == 0                  # fp32: token-serial kernel
-    # varlen calls keep the segmented kernel: a split ragged call needs scratch
-    cu = np.array([0] + [4096 * (i + 1) for i in range(8)], dtype=np.int32)
-    assert lib.wkv_prefill_varlen_workspace_bytes(cu.ctypes.data, 8, 32, 64, BF16) > 0
+    # packed calls: whole sequences too (only the control records and the
+    # planner's three tables) when no sequence is longer than twice the mean
+    # work per CU; a batch dominated by one long sequence keeps its segments
+    # (aggregates and start states)
+    vws = lambda lens, H: lib.wkv_prefill_varlen_workspace_bytes(
+        np.concatenate([[0], np.cumsum(lens)]).astype(np.int32).ctypes.data, len(lens), H, 64, BF16)
+    assert vws([4096] * 8, 32) == 262144 + 3 * 256
+    assert vws([4096] * 7 + [200000], 32) > 262144 + 3 * 256 + 16640
 
 
 def varlen(lib, cu, H=4, dt=BF16, ws_bytes=None, cu_dev=A * 20, **ptrs):

@@ -43,18 +43,21 @@ def _plan(lengths, H):
     return seg, P, off
 
 
-def test_packed_segments_longest_first():
-    lengths = [3000, 100, 2500, 40, 900, 1800, 7, 1200]
-    H = 64
-    seg, P, rank_off = _plan(lengths, H)
-    assert seg > 1024 and sum(P) * H > 512      # three launches, more items than slots
+def _check_order(lengths, H, whole):
+    import linear_attention_rnn_finch_amd as fw
     wl = make_workload(4, lengths=lengths, H=H)
     g = to_gpu(wl)
-    import linear_attention_rnn_finch_amd as fw
     need = fw.varlen_workspace_bytes(g["cu_host"], H, 64)
+    if whole:                                   # one segment per sequence, no aggregates
+        seg, P = _up(max(lengths), 64), [1] * len(lengths)
+        rank_off = 262144 + _up((len(lengths) + 1) * 4, 256) + _up(len(lengths) * 4, 256)
+    else:
+        seg, P, rank_off = _plan(lengths, H)
+        assert seg > 1024                       # three launches
+    assert sum(P) * H > (256 if whole else 512)  # more items than the device holds at once
     assert need >= rank_off + 4 * sum(P)
     ws = fw.new_workspace(need, "cuda")
-    log("case longest-first lengths=%s H=%d seg=%d" % (lengths, H, seg))
+    log("case longest-first lengths=%s H=%d whole=%s" % (lengths, H, whole))
     o, s = run_gpu(wl, g, workspace=ws)
     torch.cuda.synchronize()
     table = ws[rank_off:rank_off + 4 * sum(P)].view(torch.int32).cpu().numpy()
@@ -67,3 +70,15 @@ def test_packed_segments_longest_first():
     o_ref, s_ref = run_oracle(wl)
     eo, es = errors(wl, o, s, o_ref, s_ref)
     assert eo <= 2e-3 and es <= 2e-3, (eo, es)
+
+
+def test_split_segments_longest_first():
+    """192 (sequence, head) pairs: split into segments of 3968 tokens, 672
+    items for the 4-wave kernel."""
+    _check_order([30000, 500, 20000, 100, 9000, 4000], 32, whole=False)
+
+
+def test_whole_sequences_longest_first():
+    """512 pairs, no sequence longer than twice the mean work per CU: whole
+    sequences on the producer/consumer kernel, longest first."""
+    _check_order([3000, 100, 2500, 40, 900, 1800, 7, 1200], 64, whole=True)

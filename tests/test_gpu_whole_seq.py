@@ -1,9 +1,11 @@
-"""The producer/consumer kernel that runs whole sequences: fixed-length bf16
-calls with at least 256 (sequence, head) pairs whose sequences the 4-wave
-kernel would split into segments.  Every form against the fp64 oracle (all
-heads), with and without states, a partial last chunk, bf16 o, stiff decays,
-carried chains and graph replays; the 8 x 4096 x 32 training batch runs
-here too (tests/test_gpu_parity.py)."""
+"""The producer/consumer kernel that runs whole sequences: bf16 calls with at
+least 256 (sequence, head) pairs whose sequences the 4-wave kernel would
+split into segments (packed calls also need no sequence longer than twice
+the mean work per CU).  Every form against the fp64 oracle (all heads), with
+and without states, a partial last chunk, bf16 o, stiff decays, carried
+chains, graph replays and packed batches with empty and short sequences; the
+8 x 4096 x 32 training batch and the 16 ragged sequences run it too
+(tests/test_gpu_parity.py)."""
 from dataclasses import replace
 
 import numpy as np
@@ -164,3 +166,17 @@ def test_graph_replays_match_eager():
         graph.replay()
         torch.cuda.synchronize()
         assert torch.equal(o, o_ref) and torch.equal(st, s_ref), rep
+
+
+@pytest.mark.parametrize("decay,variant", FORMS, ids=IDS)
+def test_packed_whole_sequences(decay, variant):
+    """A packed batch of 8 sequences x 64 heads (512 pairs) with an initial
+    state, lengths 0 to 1000 (empty, shorter than a step call, exactly one
+    chunk, partial chunks): whole sequences on the producer/consumer kernel,
+    longest first, no workspace beyond the planner's tables."""
+    import linear_attention_rnn_finch_amd as fw
+    lengths = [1000, 0, 5, 700, 64, 300, 16, 900]
+    H = 64
+    cu = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
+    assert fw.varlen_workspace_bytes(torch.from_numpy(cu), H, 64) == 262144 + 3 * 256
+    _check(make_workload(4, lengths=lengths, H=H, decay=decay, variant=variant))
