@@ -147,12 +147,29 @@ def whole_sequence_plan(lengths, H, packed):
     return not packed or max(lengths) * 256 <= 2 * sum(lengths) * H
 
 
+def pc_split_segment(lengths, H, packed):
+    """Segment length when the library runs a split fixed-length bf16 call
+    with fewer than 256 (sequence, head) pairs on its producer/consumer
+    kernel (about 256 segments, at least 2 per sequence, each at least 2048
+    tokens), else None."""
+    if packed or not lengths or max(lengths) <= 16 or whole_sequence_plan(lengths, H, packed):
+        return None
+    T, B = max(lengths), len(lengths)
+    if -(-T // _segment(lengths, H)) <= 1:
+        return None                                     # not split
+    pcs = max(2, 256 // (B * H))
+    seg = -(-(-(-T // pcs)) // 64) * 64
+    return seg if seg >= 2048 else None
+
+
 def one_launch_plan(lengths, H, packed, capacity):
     """Whether the library runs this split bf16 call as one launch of its
     split kernel: segments of at most 1024 tokens, at most 4096 (sequence,
     head) pairs, and every state workgroup resident at once (`capacity`
     workgroups: compute units x 2)."""
     if not lengths or max(lengths) <= 16 or whole_sequence_plan(lengths, H, packed):
+        return False
+    if pc_split_segment(lengths, H, packed):
         return False
     seg = _segment(lengths, H)
     n_seg = sum(1 if L == 0 else -(-L // seg) for L in lengths)
@@ -168,10 +185,11 @@ def chunk_counts(lengths, H, packed=False):
     multiple of 64 tokens and at least 256, no longer than the longest sequence
     rounded up to 64.  A fixed-length call that this plan would split but that
     has at least 256 (sequence, head) pairs runs whole sequences instead (no
-    state pass)."""
+    state pass); one with fewer pairs whose producer/consumer segments would
+    be at least 2048 tokens uses those segments."""
     if whole_sequence_plan(lengths, H, packed):
         return sum(-(-L // 64) for L in lengths) * H, 0, 0
-    seg = _segment(lengths, H)
+    seg = pc_split_segment(lengths, H, packed) or _segment(lengths, H)
     main = state = inner = 0
     for L in lengths:
         P = 1 if L == 0 else -(-L // seg)
@@ -444,6 +462,7 @@ def main():
         lens = [int(x) for x in np.diff(wl.cu_seqlens)] if wl.packed else [cfg.T] * cfg.B
         capacity = 2 * torch.cuda.get_device_properties(0).multi_processor_count
         kernel_name = ("wkv_chunk_pc_kernel" if whole_sequence_plan(lens, cfg.H, wl.packed)
+                       or pc_split_segment(lens, cfg.H, wl.packed)
                        else "wkv_split_kernel" if args.split_launches == 1
                        and one_launch_plan(lens, cfg.H, wl.packed, capacity)
                        else "wkv_chunk_kernel")

@@ -39,15 +39,22 @@ wkv_status_t fail_hip(hipError_t e, const char *what) {
 // Work items the planner aims for: two resident 4-wave workgroups on each of
 // the 256 compute units of an MI355X.
 constexpr int64_t kTargetItems = 512;
-// A fixed-length bf16 call that the 4-wave kernel would split into segments
-// runs whole sequences on the producer/consumer kernel (one 512-thread
-// workgroup per compute unit) instead once it has this many (sequence, head)
-// pairs.  Measured at T = 4096, H = 32 per call: 262 -> 200 us at B = 8,
-// 481 -> 344 us at B = 12; at B = 4 to 7 (which would still need segments)
-// the 4-wave kernel with its state pass is as fast or faster, and from 512
-// pairs on it needs no segments.
+// A bf16 call that the 4-wave kernel would split into segments runs whole
+// sequences on the producer/consumer kernel (one 512-thread workgroup per
+// compute unit) instead once it has this many (sequence, head) pairs.
+// Measured at T = 4096, H = 32 per call: 262 -> 200 us at B = 8, 481 -> 344 us
+// at B = 12; at B = 4 to 7 (which would still need segments) the 4-wave kernel
+// with its state pass is as fast or faster, and from 512 pairs on it needs no
+// segments.  A packed call also needs no sequence longer than twice the mean
+// work per resident workgroup (16 ragged sequences, H = 32: 2314 -> 1862 us).
 constexpr int64_t kWholeSeqItems = 256;
 constexpr int64_t kWholeSeqSlots = 256;     // producer/consumer workgroups resident at once
+// A fixed-length call with fewer pairs whose sequences are split runs its
+// chunked scan on the producer/consumer kernel, with about kWholeSeqSlots
+// segments, when those are at least this long (its pipeline needs many
+// chunks per item: with 512-token segments at T = 4096, H = 32 it lost to
+// the 4-wave kernel, 50.1 against 47.1 us).
+constexpr int64_t kPcSplitSegment = 2048;
 // the kernels address one 64-token chunk with 32-bit byte offsets:
 // 64 rows x H heads x 256 B (fp32 o) must stay below 2^31
 constexpr int kMaxHeads = 65536;
@@ -146,6 +153,7 @@ wkv_status_t plan_fixed(int B, int T, int H, int D, wkv_dtype_t dt, Plan &p) {
     p.g.uniform_T = T;
     p.g.segs_per_seq = (int)per;
     p.g.whole_seqs = 0;
+    p.g.pc_split = 0;
     p.max_len = T;
     p.split = per > 1;
     if (p.bf16 && T > kDecodeMaxT && per > 1 && (int64_t)B * H >= kWholeSeqItems) {
@@ -156,6 +164,18 @@ wkv_status_t plan_fixed(int B, int T, int H, int D, wkv_dtype_t dt, Plan &p) {
         p.g.seg_len = (int)round_up(T, kChunk);
         p.g.n_seg = B;
         p.g.segs_per_seq = 1;
+    } else if (p.bf16 && T > kDecodeMaxT && per > 1) {
+        // fewer pairs: long segments, about one per CU, on the
+        // producer/consumer kernel, from the combined start states
+        const int64_t pcs = std::max<int64_t>(2, kWholeSeqSlots / ((int64_t)B * H));
+        const int64_t seg2 = round_up((T + pcs - 1) / pcs, kChunk);
+        if (seg2 >= kPcSplitSegment) {
+            const int64_t per2 = (T + seg2 - 1) / seg2;
+            p.g.pc_split = 1;
+            p.g.seg_len = (int)seg2;
+            p.g.n_seg = (int)(B * per2);
+            p.g.segs_per_seq = (int)per2;
+        }
     }
     choose_runs(p.g);
     layout_workspace(p, false);
@@ -193,6 +213,7 @@ wkv_status_t plan_varlen(const int32_t *cu_host, int N, int H, int D, wkv_dtype_
     p.g.uniform_T = -1;
     p.g.segs_per_seq = 0;
     p.g.whole_seqs = 0;
+    p.g.pc_split = 0;
     p.max_len = max_len;
     p.split = split;
     if (p.bf16 && max_len > kDecodeMaxT && split && (int64_t)N * H >= kWholeSeqItems &&
@@ -225,8 +246,8 @@ wkv_status_t check_grid(const Plan &p) {
         return fail(WKV_EUNSUPPORTED, "%lld work items exceed one launch", (long long)items);
     if (p.split && items * p.g.runs * 256 > kMaxWorkItems)                // state pass: one per run
         return fail(WKV_EUNSUPPORTED, "%lld state runs exceed one launch", (long long)(items * p.g.runs));
-    if (p.g.whole_seqs && slices * 512 > kMaxWorkItems)          // 512 threads per (sequence, head)
-        return fail(WKV_EUNSUPPORTED, "%lld (sequence, head) pairs exceed one launch", (long long)slices);
+    if ((p.g.whole_seqs || p.g.pc_split) && items * 512 > kMaxWorkItems)   // 512 threads per item
+        return fail(WKV_EUNSUPPORTED, "%lld work items exceed one launch", (long long)items);
     if (p.split && slices * kScanGroupThreads > kMaxWorkItems)
         return fail(WKV_EUNSUPPORTED, "%lld (sequence, head) pairs exceed the segment scan's launch",
                     (long long)slices);

@@ -1783,18 +1783,23 @@ __device__ __forceinline__ void pc_item(SmemPC<C2> &sm, const Tensors &t, int64_
 // pass).  The plan has one segment per sequence; a packed call's sequences
 // are taken longest first when the rank table is there.  Any length works,
 // zero included (both roles then pass one barrier and the state is copied
-// through).
+// through).  With a split plan (long segments, about one per CU) a segment
+// starts from the combined start state of the segment scan, and only the
+// last segment of a sequence writes state_out.
 template <bool LOGD, bool C2>
-__global__ __launch_bounds__(512, 1) void wkv_chunk_pc_kernel(Geometry g, Tensors t, Workspace) {
+__global__ __launch_bounds__(512, 1) void wkv_chunk_pc_kernel(Geometry g, Tensors t, Workspace ws) {
     __shared__ SmemPC<C2> sm;
     const int h = blockIdx.x % g.H;
     const int rank = blockIdx.x / g.H;
     const int seg = g.seg_rank ? g.seg_rank[rank] : rank;
     const ItemRange it = decode_segment(g, seg);
-    if (!it.valid || it.P != 1) return;                  // whole sequences only
+    if (!it.valid) return;
+    if (it.P > 1 && ws.seg_start == nullptr) return;     // a split the host did not plan
     const size_t slot = ((size_t)it.n * g.H + h) * (kHeadDim * kHeadDim);
-    pc_item<LOGD, C2>(sm, t, it.t0, it.t1, h, g.H, t.state_in ? t.state_in + slot : nullptr,
-                      t.state_out ? t.state_out + slot : nullptr);
+    const float *s_src = it.P > 1 ? ws.seg_start + ((size_t)seg * g.H + h) * kSegStartFloats
+                                  : (t.state_in ? t.state_in + slot : nullptr);
+    float *s_dst = t.state_out && it.p == it.P - 1 ? t.state_out + slot : nullptr;
+    pc_item<LOGD, C2>(sm, t, it.t0, it.t1, h, g.H, s_src, s_dst);
 }
 
 }  // namespace
@@ -1855,8 +1860,8 @@ hipError_t launch_chunked(const Geometry &g, const Tensors &t, const Workspace &
                            0, st, g, t, ws);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
-    if (g.whole_seqs) {                                // producer/consumer kernel, whole sequences
-        const dim3 pc_grid((unsigned)((int64_t)g.n_seq * g.H)), pc_block(512);
+    if (g.whole_seqs || g.pc_split) {                  // producer/consumer kernel
+        const dim3 pc_grid((unsigned)items), pc_block(512);
         void (*k)(Geometry, Tensors, Workspace) =
             v.log_decay ? (v.c2 ? wkv_chunk_pc_kernel<true, true> : wkv_chunk_pc_kernel<true, false>)
                         : (v.c2 ? wkv_chunk_pc_kernel<false, true> : wkv_chunk_pc_kernel<false, false>);

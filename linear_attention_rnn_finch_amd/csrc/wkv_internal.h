@@ -33,6 +33,9 @@ struct Geometry {
     // fixed-length only: 1 when every (sequence, head) is one work item of
     // the producer/consumer kernel (no segments, no state pass), else 0
     int whole_seqs;
+    // fixed-length only: 1 when the chunked scan of a split call runs on the
+    // producer/consumer kernel (one workgroup per CU and long segment), else 0
+    int pc_split;
     // state pass of the three-launch split: each segment that is not the last
     // of its sequence is covered by `runs` runs of run_len tokens (a multiple
     // of 64; the last run of a segment may be shorter), each a work item with

@@ -11,9 +11,12 @@
 namespace finch {
 namespace {
 
-// Largest scratch a fixed-length plan can need: a split plan has fewer than
-// 1024 (segment, head) work items (it splits only when B*H < 512 and aims at
-// about 512 items), each with 33,024 bytes of aggregate and start state.
+// Largest scratch a fixed-length plan can need: 256 KiB of control records,
+// then fewer than 1024 (segment, head) work items (a plan splits only when
+// B*H < 512 and aims at about 512 items, or about 256 on the
+// producer/consumer kernel), each with a 16 KiB start state, and at most
+// about 1024 state-pass aggregates of 16,640 bytes (segments, or runs of a
+// segment).
 constexpr size_t kScratchBytes = size_t(36) << 20;
 constexpr int kMaxDevices = 64;
 

@@ -145,17 +145,43 @@ def test_workspaces_start_with_the_control_records(lib):
 
 
 def test_state_pass_runs(lib):
-    """A three-launch split whose state items alone would leave the device
-    idle cuts each segment into runs, each with its own aggregate: 4 x 16384
-    tokens x 32 heads has segments of 4096 tokens, 3 x 128 = 384 state items,
-    so two runs of 2048 tokens (768 aggregates); the 1.5B-class layer (480
-    items) and 262,144 tokens x 64 heads (448) keep one run per segment."""
+    """A split whose state items alone would leave the device idle cuts each
+    segment's state pass into runs, each with its own aggregate.
+    4 x 2048 tokens x 32 heads: segments of 512 tokens, 3 x 128 = 384 state
+    items, so two runs of 256 tokens (768 aggregates).  With fewer than 256
+    (sequence, head) pairs and long enough sequences, the chunked scan runs on
+    the producer/consumer kernel over about 256 segments: 4 x 16384 x 32 has
+    two segments of 8192 tokens per sequence (128 state items in six runs of
+    1408 tokens), 262,144 tokens x 64 heads has four of 65,536 (192 state
+    items in four runs of 16,384).  The 1.5B-class layer (480 state items)
+    keeps one run per segment."""
     ctl, agg, start = 262144, 16640, 16384
     align = lambda x: -(-x // 256) * 256
-    assert lib.wkv_prefill_workspace_bytes(4, 16384, 32, 64, BF16) == (
+    assert lib.wkv_prefill_workspace_bytes(4, 2048, 32, 64, BF16) == (
         ctl + align(3 * 2 * 128 * agg) + align(4 * 4 * 32 * start))
+    assert lib.wkv_prefill_workspace_bytes(4, 16384, 32, 64, BF16) == (
+        ctl + align(1 * 6 * 128 * agg) + align(4 * 2 * 32 * start))
     assert lib.wkv_prefill_workspace_bytes(1, 262144, 64, 64, BF16) == (
-        ctl + align(7 * 64 * agg) + align(8 * 64 * start))
+        ctl + align(3 * 4 * 64 * agg) + align(4 * 64 * start))
+    assert lib.wkv_prefill_workspace_bytes(1, 4096, 32, 64, BF16) == (
+        ctl + align(15 * 32 * agg) + align(16 * 32 * start))
+
+
+def test_every_fixed_length_plan_fits_the_static_scratch(lib):
+    """wkv_prefill_noalloc runs any fixed-length plan out of its 36 MiB static
+    scratch: over a sweep of batch sizes, lengths and head counts (split
+    plans of the 4-wave kernel, with and without state runs, and of the
+    producer/consumer kernel) the workspace never needs more."""
+    f = lib.wkv_prefill_workspace_bytes
+    Ts = [17, 257, 300, 513, 1000, 1025, 2000, 2049, 4096, 5000, 8192, 9000, 16384,
+          65536, 100000, 262144, 1000000, 2000000]
+    worst = 0
+    for B in list(range(1, 33)) + [48, 64, 100, 127, 128, 255, 256, 511, 512]:
+        for H in [1, 2, 3, 5, 8, 13, 16, 24, 32, 48, 64, 100, 128, 255, 256, 511]:
+            for T in Ts:
+                if B * T < 2**31:
+                    worst = max(worst, f(B, T, H, 64, BF16))
+    assert 16 << 20 < worst <= 36 << 20, worst
 
 
 def test_split_launch_switch(lib):
