@@ -337,16 +337,26 @@ wkv_status_t check_pointers(const Plan &p, const Variant &var, const void *r, co
 // state pass, and the kernel boundaries they save are a small share.
 constexpr int64_t kOneLaunchSegment = 1024;
 
-wkv_status_t one_launch(const Plan &p, const Variant &var, bool *yes) {
-    *yes = false;
+// The relay form (each workgroup the state role and then the main role of its
+// item) needs every item resident at once; the two-role grid only the state
+// workgroups.
+enum class OneLaunch { kNone, kTwoRoles, kRelay };
+
+wkv_status_t one_launch(const Plan &p, const Variant &var, OneLaunch *form) {
+    *form = OneLaunch::kNone;
     if (!p.split || !p.bf16 || g_split_launches != 1) return WKV_OK;
     if (p.g.seg_len > kOneLaunchSegment) return WKV_OK;
     if ((int64_t)p.g.n_seq * p.g.H > kCtlRecords) return WKV_OK;
     const int64_t items = (int64_t)p.g.n_seg * p.g.H;
     if (2 * items * 256 > 0xFFFFFFFFll) return WKV_OK;
     int64_t capacity = 0;
-    if (hipError_t e = split_launch_capacity(var, &capacity)) return fail_hip(e, "occupancy query");
-    *yes = (int64_t)(p.g.n_seg - p.g.n_seq) * p.g.H <= capacity;
+    if (hipError_t e = split_launch_capacity(var, true, &capacity)) return fail_hip(e, "occupancy query");
+    if (items <= capacity) {
+        *form = OneLaunch::kRelay;
+        return WKV_OK;
+    }
+    if (hipError_t e = split_launch_capacity(var, false, &capacity)) return fail_hip(e, "occupancy query");
+    if ((int64_t)(p.g.n_seg - p.g.n_seq) * p.g.H <= capacity) *form = OneLaunch::kTwoRoles;
     return WKV_OK;
 }
 
@@ -354,8 +364,9 @@ wkv_status_t run(const Plan &p, const Tensors &t, const Variant &var, void *ws, 
     Geometry g = p.g;
     char *base = static_cast<char *>(ws);
     hipError_t e;
-    bool fused = false;
-    if (wkv_status_t s = one_launch(p, var, &fused)) return s;
+    OneLaunch form = OneLaunch::kNone;
+    if (wkv_status_t s = one_launch(p, var, &form)) return s;
+    const bool fused = form != OneLaunch::kNone;
     if (g.uniform_T < 0) {
         if (!g.cu) return fail(WKV_EINVAL, "packed launch without device offsets");
         int32_t *seg_off = reinterpret_cast<int32_t *>(base + p.off_seg_off);
@@ -391,6 +402,7 @@ wkv_status_t run(const Plan &p, const Tensors &t, const Variant &var, void *ws, 
             w.ctl = reinterpret_cast<SplitCtl *>(base);
             g.runs = 1;                                // its state role covers whole segments
             g.run_len = g.seg_len;
+            g.relay = form == OneLaunch::kRelay;
         }
     }
     if ((e = launch_chunked(g, t, w, p.split, var, st, tm)) != hipSuccess) return fail_hip(e, "scan launch");

@@ -839,15 +839,19 @@ struct SmemState {
     uint16_t kt_hi[kTileElems];                  // k~ = k 2^{Lam_63 - Lam_s}, bf16 hi/lo planes
     uint16_t kt_lo[kTileElems];
     uint16_t stage[2][kStageElems];              // raw k, w rows of the chunk
-    alignas(16) float row_dec[kHeadDim];         // decay of the whole chunk per key channel
 };
 static_assert(sizeof(SmemState) <= 53 * 1024, "three state workgroups per CU");
 
 // The state pass over one run of tokens (zero start): S ends as the run's
 // aggregate B = sum_s diag(P_end / P_s) k_s^T v_s and lam_seg (lanes with
-// i16 == 15, channels c0 .. c0+3) as its total log2-decay.  One chunk is
-// prefetched ahead (keeping two or three chunks of each item in flight was
-// measured slower).
+// i16 == 15, channels c0 .. c0+3) as its total log2-decay.  The sum does not
+// depend on the order of its terms, so the chunks are taken from the last to
+// the first: each chunk's k~ carries its whole decay to the run end (the
+// log2-decay of the later chunks, lam_after, plus its own to the chunk end),
+// the products accumulate into S with no rescaling, and the run's first
+// chunk is read last, so a chunked scan of the same tokens that follows on
+// the same XCD finds its first inputs in L2.  One chunk is prefetched ahead
+// (keeping two or three chunks of each item in flight was measured slower).
 template <bool LOGD, bool C2>
 __device__ __forceinline__ void state_run(SmemState &sm, const Tensors &t, int64_t t0, int64_t t1, int h, int H,
                                           float (&S)[4][4], float (&lam_seg)[4]) {
@@ -857,7 +861,6 @@ __device__ __forceinline__ void state_run(SmemState &sm, const Tensors &t, int64
     const int i16 = lane & 15;
     const int grp = lane >> 4;
     const LdsBases lb = make_bases(tid);
-    const int c0 = 16 * wave + 4 * grp;
     const int ld_row = tid >> 3;
     const int ld_col = (tid & 7) * 8;
     constexpr int kRowIn = kHeadDim * 2;
@@ -890,18 +893,20 @@ __device__ __forceinline__ void state_run(SmemState &sm, const Tensors &t, int64
     };
 
     const int n_chunks = (int)((t1 - t0 + kChunk - 1) / kChunk);
-    if (n_chunks > 0) issue(t0);
-    for (int c = 0; c < n_chunks; ++c) {
+    float lam_after[4] = {0.f, 0.f, 0.f, 0.f};  // log2-decay from the current chunk's end to the run end
+    if (n_chunks > 0) issue(t0 + (int64_t)(n_chunks - 1) * kChunk);
+    for (int i = 0; i < n_chunks; ++i) {
+        const int c = n_chunks - 1 - i;
         const int64_t tc = t0 + (int64_t)c * kChunk;
         const int nt = (int)min<int64_t>(kChunk, t1 - tc);
-        set_progress_priority(c, n_chunks);
+        set_progress_priority(i, n_chunks);
         #pragma unroll
         for (int m = 0; m < 2; ++m) {
             lds_write_b128(sm.v, lb.vw + 64 * 32 * m, Qv[m]);
             lds_write_b128(sm.stage[0], st_wr[m], Qk[m]);
             lds_write_b128(sm.stage[1], st_wr[m], Qw[m]);
         }
-        if (c + 1 < n_chunks) issue(tc + kChunk);
+        if (c > 0) issue(tc - kChunk);
         __syncthreads();
         u32x2 pk[4], pw[4];
         #pragma unroll
@@ -946,30 +951,25 @@ __device__ __forceinline__ void state_run(SmemState &sm, const Tensors &t, int64
             #pragma unroll
             for (int a = 0; a < 4; ++a) lam[a][q] += off;
         }
-        if (i16 == 15) {
-            #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                sm.row_dec[c0 + q] = __builtin_amdgcn_exp2f(total[q]);
-                lam_seg[q] += total[q];
-            }
-        }
         #pragma unroll
         for (int a = 0; a < 4; ++a) {
             float ks[4];
             #pragma unroll
-            for (int q = 0; q < 4; ++q) ks[q] = kk_[a][q] * __builtin_amdgcn_exp2f(-lam[a][q]);
+            for (int q = 0; q < 4; ++q) ks[q] = kk_[a][q] * __builtin_amdgcn_exp2f(lam_after[q] - lam[a][q]);
             u32x2 kh, kl;
             split4(ks[0], ks[1], ks[2], ks[3], kh, kl);
             lds_write_b64(sm.kt_hi, lb.pw_kt[a], kh);
             lds_write_b64(sm.kt_lo, lb.pw_kt[a], kl);
         }
+        #pragma unroll
+        for (int q = 0; q < 4; ++q) lam_after[q] += total[q];
         __syncthreads();
         bf16x8 vop[2];
         vop[0] = col_op(sm.v, lb.tr_v, 0);
         vop[1] = col_op(sm.v, lb.tr_v, 1);
         f32x4 pp[4];
         #pragma unroll
-        for (int ib = 0; ib < 4; ++ib) pp[ib] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int ib = 0; ib < 4; ++ib) pp[ib] = f32x4{S[ib][0], S[ib][1], S[ib][2], S[ib][3]};
         #pragma unroll
         for (int kk = 0; kk < 2; ++kk) {
             bf16x8 k_hi[4], k_lo[4];
@@ -984,12 +984,14 @@ __device__ __forceinline__ void state_run(SmemState &sm, const Tensors &t, int64
             for (int ib = 0; ib < 4; ++ib) pp[ib] = mfma(k_lo[ib], vop[kk], pp[ib]);
         }
         #pragma unroll
-        for (int ib = 0; ib < 4; ++ib) {
-            const f32x4 dec = *reinterpret_cast<const f32x4 *>(&sm.row_dec[16 * ib + 4 * grp]);
+        for (int ib = 0; ib < 4; ++ib)
             #pragma unroll
-            for (int e = 0; e < 4; ++e) S[ib][e] = dec[e] * S[ib][e] + pp[ib][e];
-        }
+            for (int e = 0; e < 4; ++e) S[ib][e] = pp[ib][e];
         __syncthreads();                       // planes and values read before the next staging
+    }
+    if (i16 == 15) {
+        #pragma unroll
+        for (int q = 0; q < 4; ++q) lam_seg[q] = lam_after[q];
     }
 }
 
@@ -1147,13 +1149,25 @@ __global__ __launch_bounds__(256, 2) void wkv_chunk_kernel(Geometry g, Tensors t
 // segment, from state_in (first segment) or from the start state, which it
 // waits for after issuing its first chunk's loads.
 //
+// Relay form (Relay = true): one workgroup per item takes the state role (if
+// its segment has one) and then the main role of the same item.  Its chunked
+// scan so needs no second dispatch, has its first chunk's loads in flight
+// while the chain finishes, and reads that chunk's k, v, w soon after the
+// state pass read them (it takes the run's chunks last to first), so they can
+// still be in L2.  The first segments' chunked scans wait for their own
+// state pass: starting them at once (with the last segment's workgroup taking
+// segment 0's state pass) was measured slower, since they then take bandwidth
+// from the state passes.  The host launches this form only when every item of
+// the grid fits on the device at once.
+//
 // Waits.  A state workgroup waits only for the other state workgroups of its
 // (sequence, head), and a main workgroup only for those.  Workgroups are
 // dispatched in index order, every state workgroup precedes every main
-// workgroup, and the host launches this form only when all state workgroups
-// fit on the device at once, so every workgroup waited for is resident or
-// finished.  Each wait is bounded (kWaitTicks) and marks the record's error
-// word if the bound expires, so no launch can hang.
+// workgroup, and the host launches the two-role form only when all state
+// workgroups fit on the device at once (the relay form only when all
+// workgroups do), so every workgroup waited for is resident or finished.
+// Each wait is bounded (kWaitTicks) and marks the record's error word if the
+// bound expires, so no launch can hang.
 //
 // Memory.  Everything handed between workgroups (aggregates, start states,
 // counters, flags) is written and read with agent-scope atomic accesses,
@@ -1239,11 +1253,11 @@ union SmemSplit {
     SmemState state;
 };
 
-template <bool LOGD, bool C2>
+template <bool LOGD, bool C2, bool Relay>
 __global__ __launch_bounds__(256, 2) void wkv_split_kernel(Geometry g, Tensors t, Workspace ws) {
     __shared__ SmemSplit<C2> sm;
     const int items = g.n_seg * g.H;
-    const bool state_role = (int)blockIdx.x < items;
+    const bool state_role = Relay || (int)blockIdx.x < items;
     const int item = state_role ? (int)blockIdx.x : (int)blockIdx.x - items;
     const int h = item % g.H;
     const int seg = item / g.H;
@@ -1253,7 +1267,8 @@ __global__ __launch_bounds__(256, 2) void wkv_split_kernel(Geometry g, Tensors t
     // a split the host did not plan (device offsets differing from the host
     // copy) has no workspace behind it: leave the item alone
     if (split && (ws.ctl == nullptr || ws.seg_state == nullptr || ws.seg_start == nullptr)) return;
-    if (state_role && (!split || it.p == it.P - 1)) return;   // the last segment's aggregate is unused
+    const bool has_state = split && it.p < it.P - 1;       // the last segment's aggregate is unused
+    if (!Relay && state_role && !has_state) return;
     const int tid = threadIdx.x;
     const int n_state = it.P - 1;
     const size_t slot = ((size_t)it.n * g.H + h) * (kHeadDim * kHeadDim);
@@ -1262,7 +1277,7 @@ __global__ __launch_bounds__(256, 2) void wkv_split_kernel(Geometry g, Tensors t
     if (split && tid == 0) epoch = ctl_load(&rec->epoch);
     const int next = (int)((unsigned)epoch + 1u);          // wraps after 2^32 calls
 
-    if (state_role) {
+    if (state_role && has_state) {
         float S[4][4], lam[4] = {0.f, 0.f, 0.f, 0.f};
         #pragma unroll
         for (int ib = 0; ib < 4; ++ib)
@@ -1333,7 +1348,9 @@ __global__ __launch_bounds__(256, 2) void wkv_split_kernel(Geometry g, Tensors t
         }
         complete_stores();
         if (tid == 0) ctl_arrive(&rec->scanned, n_state, &rec->started, next);
-        return;
+        if constexpr (!Relay) return;
+        // relay: the main role follows; every thread has passed the barrier
+        // above, so the state role's LDS is free
     }
 
     // main role
@@ -1806,19 +1823,23 @@ __global__ __launch_bounds__(512, 1) void wkv_chunk_pc_kernel(Geometry g, Tensor
 
 namespace {
 using KernelFn = void (*)(Geometry, Tensors, Workspace);
-KernelFn split_kernel_for(const Variant &v) {
-    return v.log_decay ? (v.c2 ? wkv_split_kernel<true, true> : wkv_split_kernel<true, false>)
-                       : (v.c2 ? wkv_split_kernel<false, true> : wkv_split_kernel<false, false>);
+template <bool Relay>
+KernelFn split_kernel_form(const Variant &v) {
+    return v.log_decay ? (v.c2 ? wkv_split_kernel<true, true, Relay> : wkv_split_kernel<true, false, Relay>)
+                       : (v.c2 ? wkv_split_kernel<false, true, Relay> : wkv_split_kernel<false, false, Relay>);
+}
+KernelFn split_kernel_for(const Variant &v, bool relay) {
+    return relay ? split_kernel_form<true>(v) : split_kernel_form<false>(v);
 }
 }  // namespace
 
-hipError_t split_launch_capacity(const Variant &v, int64_t *capacity) {
+hipError_t split_launch_capacity(const Variant &v, bool relay, int64_t *capacity) {
     constexpr int kMaxDevices = 64;
-    static std::atomic<int64_t> cache[kMaxDevices][4];       // 0: not yet measured
+    static std::atomic<int64_t> cache[kMaxDevices][8];       // 0: not yet measured
     int dev = -1;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return e;
-    const int form = (v.log_decay ? 1 : 0) + (v.c2 ? 2 : 0);
+    const int form = (v.log_decay ? 1 : 0) + (v.c2 ? 2 : 0) + (relay ? 4 : 0);
     if (dev >= 0 && dev < kMaxDevices) {
         const int64_t c = cache[dev][form].load(std::memory_order_relaxed);
         if (c > 0) {
@@ -1828,7 +1849,7 @@ hipError_t split_launch_capacity(const Variant &v, int64_t *capacity) {
     }
     int cus = 0, per_cu = 0;
     if ((e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess) return e;
-    if ((e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, split_kernel_for(v), 256, 0)) != hipSuccess)
+    if ((e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, split_kernel_for(v, relay), 256, 0)) != hipSuccess)
         return e;
     *capacity = (int64_t)cus * per_cu;
     if (dev >= 0 && dev < kMaxDevices && *capacity > 0) cache[dev][form].store(*capacity, std::memory_order_relaxed);
@@ -1841,8 +1862,8 @@ hipError_t launch_chunked(const Geometry &g, const Tensors &t, const Workspace &
     if (items <= 0) return hipSuccess;
     const dim3 grid((unsigned)items), block(256);
     if (split && ws.ctl) {                             // one launch: state, scan and chunked roles
-        const dim3 grid2((unsigned)(2 * items));
-        const KernelFn k = split_kernel_for(v);
+        const dim3 grid2((unsigned)(g.relay ? items : 2 * items));
+        const KernelFn k = split_kernel_for(v, g.relay != 0);
         if (tm.start || tm.stop)
             hipExtLaunchKernelGGL(k, grid2, block, 0, st, tm.start, tm.stop, 0, g, t, ws);
         else

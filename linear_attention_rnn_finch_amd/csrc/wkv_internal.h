@@ -42,6 +42,10 @@ struct Geometry {
     // its own aggregate, which the segment scan chains in order
     int runs;
     int run_len;
+    // one-launch split only: 1 when each workgroup takes the state role and
+    // then the main role of its item (grid of items), 0 for the two-role grid
+    // of 2 * items
+    int relay;
 };
 
 // One work item's token range and position inside its sequence.
@@ -192,7 +196,7 @@ hipError_t launch_chunked(const Geometry &g, const Tensors &t, const Workspace &
                           Variant v, hipStream_t st, KernelTiming tm = {});
 // workgroups of the one-launch split kernel that the current device holds at
 // once (compute units x resident workgroups per unit)
-hipError_t split_launch_capacity(const Variant &v, int64_t *capacity);
+hipError_t split_launch_capacity(const Variant &v, bool relay, int64_t *capacity);
 // epilogue of Finch-C2 pre-fill: LayerNorm over heads, GOLD key compression
 hipError_t launch_layernorm_rows(const float *x, const float *gamma, const float *beta, float eps, void *y,
                                  bool out_bf16, int64_t rows, int width, hipStream_t st, KernelTiming tm = {});

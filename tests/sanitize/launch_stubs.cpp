@@ -25,5 +25,5 @@ hipError_t launch_gold_compress(const uint16_t *, const uint16_t *, void *, bool
 hipError_t launch_plan_varlen(const Geometry &, int32_t *, int32_t *, int32_t *, hipStream_t) {
     return hipErrorInvalidValue;
 }
-hipError_t split_launch_capacity(const Variant &, int64_t *) { return hipErrorInvalidValue; }
+hipError_t split_launch_capacity(const Variant &, bool, int64_t *) { return hipErrorInvalidValue; }
 }  // namespace finch

@@ -1,6 +1,9 @@
 """The one-launch form of split calls (wkv_split_kernel): state pass, segment
 combine and chunked scan as workgroup roles of one grid, handing segment
-states to each other through the workspace's control records.
+states to each other through the workspace's control records.  When every
+(segment, head) item fits on the device at once (512 workgroups on MI355X),
+one workgroup per item takes both roles in turn (the relay grid); with more
+items the grid has a state workgroup and a main workgroup per item.
 
 Every case runs both launch forms on the same inputs: one launch must equal
 the three launches (state pass, segment scan, chunked scan) bit for bit, both
@@ -136,6 +139,26 @@ def test_one_workspace_serves_calls_of_other_sizes():
         o_ref, s_ref = run_oracle(wl)
         eo, es = errors(wl, o, s, o_ref, s_ref)
         assert eo <= 2e-3 and es <= 2e-3, (B, T, H, eo, es)
+
+
+@pytest.mark.parametrize("B,T,H,decay,variant", [(3, 520, 57, "w", "finch"), (4, 600, 48, "log", "c2")],
+                         ids=["513_items", "576_items_c2_logdecay"])
+def test_two_role_grid_when_items_exceed_the_device(B, T, H, decay, variant):
+    """More (segment, head) items than the device holds at once (three
+    segments of 256 tokens per sequence, 513 and 576 items) but every state
+    workgroup resident: the two-role grid, with an initial state."""
+    import linear_attention_rnn_finch_amd as fw
+    assert fw.workspace_bytes(B, T, H, 64) > 0
+    wl = make_workload(3, B=B, T=T, H=H, decay=decay, variant=variant)
+    g = to_gpu(wl)
+    ws = _workspace(wl)
+    log("case two-role grid B=%d T=%d H=%d" % (B, T, H))
+    out = _both_forms(wl, g, ws)
+    assert torch.equal(out[1][0], out[3][0]) and torch.equal(out[1][1], out[3][1])
+    _check_records(_records(ws, B * H), calls=1)
+    o_ref, s_ref = run_oracle(wl)
+    eo, es = errors(wl, out[1][0], out[1][1], o_ref, s_ref)
+    assert eo <= 2e-3 and es <= 2e-3, (eo, es)
 
 
 def test_more_pairs_than_records_take_three_launches():
