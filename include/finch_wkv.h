@@ -123,7 +123,7 @@ const char *wkv_last_error(void);
  * same device.
  *
  * A nonzero workspace begins with WKV_WORKSPACE_CONTROL_BYTES of control
- * records: counters and flags through which the workgroups of one launch hand
+ * records: counters through which the workgroups of one launch hand
  * segment states to each other.  Zero its first WKV_WORKSPACE_CONTROL_BYTES
  * bytes once, before the first call that uses it (e.g. one hipMemset after
  * allocating it); every call leaves them ready for the next one, so they must

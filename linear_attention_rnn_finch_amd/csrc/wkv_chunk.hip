@@ -1170,12 +1170,14 @@ __global__ __launch_bounds__(256, 2) void wkv_chunk_kernel(Geometry g, Tensors t
 // bound expires, so no launch can hang.
 //
 // Memory.  Everything handed between workgroups (aggregates, start states,
-// counters, flags) is written and read with agent-scope atomic accesses,
-// which go through to the level that every XCD shares; a publisher waits for
-// its stores to complete before it counts itself.  No cache-wide release or
-// acquire is needed.  The per-(sequence, head) control records (SplitCtl)
-// carry an epoch that the last workgroup advances, so no record is cleared
-// between calls.
+// counters) is written and read with agent-scope atomic accesses, which go
+// through to the level that every XCD shares; a publisher waits for its
+// stores to complete before it counts itself.  No cache-wide release or
+// acquire is needed.  Waiters poll the counters of the per-(sequence, head)
+// control record (SplitCtl) themselves, so the last arrival needs no second
+// store to release them.  The counters of a call are reset by the last main
+// workgroup of a later segment to finish, when every workgroup of the record
+// has passed its waits, so no record is cleared between calls.
 constexpr uint64_t kWaitTicks = 1ull << 27;     // ~1.3 s of the 100 MHz clock: a safety bound only
 constexpr int kChainBatch = 16;                 // aggregates whose loads are issued together
 
@@ -1197,18 +1199,14 @@ __device__ __forceinline__ void complete_stores() {
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
 }
-// Thread 0: count the workgroup in *ctr; the last of n resets the counter and
-// sets *flag = val.
-__device__ __forceinline__ bool ctl_arrive(int *ctr, int n, int *flag, int val) {
-    if (__hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != n - 1) return false;
-    ctl_store(ctr, 0);
-    ctl_store(flag, val);
-    return true;
+// Thread 0: count the workgroup in *ctr; returns the count before it.
+__device__ __forceinline__ int ctl_add(int *ctr) {
+    return __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-// Thread 0: wait until *flag == val (bounded; on expiry the record is marked).
-__device__ __forceinline__ void ctl_wait(int *flag, int val, int *err) {
+// Thread 0: wait until *ctr == n (bounded; on expiry the record is marked).
+__device__ __forceinline__ void ctl_wait(int *ctr, int n, int *err) {
     const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
-    while (ctl_load(flag) != val) {
+    while (ctl_load(ctr) != n) {
         __builtin_amdgcn_s_sleep(2);
         if (__builtin_amdgcn_s_memrealtime() - t0 > kWaitTicks) {
             ctl_store(err, 1);
@@ -1218,17 +1216,18 @@ __device__ __forceinline__ void ctl_wait(int *flag, int val, int *err) {
 }
 
 // Start state of a main-role workgroup: state_in (or zeros) for the first
-// segment of a sequence, else the published start state.  Then the flag is
-// read before the first chunk's loads are issued, so that checking it waits
-// for that one load only, and the state is read with agent-scope loads.
+// segment of a sequence, else the published start state.  Then the counter
+// of written start-state slices is read before the first chunk's loads are
+// issued, so that checking it waits for that one load only, and the state is
+// read with agent-scope loads.
 struct SplitStartState {
     SplitCtl *rec;                          // null: a first segment
     const float *first;                     // state_in of the sequence, or null
     const float *src;                       // published start state
-    int epoch;                              // thread 0 only
+    int n_state;                            // state workgroups of the (sequence, head)
     int seen = 0;
     __device__ void begin() {
-        if (rec && threadIdx.x == 0) seen = ctl_load(&rec->started);
+        if (rec && threadIdx.x == 0) seen = ctl_load(&rec->scanned);
     }
     __device__ void load(float (&S)[4][4]) {
         if (!rec) {
@@ -1236,8 +1235,7 @@ struct SplitStartState {
             return;
         }
         const int tid = threadIdx.x;
-        const int want = (int)((unsigned)epoch + 1u);
-        if (tid == 0 && seen != want) ctl_wait(&rec->started, want, &rec->error);
+        if (tid == 0 && seen != n_state) ctl_wait(&rec->scanned, n_state, &rec->error);
         __syncthreads();
         const int wave = tid >> 6, i16 = tid & 15, grp = (tid & 63) >> 4;
         #pragma unroll
@@ -1273,9 +1271,6 @@ __global__ __launch_bounds__(256, 2) void wkv_split_kernel(Geometry g, Tensors t
     const int n_state = it.P - 1;
     const size_t slot = ((size_t)it.n * g.H + h) * (kHeadDim * kHeadDim);
     SplitCtl *rec = split ? ws.ctl + ((size_t)it.n * g.H + h) : nullptr;
-    int epoch = 0;                                         // thread 0 only; flags hold epoch + 1
-    if (split && tid == 0) epoch = ctl_load(&rec->epoch);
-    const int next = (int)((unsigned)epoch + 1u);          // wraps after 2^32 calls
 
     if (state_role && has_state) {
         float S[4][4], lam[4] = {0.f, 0.f, 0.f, 0.f};
@@ -1300,8 +1295,7 @@ __global__ __launch_bounds__(256, 2) void wkv_split_kernel(Geometry g, Tensors t
             }
         }
         complete_stores();
-        if (tid == 0 && !ctl_arrive(&rec->arrived, n_state, &rec->ready, next))
-            ctl_wait(&rec->ready, next, &rec->error);
+        if (tid == 0 && ctl_add(&rec->arrived) != n_state - 1) ctl_wait(&rec->arrived, n_state, &rec->error);
         __syncthreads();
         // this workgroup's share of the chain: rows of 256 entries (one per
         // thread) numbered p, p + P - 1, ...; two rows at a time, their loads
@@ -1347,7 +1341,7 @@ __global__ __launch_bounds__(256, 2) void wkv_split_kernel(Geometry g, Tensors t
             }
         }
         complete_stores();
-        if (tid == 0) ctl_arrive(&rec->scanned, n_state, &rec->started, next);
+        if (tid == 0) ctl_add(&rec->scanned);
         if constexpr (!Relay) return;
         // relay: the main role follows; every thread has passed the barrier
         // above, so the state role's LDS is free
@@ -1358,12 +1352,18 @@ __global__ __launch_bounds__(256, 2) void wkv_split_kernel(Geometry g, Tensors t
     float S[4][4];
     const bool later = split && it.p > 0;
     SplitStartState src{later ? rec : nullptr, t.state_in ? t.state_in + slot : nullptr,
-                        later ? ws.seg_start + (size_t)item * kSegStartFloats : nullptr, epoch};
+                        later ? ws.seg_start + (size_t)item * kSegStartFloats : nullptr, n_state};
     scan_chunks<LOGD, C2>(sm.main, t, it.t0, it.t1, h, g.H, src, keep, S);
     // the main workgroups of later segments count the call done: each has seen
     // every start state published, so every other use of the record in this
-    // call is over once all of them have arrived
-    if (later && tid == 0) ctl_arrive(&rec->done, n_state, &rec->epoch, next);
+    // call is over (every wait passed) once all of them have arrived, and the
+    // last resets its counters for the next call
+    if (later && tid == 0 && ctl_add(&rec->done) == n_state - 1) {
+        ctl_store(&rec->arrived, 0);
+        ctl_store(&rec->scanned, 0);
+        ctl_store(&rec->done, 0);
+        ctl_add(&rec->epoch);
+    }
     if (keep) store_public_state(t.state_out + slot, S);
 }
 

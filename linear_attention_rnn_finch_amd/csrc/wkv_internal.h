@@ -137,20 +137,18 @@ struct Variant {
 };
 
 // Control record of one (sequence, head) for the one-launch split path: the
-// workgroups of a call meet through these counters and flags (agent-scope
-// atomics).  A flag is set to epoch + 1 and read against that value, and the
-// last main workgroup of the (sequence, head) to finish advances the epoch, so a
-// record is ready for the next call without any clearing; counters return to
-// zero at the end of each call.  A record must be zero before its first use.
+// workgroups of a call meet through these counters (agent-scope atomics),
+// which waiters poll until they reach the number of workgroups counted.  The
+// last main workgroup of the (sequence, head) to finish resets them to zero
+// and advances the epoch, so a record is ready for the next call without any
+// clearing.  A record must be zero before its first use.
 struct SplitCtl {
     int epoch;      // calls that have completed on this record
     int done;       // main workgroups of later segments that have finished
     int arrived;    // state workgroups that have published their aggregate
-    int ready;      // epoch + 1: every aggregate of the call is published
     int scanned;    // state workgroups that have written their start-state slices
-    int started;    // epoch + 1: every start state of the call is written
     int error;      // sticky: a bounded wait expired (results of that call are void)
-    int pad[9];
+    int pad[11];
 };
 static_assert(sizeof(SplitCtl) == 64, "one 64-byte record per (sequence, head)");
 // records at the head of every split plan's workspace: calls with more
