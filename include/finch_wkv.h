@@ -293,6 +293,11 @@ wkv_status_t wkv_set_kernel_timing_events(void *event_before, void *event_after)
  * when the call has more than WKV_WORKSPACE_CONTROL_BYTES / 64 (sequence,
  * head) pairs or more state workgroups than the device holds at once.
  * launches = 3 always takes the three launches.  Both give identical results.
+ * The one launch counts on its waiting workgroups being resident together
+ * (the occupancy of an otherwise idle device): beside kernels of other
+ * streams it may wait for them to leave, and a wait longer than about 1.3 s
+ * ends the launch with that call's results void.  Callers that share the
+ * device with long-running kernels should take the three launches.
  * Per thread; WKV_EINVAL for other values.
  */
 wkv_status_t wkv_set_split_launches(int launches);

@@ -78,7 +78,9 @@ def abi_version() -> int:
 def set_split_launches(launches: int) -> None:
     """Launch form of split bf16 calls made from this thread: 1 (default) runs
     one launch where it can, 3 always the state pass, the segment scan and the
-    chunked scan.  Both give identical results."""
+    chunked scan.  Both give identical results.  The one launch needs its
+    workgroups resident together; beside long-running kernels of other
+    streams, take 3 (see wkv_set_split_launches in finch_wkv.h)."""
     st = int(_lib.wkv_set_split_launches(int(launches)))
     if st != WKV_OK:
         raise WkvError(st, _lib.wkv_last_error().decode())
