@@ -15,6 +15,9 @@ not part of the figure.  The main chunked-scan kernel is also timed per launch
 with HIP events attached to its dispatch (through the library's timing hook),
 which gives the roofline figure.  The fp64 CPU oracle is timed on the
 host cores over a bounded sample of the same workload (cpu_baseline).
+With the default workload (one 4096-token sequence, d_model 2048) the batch
+of eight such sequences is timed after it in the same process and reported
+beside the headline (``same_metric_other_shape``; ``--also ''`` skips it).
 ``--decay log`` feeds the decay as d (w = exp(-exp(d))) and ``--variant c2``
 runs the Finch-C2 mixer (with its second-value stream); each such form is
 its own workload name ("<config>+logdecay", "<config>+c2", ...).
@@ -342,6 +345,10 @@ def main():
     ap.add_argument("--split-launches", type=int, choices=(1, 3), default=1,
                     help="launch form of split calls: 1 (the library's default: one launch where it "
                          "can) or 3 (state pass, segment scan, chunked scan), for comparison")
+    ap.add_argument("--also", default="train_batch_b8_t4096",
+                    help="with the default workload: also time this one (the metric's batch of "
+                         "eight sequences at the same d_model and T) and report it beside the "
+                         "headline; '' to skip")
     ap.add_argument("--op", choices=("wkv", "layernorm", "compress"), default="wkv",
                     help="the pre-fill scan (default), or one epilogue step on the 1.5B layer "
                          "shape: LayerNorm over heads, GOLD key compression")
@@ -353,7 +360,28 @@ def main():
         sys.exit(2)
     if args.op != "wkv":
         return bench_epilogue(args)
+    rec = bench_wkv(args, args.config)
+    # the metric's other workload at d_model 2048, T = 4096 (the batch of
+    # eight sequences), measured in the same process after the headline and
+    # reported beside it; the headline value stays the one-sequence layer's
+    if (args.also and rec["config"]["workload"] == "layer_1p5b_t4096"
+            and args.decay == "w" and args.variant == "finch"):
+        sub = argparse.Namespace(**vars(args))
+        sub.no_cpu_baseline, sub.steps, sub.warmup, sub.rotate = True, 50, 5, 0
+        other = bench_wkv(sub, args.also)
+        rec["same_metric_other_shape"] = {
+            "workload": other["config"]["workload"],
+            "B": other["config"]["B"], "T": other["config"]["T"], "H": other["config"]["H"],
+            "value": other["value"], "unit": other["unit"], "steps": sub.steps,
+            "ms_per_step": other["ms_per_step"],
+            "frac": other["roofline"]["frac"], "traffic": other["roofline"]["traffic"],
+            "algorithmic_bytes_per_call": other["roofline"]["algorithmic_bytes_per_call"],
+            "main_kernel": other["roofline"]["main_kernel"]}
+    print(json.dumps(rec), flush=True)
 
+
+def bench_wkv(args, config):
+    """The pre-fill scan on one workload (name or index); returns the record."""
     import numpy as np
     import torch
     import linear_attention_rnn_finch_amd as fw
@@ -361,7 +389,7 @@ def main():
     from synth import make_workload, get_config, error_report
 
     fw.set_split_launches(args.split_launches)
-    cfg = get_config(int(args.config) if args.config.isdigit() else args.config)
+    cfg = get_config(int(config) if config.isdigit() else config)
     wl = make_workload(cfg, decay=args.decay, variant=args.variant)
     name = workload_name(cfg.name, args.decay, args.variant)
     dev = torch.device("cuda", 0)
@@ -549,7 +577,7 @@ def main():
             "max_row_err_o": ro["row"], "max_row_err_state": rs["row"],
             "max_elem_err_floored_o": ro["elem_floored"],
             "tol": cfg.tolerance}
-    print(json.dumps(rec), flush=True)
+    return rec
 
 
 def bench_epilogue(args):
