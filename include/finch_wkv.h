@@ -63,7 +63,7 @@
 extern "C" {
 #endif
 
-#define FINCH_WKV_ABI_VERSION 4
+#define FINCH_WKV_ABI_VERSION 5
 
 /* Bytes of control records at the start of every nonzero workspace (see
  * wkv_prefill_workspace_bytes). */
@@ -301,6 +301,26 @@ wkv_status_t wkv_set_kernel_timing_events(void *event_before, void *event_after)
  * Per thread; WKV_EINVAL for other values.
  */
 wkv_status_t wkv_set_split_launches(int launches);
+
+/*
+ * Whether one-launch calls on a workspace kept their results.  A bounded wait
+ * of the one launch (see wkv_set_split_launches) that expires marks its
+ * (sequence, head) control record, and that call's results are void; the
+ * mark stays until cleared here.  This reads the control records of
+ * `workspace` (the first WKV_WORKSPACE_CONTROL_BYTES) after the work queued
+ * on `stream` so far, waiting for that work, and sets *count to the number of
+ * marked records (0: every one-launch call on the workspace since the marks
+ * were last cleared kept its results).  With clear != 0 it then zeroes the
+ * marks it found.  workspace NULL reads the static scratch of
+ * wkv_prefill_noalloc on the current device (count 0 if no such call has
+ * run there).  workspace_bytes 0 (a call that needed no workspace): count 0.
+ *   WKV_EINVAL      count is NULL
+ *   WKV_EWORKSPACE  0 < workspace_bytes < WKV_WORKSPACE_CONTROL_BYTES
+ *   WKV_EHIP        the copy or the wait failed
+ * Synchronous with the host (not for graph capture).
+ */
+wkv_status_t wkv_workspace_errors(const void *workspace, size_t workspace_bytes, int clear, int *count,
+                                  void *stream);
 
 #ifdef __cplusplus
 }

@@ -59,6 +59,8 @@ _lib.wkv_gold_compress.restype = _i
 _lib.wkv_gold_compress.argtypes = [_vp, _vp, _vp, _i, ctypes.c_int64, _i, _vp]
 _lib.wkv_set_split_launches.restype = _i
 _lib.wkv_set_split_launches.argtypes = [_i]
+_lib.wkv_workspace_errors.restype = _i
+_lib.wkv_workspace_errors.argtypes = [_vp, _sz, _i, ctypes.POINTER(ctypes.c_int), _vp]
 _lib.wkv_prefill_varlen_ex.restype = _i
 _lib.wkv_prefill_varlen_ex.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i,
                                        _vp, _vp, _vp, _i, _i, _i, ctypes.c_uint, _vp, _sz, _vp]
@@ -92,6 +94,25 @@ def new_workspace(nbytes: int, device) -> torch.Tensor:
     ws = torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=device)
     ws[:WORKSPACE_CONTROL_BYTES].zero_()
     return ws
+
+
+def workspace_errors(workspace=None, clear: bool = False, stream=None) -> int:
+    """Control records of `workspace` (a tensor from new_workspace, or None
+    for the static scratch of the allocation-free entry point on the current
+    device) marked by a one-launch call whose bounded wait expired, i.e. whose
+    results are void; 0 means every such call kept its results.  Waits for the
+    work queued on the stream; clear=True also resets the marks."""
+    if workspace is None:
+        ptr, nbytes = None, 0
+    else:
+        _device_tensor("workspace", workspace)
+        ptr, nbytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
+        if nbytes == 0:                  # a call that needed no workspace: no records
+            return 0
+    n = ctypes.c_int(0)
+    _check(int(_lib.wkv_workspace_errors(ptr, nbytes, 1 if clear else 0, ctypes.byref(n),
+                                         _stream_handle(stream))))
+    return int(n.value)
 
 
 def _check(status: int):

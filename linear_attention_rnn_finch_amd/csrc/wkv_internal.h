@@ -224,5 +224,8 @@ wkv_status_t prefill_fixed_from(const void *r, const void *k, const void *v, con
                                 const float *u, const void *u2, const float *state_in, void *o,
                                 float *state_out, int B, int T, int H, int D, wkv_dtype_t dt,
                                 unsigned flags, ScratchSource scratch, void *stream);
+// The static scratch of wkv_prefill_noalloc on the current device, or null
+// when no such call has set it up there.
+void *static_scratch_if_set();
 
 }  // namespace finch

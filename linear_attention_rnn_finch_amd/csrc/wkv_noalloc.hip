@@ -50,6 +50,14 @@ wkv_status_t scratch_for_call(size_t bytes, void **out) {
 }
 
 }  // namespace
+
+void *static_scratch_if_set() {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+    std::lock_guard<std::mutex> lock(g_mu);
+    return g_scratch_ptr[dev];
+}
+
 }  // namespace finch
 
 extern "C" wkv_status_t wkv_prefill_noalloc(const void *r, const void *k, const void *v, const void *decay,

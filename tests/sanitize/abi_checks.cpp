@@ -53,6 +53,14 @@ int main() {
            WKV_EUNSUPPORTED);
     EXPECT(wkv_prefill_noalloc(nullptr, k, v, w, u, nullptr, s_in, o, s_out, 1, 4096, 32, 64, WKV_BF16, 0, nullptr),
            WKV_EINVAL);
+    int marked = -1;
+    EXPECT(wkv_workspace_errors(ws, need, 0, nullptr, nullptr), WKV_EINVAL);                  // no count
+    EXPECT(wkv_workspace_errors(ws, WKV_WORKSPACE_CONTROL_BYTES - 64, 1, &marked, nullptr), WKV_EWORKSPACE);
+    EXPECT(wkv_workspace_errors(ws, 0, 0, &marked, nullptr), WKV_OK);                         // no records
+    if (marked != 0) {
+        std::printf("FAIL: a workspace of 0 bytes reported %d marks\n", marked);
+        ++g_fail;
+    }
 
     // ragged offsets: host copies of every shape the planner reads
     std::vector<int32_t> bad_start = {1, 5, 9}, decreasing = {0, 5, 3}, good = {0, 100, 300};

@@ -61,7 +61,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_abi_version_and_status_strings(lib):
-    assert lib.wkv_abi_version() == 4
+    assert lib.wkv_abi_version() == 5
     for s in range(5):
         assert lib.wkv_status_string(s)
     assert lib.wkv_status_string(99) == b"unknown status"
@@ -338,6 +338,21 @@ def test_compress_validation(lib, kw, expect):
     a.update(kw)
     st = lib.wkv_gold_compress(a["x"], a["w"], a["c"], a["out"], a["tokens"], a["d"], None)
     assert st == expect, lib.wkv_last_error()
+
+
+def test_workspace_errors_validates_before_any_hip_call(lib):
+    lib.wkv_workspace_errors.restype = ctypes.c_int
+    lib.wkv_workspace_errors.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int,
+                                         ctypes.POINTER(ctypes.c_int), ctypes.c_void_p]
+    n = ctypes.c_int(-1)
+    assert lib.wkv_workspace_errors(A, 1 << 20, 0, None, None) == EINVAL
+    assert lib.wkv_workspace_errors(A, 4096, 1, ctypes.byref(n), None) == EWS and n.value == 0
+    n.value = -1
+    assert lib.wkv_workspace_errors(A, 0, 0, ctypes.byref(n), None) == OK and n.value == 0
+    # no workspace and no allocation-free call made on this device (or no
+    # device at all): nothing to read
+    n.value = -1
+    assert lib.wkv_workspace_errors(None, 0, 0, ctypes.byref(n), None) == OK and n.value == 0
 
 
 def test_noalloc_entry_point_validates_before_any_hip_call(lib):

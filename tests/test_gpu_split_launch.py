@@ -213,3 +213,30 @@ def test_random_shapes():
         o_ref, s_ref = run_oracle(wl)
         eo, es = errors(wl, out[1][0], out[1][1], o_ref, s_ref)
         assert eo <= 2e-3 and es <= 2e-3, (case, eo, es)
+
+
+def test_workspace_errors_query():
+    """wkv_workspace_errors: no marks after one-launch calls; a mark planted
+    from the host (what an expired wait leaves; the kernels only ever write
+    that word) is counted, cleared on request, and the workspace then gives
+    the same results as before."""
+    import linear_attention_rnn_finch_amd as fw
+    wl = make_workload(3, B=2, T=2000, H=8)
+    g = to_gpu(wl)
+    ws = _workspace(wl)
+    log("case workspace_errors query")
+    o1, s1 = run_gpu(wl, g, workspace=ws)
+    assert fw.workspace_errors(ws) == 0
+    recs = ws[:fw.WORKSPACE_CONTROL_BYTES].view(torch.int32).view(-1, 16)
+    recs[3, ERROR] = 1
+    recs[9, ERROR] = 7
+    assert fw.workspace_errors(ws) == 2
+    assert fw.workspace_errors(ws, clear=True) == 2
+    assert fw.workspace_errors(ws) == 0
+    _check_records(_records(ws, 2 * 8), calls=1)
+    o2, s2 = run_gpu(wl, g, workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(s1, s2)
+    assert fw.workspace_errors(ws) == 0
+    # a call that needs no workspace has no records to read
+    assert fw.workspace_errors(torch.empty(0, dtype=torch.uint8, device="cuda")) == 0

@@ -48,3 +48,6 @@ def test_noalloc_matches_regular_entry_point():
         o_or, s_or = run_oracle(wl, heads)
         eo, es = errors(wl, o, st, o_or, s_or, heads)
         assert eo <= 2e-3 and es <= 2e-3
+    # the static scratch's control records: no bounded wait expired
+    import linear_attention_rnn_finch_amd as fw
+    assert fw.workspace_errors(None) == 0
