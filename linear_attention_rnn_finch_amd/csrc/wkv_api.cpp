@@ -5,7 +5,6 @@
 #include "wkv_internal.h"
 
 #include <algorithm>
-#include <cstddef>
 #include <cstdarg>
 #include <cstdio>
 #include <cstdlib>
@@ -519,40 +518,6 @@ wkv_status_t wkv_set_kernel_timing_events(void *before, void *after) {
 wkv_status_t wkv_set_split_launches(int launches) {
     if (launches != 1 && launches != 3) return fail(WKV_EINVAL, "launches=%d must be 1 or 3", launches);
     g_split_launches = launches;
-    return WKV_OK;
-}
-
-wkv_status_t wkv_workspace_errors(const void *workspace, size_t workspace_bytes, int clear, int *count,
-                                  void *stream) {
-    g_last_error.clear();
-    if (!count) return fail(WKV_EINVAL, "count is NULL");
-    *count = 0;
-    const char *base = static_cast<const char *>(workspace);
-    if (!base) {
-        base = static_cast<const char *>(static_scratch_if_set());
-        if (!base) return WKV_OK;
-    } else if (workspace_bytes == 0) {
-        return WKV_OK;
-    } else if (workspace_bytes < (size_t)WKV_WORKSPACE_CONTROL_BYTES) {
-        return fail(WKV_EWORKSPACE, "workspace_bytes=%zu is below the %d bytes of control records",
-                    workspace_bytes, WKV_WORKSPACE_CONTROL_BYTES);
-    }
-    const hipStream_t st = static_cast<hipStream_t>(stream);
-    std::vector<SplitCtl> rec(kCtlRecords);
-    hipError_t e = hipMemcpyAsync(rec.data(), base, WKV_WORKSPACE_CONTROL_BYTES, hipMemcpyDeviceToHost, st);
-    if (e == hipSuccess) e = hipStreamSynchronize(st);
-    if (e != hipSuccess) return fail_hip(e, "reading the control records");
-    int marked = 0;
-    for (int i = 0; i < kCtlRecords; ++i) {
-        if (rec[i].error == 0) continue;
-        ++marked;
-        if (clear) {
-            char *at = const_cast<char *>(base) + i * sizeof(SplitCtl) + offsetof(SplitCtl, error);
-            if ((e = hipMemsetAsync(at, 0, sizeof(int), st)) != hipSuccess) return fail_hip(e, "clearing a mark");
-        }
-    }
-    if (clear && marked > 0 && (e = hipStreamSynchronize(st)) != hipSuccess) return fail_hip(e, "clearing the marks");
-    *count = marked;
     return WKV_OK;
 }
 

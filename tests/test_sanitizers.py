@@ -43,7 +43,8 @@ def test_abi_validation_under_host_asan_and_ubsan(tmp_path):
            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
            "-I", os.path.join(ROOT, "include"), "-I", CSRC,
            os.path.join(HERE, "abi_checks.cpp"), os.path.join(HERE, "launch_stubs.cpp"),
-           os.path.join(CSRC, "wkv_api.cpp"), os.path.join(CSRC, "wkv_noalloc.hip"), "-o", exe]
+           os.path.join(CSRC, "wkv_api.cpp"), os.path.join(CSRC, "wkv_noalloc.hip"),
+           os.path.join(CSRC, "wkv_query.cpp"), "-o", exe]
     res = subprocess.run(cmd, capture_output=True, text=True, timeout=600)
     assert res.returncode == 0, res.stderr[-3000:]
     _run(exe)
