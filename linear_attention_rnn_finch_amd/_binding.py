@@ -109,6 +109,7 @@ def workspace_errors(workspace=None, clear: bool = False, stream=None) -> int:
         ptr, nbytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
         if nbytes == 0:                  # a call that needed no workspace: no records
             return 0
+        _same_device(workspace.device, stream)
     n = ctypes.c_int(0)
     _check(int(_lib.wkv_workspace_errors(ptr, nbytes, 1 if clear else 0, ctypes.byref(n),
                                          _stream_handle(stream))))
@@ -147,6 +148,17 @@ def _device_tensor(name, t, dtype=None):
         raise ValueError("%s must be contiguous" % name)
     if dtype is not None and t.dtype != dtype:
         raise TypeError("%s must be %s, got %s" % (name, dtype, t.dtype))
+
+
+def _same_device(device, stream, **tensors):
+    """Every given tensor (and the stream, if any) on `device`: the C ABI takes
+    bare pointers and launches on the stream's device, so a tensor of another
+    GPU would be read or written by kernels that cannot see it."""
+    for name, t in tensors.items():
+        if t is not None and t.device != device:
+            raise ValueError("%s is on %s, the call's inputs on %s" % (name, t.device, device))
+    if stream is not None and stream.device != device:
+        raise ValueError("stream belongs to %s, the call's inputs to %s" % (stream.device, device))
 
 
 def workspace_bytes(B: int, T: int, H: int, D: int = HEAD_DIM, dtype=torch.bfloat16) -> int:
@@ -250,6 +262,8 @@ def prefill(r, k, v, w, u, state_in=None, *, o=None, state_out=None, want_state=
             raise ValueError("state_in must be [B, H, D, D]")
     code = _dtype_code(r)
     _check_outputs(o, state_out, (B, T, H, D), (B, H, D, D), out_dtype)
+    _same_device(r.device, stream, k=k, v=v, w=w, u=u, second_value=second_value, state_in=state_in,
+                 o=o, state_out=state_out, workspace=workspace)
     with _on_stream(stream):
         if o is None:
             o = torch.empty((B, T, H, D), dtype=out_dtype, device=r.device)
@@ -305,6 +319,8 @@ def prefill_varlen(r, k, v, w, u, cu_seqlens, state_in=None, *, cu_seqlens_host=
             raise ValueError("state_in must be [N, H, D, D]")
     code = _dtype_code(r)
     _check_outputs(o, state_out, (total, H, D), (N, H, D, D), out_dtype)
+    _same_device(r.device, stream, k=k, v=v, w=w, u=u, second_value=second_value, cu_seqlens=cu_seqlens,
+                 state_in=state_in, o=o, state_out=state_out, workspace=workspace)
     with _on_stream(stream):
         if o is None:
             o = torch.empty((total, H, D), dtype=out_dtype, device=r.device)
@@ -343,12 +359,14 @@ def layernorm_heads(x, gamma, beta, eps=1e-5, *, out_dtype=torch.bfloat16, y=Non
         if tuple(t.shape) != (W,):
             raise ValueError("%s must be [%d]" % (name, W))
     code = _out_code(out_dtype)
-    if y is None:
-        y = torch.empty(x.shape, dtype=out_dtype, device=x.device)
-    else:
+    if y is not None:
         _device_tensor("y", y, out_dtype)
         if y.shape != x.shape:
             raise ValueError("y must have x's shape")
+    _same_device(x.device, stream, gamma=gamma, beta=beta, y=y)
+    if y is None:
+        with _on_stream(stream):
+            y = torch.empty(x.shape, dtype=out_dtype, device=x.device)
     tokens = x.numel() // W if W else 0
     with torch.cuda.device(x.device):
         status = _lib.wkv_layernorm_heads(_ptr(x), _ptr(gamma), _ptr(beta), float(eps), _ptr(y), code,
@@ -371,12 +389,14 @@ def gold_compress(x, w_kd, *, out_dtype=torch.float32, c=None, stream=None):
     if tuple(w_kd.shape) != (D // 16, D):
         raise ValueError("w_kd must be [d_model/16, d_model] = %s" % ((D // 16, D),))
     code = _out_code(out_dtype)
-    if c is None:
-        c = torch.empty((tokens, D // 16), dtype=out_dtype, device=x.device)
-    else:
+    if c is not None:
         _device_tensor("c", c, out_dtype)
         if tuple(c.shape) != (tokens, D // 16):
             raise ValueError("c must be [tokens, d_model/16]")
+    _same_device(x.device, stream, w_kd=w_kd, c=c)
+    if c is None:
+        with _on_stream(stream):
+            c = torch.empty((tokens, D // 16), dtype=out_dtype, device=x.device)
     with torch.cuda.device(x.device):
         status = _lib.wkv_gold_compress(_ptr(x), _ptr(w_kd), _ptr(c), code, tokens, D, _stream_handle(stream))
     _check(status)
