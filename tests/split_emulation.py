@@ -4,8 +4,8 @@ split products the matrix-core evaluation needs.
 The chunked form (64-token chunks; [Summary] section 3.4, "Training and
 Inference Procedures": pre-fill in parallel chunks of the recurrence) feeds
 the matrix cores bf16 operands.  An fp32 operand x is carried as
-hi = x truncated to bf16 and lo = x - hi rounded to nearest-even bf16, and a
-product of two such operands as hi*hi + hi*lo + lo*hi.  This module repeats the
+hi = x rounded to nearest-even bf16 and lo = x - hi rounded the same way, and
+a product of two such operands as hi*hi + hi*lo + lo*hi.  This module repeats the
 kernel's chunk arithmetic on the CPU with every operand rounded as the kernel
 rounds it, and can leave out any of the split products:
 
@@ -15,9 +15,9 @@ rounds it, and can leave out any of the split products:
 - o = r~ S (split r~, split S) + A v (split A, bf16 v);
 - S <- diag(P_63) (S + k~^T v) (split k~).
 
-The kernel truncates the hi parts.  A form that drops products would round
-them to nearest instead (same cost: one packing instruction per two values),
-so the variants with dropped products are evaluated that way, their best case.
+The hi parts may also be truncated instead (the kernel's earlier form, one
+byte permute per two values in place of one packing convert): the remainder
+is then up to a whole bf16 ulp, and the errors are about twice as large.
 
 A matrix-core instruction is emulated as exact products of its bf16 inputs
 summed in fp64 over its 32-wide contraction slice, added to the fp32
@@ -44,6 +44,7 @@ MIN_CHUNK_DECAY = 2.0 ** -96
 FULL = dict(a_hl=True, a_lh=True, ro_rl=True, ro_sl=True, st_kl=True, pr_al=True)
 VARIANTS = {
     "all splits (the kernel)": {},
+    "all splits, hi truncated (the earlier kernel)": dict(hi_trunc=True),
     "A's lo part dropped in the in-chunk pairs": dict(pr_al=False),
     "k~'s lo part dropped in the state update": dict(st_kl=False),
     "S's lo part dropped in the read-out": dict(ro_sl=False),
@@ -90,16 +91,13 @@ def mfma_chain(acc, pairs):
     return acc
 
 
-def chunked_scan(r, k, v, w, u, state0=None, keep=None, hi_rne=None):
+def chunked_scan(r, k, v, w, u, state0=None, keep=None):
     """One sequence: r, k, v, w fp32 [T, H, D] (bf16 values), u fp32 [H, D],
     state0 fp32 [H, D, D] or None.  Returns o fp32 [T, H, D] and the final
-    state fp32 [H, D, D].  With hi_rne the hi parts are rounded to nearest
-    instead of truncated (the better choice once lo parts are dropped: a
-    single bf16 operand then carries half the error); by default only when
-    some product is dropped."""
-    keep = dict(FULL, **(keep or {}))
-    if hi_rne is None:
-        hi_rne = not all(keep.values())
+    state fp32 [H, D, D].  `keep` names products to leave out (False) and
+    hi_trunc=True truncates the hi parts."""
+    keep = {**FULL, "hi_trunc": False, **(keep or {})}
+    hi_rne = not keep.pop("hi_trunc")
     split_ = lambda x: split(x, hi_rne)
     T, H, D = r.shape
     S = np.zeros((H, D, D), np.float32) if state0 is None else state0.astype(np.float32).copy()

@@ -42,7 +42,15 @@ def test_all_splits_stay_far_inside_the_bar(layer_slice):
     assert block < 1e-4 and row < 2e-4 and state < 1e-4, (block, row, state)
 
 
-@pytest.mark.parametrize("name", [n for n in se.VARIANTS if n != "all splits (the kernel)"])
+def test_nearest_rounded_hi_parts_halve_the_error(layer_slice):
+    (r, k, v, w, u, s0), o_ref, s_ref = layer_slice
+    o, s = se.chunked_scan(r, k, v, w, u, s0)
+    o_t, s_t = se.chunked_scan(r, k, v, w, u, s0, dict(hi_trunc=True))
+    near, trunc = se.errors(o, o_ref, s, s_ref), se.errors(o_t, o_ref, s_t, s_ref)
+    assert all(a <= 0.6 * b for a, b in zip(near, trunc)), (near, trunc)
+
+
+@pytest.mark.parametrize("name", [n for n in se.VARIANTS if n.startswith(("A's", "k~", "S's", "r~", "no "))])
 def test_dropping_any_product_fails_the_row_bar(layer_slice, name):
     (r, k, v, w, u, s0), o_ref, s_ref = layer_slice
     o, s = se.chunked_scan(r, k, v, w, u, s0, se.VARIANTS[name])
