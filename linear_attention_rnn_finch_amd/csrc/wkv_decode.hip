@@ -304,15 +304,17 @@ __device__ __forceinline__ int stage_off(int r, int unit) {
     return r * kHeadDim + ((((unit >> 1) ^ f) & 7) << 3) + ((unit & 1) << 2);
 }
 
-// x = hi + lo, hi the bf16 truncation of x (exact remainder), lo rounded to
-// bf16; eight values -> two operands
+// x = hi + lo, hi = x rounded to the nearest bf16 (ties to even), lo the
+// remainder (exact in fp32) rounded the same way; eight values -> two
+// operands.  A nearest-rounded hi leaves at most half a bf16 ulp for lo, one
+// bit more than a truncated hi, for the same instruction count.
 __device__ __forceinline__ void split8(const float (&x)[8], bf16x8 &hi, bf16x8 &lo) {
     u32x4 h4, l4;
     #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        const unsigned b0 = __float_as_uint(x[2 * i]), b1 = __float_as_uint(x[2 * i + 1]);
-        h4[i] = __builtin_amdgcn_perm(b1, b0, 0x07060302u);
-        const f32x2 l = {x[2 * i] - __uint_as_float(b0 & 0xFFFF0000u), x[2 * i + 1] - __uint_as_float(b1 & 0xFFFF0000u)};
+        const f32x2 v = {x[2 * i], x[2 * i + 1]};
+        h4[i] = __builtin_bit_cast(unsigned, __builtin_convertvector(v, bf16x2));
+        const f32x2 l = {x[2 * i] - __uint_as_float(h4[i] << 16), x[2 * i + 1] - __uint_as_float(h4[i] & 0xFFFF0000u)};
         l4[i] = __builtin_bit_cast(unsigned, __builtin_convertvector(l, bf16x2));
     }
     hi = __builtin_bit_cast(bf16x8, h4);
