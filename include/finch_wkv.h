@@ -310,8 +310,11 @@ wkv_status_t wkv_set_split_launches(int launches);
  * `workspace` (the first WKV_WORKSPACE_CONTROL_BYTES) after the work queued
  * on `stream` so far, waiting for that work, and sets *count to the number of
  * marked records (0: every one-launch call on the workspace since the marks
- * were last cleared kept its results).  With clear != 0 it then zeroes the
- * marks it found.  workspace NULL reads the static scratch of
+ * were last cleared kept its results).  With clear != 0 it then zeroes each
+ * marked record whole: an expired wait can leave the record's counters out
+ * of step, and later calls on the workspace may give wrong results without a
+ * mark until it is cleared, so clear (or re-zero the control records) before
+ * using a marked workspace again.  workspace NULL reads the static scratch of
  * wkv_prefill_noalloc on the current device (count 0 if no such call has
  * run there).  workspace_bytes 0 (a call that needed no workspace): count 0.
  *   WKV_EINVAL      count is NULL

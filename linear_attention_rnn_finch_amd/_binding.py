@@ -101,7 +101,9 @@ def workspace_errors(workspace=None, clear: bool = False, stream=None) -> int:
     for the static scratch of the allocation-free entry point on the current
     device) marked by a one-launch call whose bounded wait expired, i.e. whose
     results are void; 0 means every such call kept its results.  Waits for the
-    work queued on the stream; clear=True also resets the marks."""
+    work queued on the stream; clear=True also zeroes each marked record (its
+    counters may be out of step after an expired wait: clear before using a
+    marked workspace again)."""
     if workspace is None:
         ptr, nbytes = None, 0
     else:

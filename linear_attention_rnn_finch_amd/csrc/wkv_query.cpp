@@ -2,8 +2,13 @@
 // their results.  A bounded wait of the one launch that expires marks the
 // error word of its (sequence, head) control record (SplitCtl), and that
 // call's results are void; the kernels only ever set that word, so it stays
-// until a caller clears it here.
-#include <cstddef>
+// until a caller clears it here.  A call whose wait expired can also leave
+// the record's counters out of step (a late arrival counted after the record
+// was reset for the next call), which a later call would read as an arrival
+// of its own; clearing therefore zeroes the whole record, the state every
+// record starts from.  Without an expired wait every count of a call lands
+// before its last main workgroup resets the record, so unmarked records are
+// left as they are.
 #include <cstdio>
 #include <vector>
 
@@ -37,8 +42,8 @@ extern "C" wkv_status_t wkv_workspace_errors(const void *workspace, size_t works
         if (rec[i].error == 0) continue;
         ++marked;
         if (clear) {
-            char *at = const_cast<char *>(base) + i * sizeof(SplitCtl) + offsetof(SplitCtl, error);
-            if ((e = hipMemsetAsync(at, 0, sizeof(int), st)) != hipSuccess)
+            char *at = const_cast<char *>(base) + i * sizeof(SplitCtl);
+            if ((e = hipMemsetAsync(at, 0, sizeof(SplitCtl), st)) != hipSuccess)
                 return record_error(WKV_EHIP, hipGetErrorString(e));
         }
     }
