@@ -303,6 +303,16 @@ wkv_status_t wkv_set_kernel_timing_events(void *event_before, void *event_after)
 wkv_status_t wkv_set_split_launches(int launches);
 
 /*
+ * Bound of each wait of the one launch (see wkv_set_split_launches), in ticks
+ * of the GPU's 100 MHz clock, for tests of the error path: with a bound too
+ * short for the workgroups to meet, waits expire, the launch still ends
+ * normally, its results are void and wkv_workspace_errors reports it.  Per
+ * thread; 0 restores the default of 2^27 ticks (about 1.3 s).  WKV_EINVAL
+ * above 2^32 - 1.
+ */
+wkv_status_t wkv_set_wait_bound(unsigned long long ticks);
+
+/*
  * Whether one-launch calls on a workspace kept their results.  A bounded wait
  * of the one launch (see wkv_set_split_launches) that expires marks its
  * (sequence, head) control record, and that call's results are void; the

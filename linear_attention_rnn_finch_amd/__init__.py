@@ -7,5 +7,5 @@ thin Python binding over that library.
 """
 from ._binding import (  # noqa: F401
     HEAD_DIM, LIBRARY_PATH, WORKSPACE_CONTROL_BYTES, WkvError, abi_version, gold_compress,
-    layernorm_heads, new_workspace, prefill, prefill_varlen, set_split_launches, varlen_workspace_bytes,
-    workspace_bytes, workspace_errors)
+    layernorm_heads, new_workspace, prefill, prefill_varlen, set_split_launches, set_wait_bound,
+    varlen_workspace_bytes, workspace_bytes, workspace_errors)

@@ -59,6 +59,8 @@ _lib.wkv_gold_compress.restype = _i
 _lib.wkv_gold_compress.argtypes = [_vp, _vp, _vp, _i, ctypes.c_int64, _i, _vp]
 _lib.wkv_set_split_launches.restype = _i
 _lib.wkv_set_split_launches.argtypes = [_i]
+_lib.wkv_set_wait_bound.restype = _i
+_lib.wkv_set_wait_bound.argtypes = [ctypes.c_ulonglong]
 _lib.wkv_workspace_errors.restype = _i
 _lib.wkv_workspace_errors.argtypes = [_vp, _sz, _i, ctypes.POINTER(ctypes.c_int), _vp]
 _lib.wkv_prefill_varlen_ex.restype = _i
@@ -86,6 +88,15 @@ def set_split_launches(launches: int) -> None:
     st = int(_lib.wkv_set_split_launches(int(launches)))
     if st != WKV_OK:
         raise WkvError(st, _lib.wkv_last_error().decode())
+
+
+def set_wait_bound(ticks: int) -> None:
+    """Bound of each wait of the one launch, in ticks of the GPU's 100 MHz
+    clock, for tests of the error path (calls made from this thread); 0
+    restores the default (2^27 ticks, about 1.3 s).  A bound too short for
+    the workgroups to meet voids the call's results, which
+    workspace_errors() then reports."""
+    _check(int(_lib.wkv_set_wait_bound(int(ticks))))
 
 
 def new_workspace(nbytes: int, device) -> torch.Tensor:

@@ -19,6 +19,7 @@ thread_local std::string g_last_error;
 thread_local hipEvent_t g_ev_before = nullptr;   // optional timing of the main kernel
 thread_local hipEvent_t g_ev_after = nullptr;
 thread_local int g_split_launches = 1;           // 1: one launch where possible; 3: always three
+thread_local unsigned g_wait_ticks = kDefaultWaitTicks;   // bound of the one launch's waits
 
 wkv_status_t fail(wkv_status_t st, const char *fmt, ...) {
     char buf[512];
@@ -362,6 +363,7 @@ wkv_status_t one_launch(const Plan &p, const Variant &var, OneLaunch *form) {
 
 wkv_status_t run(const Plan &p, const Tensors &t, const Variant &var, void *ws, hipStream_t st) {
     Geometry g = p.g;
+    g.wait_ticks = g_wait_ticks;
     char *base = static_cast<char *>(ws);
     hipError_t e;
     OneLaunch form = OneLaunch::kNone;
@@ -518,6 +520,12 @@ wkv_status_t wkv_set_kernel_timing_events(void *before, void *after) {
 wkv_status_t wkv_set_split_launches(int launches) {
     if (launches != 1 && launches != 3) return fail(WKV_EINVAL, "launches=%d must be 1 or 3", launches);
     g_split_launches = launches;
+    return WKV_OK;
+}
+
+wkv_status_t wkv_set_wait_bound(unsigned long long ticks) {
+    if (ticks > 0xFFFFFFFFull) return fail(WKV_EINVAL, "ticks=%llu exceeds 2^32 - 1", ticks);
+    g_wait_ticks = ticks == 0 ? kDefaultWaitTicks : (unsigned)ticks;
     return WKV_OK;
 }
 

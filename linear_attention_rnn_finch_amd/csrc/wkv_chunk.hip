@@ -1172,7 +1172,7 @@ __global__ __launch_bounds__(256, 2) void wkv_chunk_kernel(Geometry g, Tensors t
 // workgroup, and the host launches the two-role form only when all state
 // workgroups fit on the device at once (the relay form only when all
 // workgroups do), so every workgroup waited for is resident or finished.
-// Each wait is bounded (kWaitTicks) and marks the record's error word if the
+// Each wait is bounded (g.wait_ticks) and marks the record's error word if the
 // bound expires, so no launch can hang.
 //
 // Memory.  Everything handed between workgroups (aggregates, start states,
@@ -1184,7 +1184,6 @@ __global__ __launch_bounds__(256, 2) void wkv_chunk_kernel(Geometry g, Tensors t
 // store to release them.  The counters of a call are reset by the last main
 // workgroup of a later segment to finish, when every workgroup of the record
 // has passed its waits, so no record is cleared between calls.
-constexpr uint64_t kWaitTicks = 1ull << 27;     // ~1.3 s of the 100 MHz clock: a safety bound only
 constexpr int kChainBatch = 16;                 // aggregates whose loads are issued together
 
 __device__ __forceinline__ int ctl_load(int *p) {
@@ -1210,11 +1209,11 @@ __device__ __forceinline__ int ctl_add(int *ctr) {
     return __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 // Thread 0: wait until *ctr == n (bounded; on expiry the record is marked).
-__device__ __forceinline__ void ctl_wait(int *ctr, int n, int *err) {
+__device__ __forceinline__ void ctl_wait(int *ctr, int n, int *err, unsigned bound) {
     const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
     while (ctl_load(ctr) != n) {
         __builtin_amdgcn_s_sleep(2);
-        if (__builtin_amdgcn_s_memrealtime() - t0 > kWaitTicks) {
+        if (__builtin_amdgcn_s_memrealtime() - t0 > bound) {
             ctl_store(err, 1);
             return;
         }
@@ -1231,6 +1230,7 @@ struct SplitStartState {
     const float *first;                     // state_in of the sequence, or null
     const float *src;                       // published start state
     int n_state;                            // state workgroups of the (sequence, head)
+    unsigned bound;                         // of the wait, in ticks of the 100 MHz clock
     int seen = 0;
     __device__ void begin() {
         if (rec && threadIdx.x == 0) seen = ctl_load(&rec->scanned);
@@ -1241,7 +1241,7 @@ struct SplitStartState {
             return;
         }
         const int tid = threadIdx.x;
-        if (tid == 0 && seen != n_state) ctl_wait(&rec->scanned, n_state, &rec->error);
+        if (tid == 0 && seen != n_state) ctl_wait(&rec->scanned, n_state, &rec->error, bound);
         __syncthreads();
         const int wave = tid >> 6, i16 = tid & 15, grp = (tid & 63) >> 4;
         #pragma unroll
@@ -1301,7 +1301,8 @@ __global__ __launch_bounds__(256, 2) void wkv_split_kernel(Geometry g, Tensors t
             }
         }
         complete_stores();
-        if (tid == 0 && ctl_add(&rec->arrived) != n_state - 1) ctl_wait(&rec->arrived, n_state, &rec->error);
+        if (tid == 0 && ctl_add(&rec->arrived) != n_state - 1)
+            ctl_wait(&rec->arrived, n_state, &rec->error, g.wait_ticks);
         __syncthreads();
         // this workgroup's share of the chain: rows of 256 entries (one per
         // thread) numbered p, p + P - 1, ...; two rows at a time, their loads
@@ -1358,7 +1359,8 @@ __global__ __launch_bounds__(256, 2) void wkv_split_kernel(Geometry g, Tensors t
     float S[4][4];
     const bool later = split && it.p > 0;
     SplitStartState src{later ? rec : nullptr, t.state_in ? t.state_in + slot : nullptr,
-                        later ? ws.seg_start + (size_t)item * kSegStartFloats : nullptr, n_state};
+                        later ? ws.seg_start + (size_t)item * kSegStartFloats : nullptr, n_state,
+                        g.wait_ticks};
     scan_chunks<LOGD, C2>(sm.main, t, it.t0, it.t1, h, g.H, src, keep, S);
     // the main workgroups of later segments count the call done: each has seen
     // every start state published, so every other use of the record in this

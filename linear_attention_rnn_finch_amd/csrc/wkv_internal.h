@@ -46,7 +46,11 @@ struct Geometry {
     // then the main role of its item (grid of items), 0 for the two-role grid
     // of 2 * items
     int relay;
+    // one-launch split only: the bound of each wait, in ticks of the 100 MHz
+    // clock (kDefaultWaitTicks unless a test shortens it)
+    unsigned wait_ticks;
 };
+constexpr unsigned kDefaultWaitTicks = 1u << 27;   // ~1.3 s: a safety bound only
 
 // One work item's token range and position inside its sequence.
 struct ItemRange {

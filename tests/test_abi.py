@@ -355,6 +355,14 @@ def test_workspace_errors_validates_before_any_hip_call(lib):
     assert lib.wkv_workspace_errors(None, 0, 0, ctypes.byref(n), None) == OK and n.value == 0
 
 
+def test_wait_bound_switch(lib):
+    lib.wkv_set_wait_bound.restype = ctypes.c_int
+    lib.wkv_set_wait_bound.argtypes = [ctypes.c_ulonglong]
+    assert lib.wkv_set_wait_bound(1 << 32) == EINVAL
+    assert lib.wkv_set_wait_bound(100) == OK
+    assert lib.wkv_set_wait_bound(0) == OK          # back to the default
+
+
 def test_noalloc_entry_point_validates_before_any_hip_call(lib):
     """wkv_prefill_noalloc plans and checks its arguments like wkv_prefill_ex
     before it looks up its static scratch (so these fail without a GPU)."""

@@ -246,3 +246,32 @@ def test_workspace_errors_query():
     _check_records(np.delete(rec, [3, 9], axis=0), calls=2)
     # a call that needs no workspace has no records to read
     assert fw.workspace_errors(torch.empty(0, dtype=torch.uint8, device="cuda")) == 0
+
+
+def test_expired_waits_are_reported_and_the_workspace_recovers():
+    """The error path, forced from the host: with a wait bound of one tick
+    (10 ns) the one launch's waits expire, the launch still ends, the
+    records are marked; after clearing them the same workspace gives the
+    results of a normal call again, bit for bit."""
+    import linear_attention_rnn_finch_amd as fw
+    wl = make_workload(3, B=2, T=2000, H=8)
+    g = to_gpu(wl)
+    ws = _workspace(wl)
+    log("case expired waits")
+    o1, s1 = run_gpu(wl, g, workspace=ws)
+    torch.cuda.synchronize()
+    assert fw.workspace_errors(ws) == 0
+    fw.set_wait_bound(1)
+    try:
+        run_gpu(wl, g, workspace=ws)
+        torch.cuda.synchronize()
+    finally:
+        fw.set_wait_bound(0)
+    marked = fw.workspace_errors(ws, clear=True)
+    assert 0 < marked <= 2 * 8, marked
+    assert fw.workspace_errors(ws) == 0
+    for _ in range(2):
+        o2, s2 = run_gpu(wl, g, workspace=ws)
+        torch.cuda.synchronize()
+        assert torch.equal(o1, o2) and torch.equal(s1, s2)
+    assert fw.workspace_errors(ws) == 0
